@@ -1,0 +1,212 @@
+"""Seeded synthetic inputs for absorbed-MLA decode.
+
+This module only draws and lays out random data: it holds none of the
+method's arithmetic, and both the GPU library's tests and the CPU oracle take
+their inputs from here. Nothing in it imports either side.
+
+Recipes (all seeded, all synthetic):
+
+* ``tiny_mla_weights``: the tiny full-MLA instance of the handbook chapter
+  "MLA 推理：两条计算路径与 FlashMLA", section "两条等价的路径": torch seed 0,
+  T=6, D=64, H=4, nope 8, rope 4, v 8, latent 16, with weights drawn by
+  ``torch.randn`` in the chapter's order (W_q, W_dkv, W_kr, W_uk, W_uv, W_o, h)
+  and scaled by 1/8 or 1/4 as the chapter does.
+* ``make_decode_case``: a paged latent cache and absorbed queries. Cache rows
+  and queries are standard normals from ``numpy.random.default_rng(seed)``;
+  queries are scaled (default 1/sqrt(576)); both are rounded to bf16 with
+  round-to-nearest-even (or kept fp32). Pages hold 64 tokens. Physical pages
+  come from one shuffled global pool with about 10% spare pages. Every slot no
+  sequence owns (spare pages, the tail of each last page, block-table entries
+  past a sequence's pages, which point at a spare page) holds NaN, so any read
+  of it shows up in the output. Optionally a fraction of each sequence's token
+  rows is multiplied by 8 (exact in bf16) as outliers.
+* ``config_case``: the five workload shapes (tiny fp32 case aside) used for
+  parity and measurement: single-sequence 4096-token decode, 64 x 4096 batched
+  decode, 128-sequence two-token speculative decode with lengths uniform in
+  [1024, 8192], and 8-sequence long-context variable-length decode.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import math
+
+import numpy as np
+import torch
+
+PAGE = 64
+D_QK = 576
+D_V = 512
+SCALE_DS = 1.0 / math.sqrt(192.0)  # 1/sqrt(d_nope + d_rope) with 128 + 64
+
+
+@dataclass
+class DecodeCase:
+    """One decode problem, CPU tensors, row-major and contiguous."""
+
+    q_lat: torch.Tensor  # [B, s_q, H, 576] bf16 or fp32
+    cache: torch.Tensor  # [num_pages, 64, 576] same dtype
+    block_table: torch.Tensor  # [B, max_pages] int32
+    seqlens: torch.Tensor  # [B] int32, L_b counting the s_q new tokens
+    s_q: int
+    H: int
+    causal: bool
+    scale: float
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.q_lat.shape[0])
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.q_lat.dtype
+
+
+def _round_to(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(dtype) if dtype != torch.float32 else t.clone()
+
+
+def make_decode_case(
+    seqlens: Sequence[int],
+    s_q: int = 1,
+    H: int = 128,
+    seed: int = 0,
+    dtype: torch.dtype = torch.bfloat16,
+    q_scale: float = 1.0 / math.sqrt(D_QK),
+    causal: Optional[bool] = None,
+    scale: float = SCALE_DS,
+    spare_frac: float = 0.10,
+    outlier_frac: float = 0.0,
+    extra_table_cols: int = 1,
+    d_qk: int = D_QK,
+    name: str = "",
+) -> DecodeCase:
+    """Draw one paged decode problem.
+
+    Draw order from ``default_rng(seed)``: page permutation, cache normals,
+    query normals, then (if ``outlier_frac``) the outlier rows per sequence.
+    ``causal`` defaults to ``s_q > 1``.
+    """
+    seqlens = [int(x) for x in seqlens]
+    B = len(seqlens)
+    if any(L < s_q for L in seqlens):
+        raise ValueError("every sequence must hold its s_q new tokens")
+    causal = (s_q > 1) if causal is None else bool(causal)
+    pages = [(L + PAGE - 1) // PAGE for L in seqlens]
+    used = sum(pages)
+    spares = max(1, int(round(spare_frac * used)))
+    num_pages = used + spares
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(num_pages)
+    max_pages = max(pages) + extra_table_cols
+    spare_ids = perm[used:]
+    table = np.empty((B, max_pages), dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        table[b, : pages[b]] = perm[pos : pos + pages[b]]
+        table[b, pages[b] :] = spare_ids[b % len(spare_ids)]
+        pos += pages[b]
+    cache32 = rng.standard_normal((num_pages, PAGE, d_qk), dtype=np.float32)
+    q32 = rng.standard_normal((B, s_q, H, d_qk), dtype=np.float32) * np.float32(q_scale)
+    cache = _round_to(cache32, dtype)
+    del cache32
+    if outlier_frac > 0:
+        for b in range(B):
+            k = int(round(outlier_frac * seqlens[b]))
+            if k == 0:
+                continue
+            rows = rng.choice(seqlens[b], size=k, replace=False)
+            phys = torch.from_numpy(table[b, rows // PAGE].astype(np.int64))
+            slot = torch.from_numpy((rows % PAGE).astype(np.int64))
+            cache[phys, slot] = cache[phys, slot] * 8
+    # Poison every slot no sequence owns.
+    owned = np.zeros((num_pages, PAGE), dtype=bool)
+    for b in range(B):
+        full, rem = divmod(seqlens[b], PAGE)
+        owned[table[b, :full]] = True
+        if rem:
+            owned[table[b, full], :rem] = True
+    cache[torch.from_numpy(~owned)] = float("nan")
+    return DecodeCase(
+        q_lat=_round_to(q32, dtype),
+        cache=cache,
+        block_table=torch.from_numpy(table),
+        seqlens=torch.tensor(seqlens, dtype=torch.int32),
+        s_q=s_q,
+        H=H,
+        causal=causal,
+        scale=scale,
+        name=name,
+        meta={"seed": seed, "num_pages": num_pages, "used_pages": used,
+              "q_scale": q_scale, "outlier_frac": outlier_frac},
+    )
+
+
+def mtp_lengths(B: int, lo: int, hi: int, seed: int) -> list:
+    """Per-sequence cached lengths uniform in [lo, hi] (a separate stream, seed+1000)."""
+    rng = np.random.default_rng(seed + 1000)
+    return [int(x) for x in rng.integers(lo, hi + 1, size=B)]
+
+
+LONG_CONTEXT_LENGTHS = [65536, 32768, 16384, 8192, 4096, 2048, 1024, 513]
+
+
+def config_case(idx: int) -> DecodeCase:
+    """The workload shapes, by index 1..4 (index 0 is ``tiny_mla_weights``)."""
+    if idx == 1:
+        return make_decode_case([4096], s_q=1, seed=1, name="single-seq B=1 ctx=4096",
+                                spare_frac=0.25)
+    if idx == 2:
+        return make_decode_case([4096] * 64, s_q=1, seed=2, name="batched B=64 ctx=4096")
+    if idx == 3:
+        return make_decode_case(mtp_lengths(128, 1024, 8192, 3), s_q=2, seed=3,
+                                name="mtp B=128 s_q=2 ctx~U[1024,8192]")
+    if idx == 4:
+        return make_decode_case(LONG_CONTEXT_LENGTHS, s_q=1, seed=4, outlier_frac=0.01,
+                                name="long-context varlen B=8")
+    raise ValueError(f"no decode workload with index {idx}")
+
+
+def tiny_mla_weights(seed: int = 0) -> dict:
+    """The tiny full-MLA draws of the handbook chapter's worked example.
+
+    ``torch.manual_seed(seed)`` then ``torch.randn`` in the chapter's order:
+    W_q [D, H(nope+rope)]/8, W_dkv [D, DC]/8, W_kr [D, rope]/8,
+    W_uk [H, DC, nope]/4, W_uv [H, DC, DV]/4, W_o [H DV, D]/8, h [T, D].
+    Returns float32 numpy arrays and the dimensions.
+    """
+    T, D, H = 6, 64, 4
+    NOPE, ROPE, DV, DC = 8, 4, 8, 16
+    g = torch.Generator().manual_seed(seed)
+    W_q = torch.randn(D, H * (NOPE + ROPE), generator=g) / 8
+    W_dkv = torch.randn(D, DC, generator=g) / 8
+    W_kr = torch.randn(D, ROPE, generator=g) / 8
+    W_uk = torch.randn(H, DC, NOPE, generator=g) / 4
+    W_uv = torch.randn(H, DC, DV, generator=g) / 4
+    W_o = torch.randn(H * DV, D, generator=g) / 8
+    h = torch.randn(T, D, generator=g)
+    arrays = dict(W_q=W_q, W_dkv=W_dkv, W_kr=W_kr, W_uk=W_uk, W_uv=W_uv, W_o=W_o, h=h)
+    out = {k: v.numpy() for k, v in arrays.items()}
+    out.update(T=T, D=D, H=H, NOPE=NOPE, ROPE=ROPE, DV=DV, DC=DC)
+    return out
+
+
+def random_tiny_mla(seed: int, T: int = 5, D: int = 32, H: int = 3, NOPE: int = 6,
+                    ROPE: int = 4, DV: int = 5, DC: int = 10) -> dict:
+    """Other tiny full-MLA instances, same recipe with a numpy stream."""
+    rng = np.random.default_rng(seed)
+    out = dict(
+        W_q=rng.standard_normal((D, H * (NOPE + ROPE))) / 8,
+        W_dkv=rng.standard_normal((D, DC)) / 8,
+        W_kr=rng.standard_normal((D, ROPE)) / 8,
+        W_uk=rng.standard_normal((H, DC, NOPE)) / 4,
+        W_uv=rng.standard_normal((H, DC, DV)) / 4,
+        W_o=rng.standard_normal((H * DV, D)) / 8,
+        h=rng.standard_normal((T, D)),
+    )
+    out.update(T=T, D=D, H=H, NOPE=NOPE, ROPE=ROPE, DV=DV, DC=DC)
+    return out

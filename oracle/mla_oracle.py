@@ -1,0 +1,307 @@
+"""Plain fp64 CPU oracle for Multi-head Latent Attention (MLA) decode.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import or
+call this module. The GPU library never imports it, and this module imports
+nothing from the GPU library: the two share no code. Inputs reach both sides
+from the seeded generators in ``mla_inputs``, which hold none of the method's
+arithmetic.
+
+Everything here is a direct, unblocked statement of what the pages define,
+computed in float64 with numpy. There is no tiling, no online softmax and no
+reordering beyond what each definition states.
+
+Sources. Each citation names the page by its title and the section:
+  [MLA-推理]  "MLA 推理：两条计算路径与 FlashMLA" (AI infra handbook, serving/moe/mla)
+  [DSV2-MLA]  "DeepSeekV2之MLA" (blog post with the DeepSeek-V2 equations and SGLang code)
+  [AI-MTP]    "为什么 MLA + MTP 容易吃亏？从 Arithmetic Intensity 看 Attention"
+
+Function list and pins:
+  rope_adjacent      RoPE on adjacent pairs                 pinned (rotation identities)
+  project            hidden -> q_n, q_r, c, k_r             pinned (path equivalence)
+  expanded_attention path one: per-head K, V, ordinary MHA  pinned (path equivalence, SDPA)
+  mla_forward_*      both full tiny MLA paths to y          pinned (the page prints True)
+  absorb_q           q_lat = [W_UK q^N ; q^R]               pinned (path equivalence)
+  out_uv             o = o_lat W_UV[h]                      pinned (path equivalence)
+  decode_absorbed    absorbed decode on a paged cache       pinned (brute force, SDPA, closed forms)
+  decode_partials    the same over a token chunk            pinned (merge invariant)
+  lse_merge          log-sum-exp merge of chunk results     pinned (merge == unsplit)
+No function is left without a pin.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "rope_adjacent",
+    "project",
+    "expanded_attention",
+    "mla_forward_expanded",
+    "mla_forward_absorbed",
+    "absorb_q",
+    "out_uv",
+    "gather_tokens",
+    "decode_absorbed",
+    "decode_partials",
+    "lse_merge",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Full tiny MLA: the worked example of [MLA-推理] §"两条等价的路径".
+# ---------------------------------------------------------------------------
+
+def rope_adjacent(x, base: float = 10000.0) -> np.ndarray:
+    """Rotary embedding that rotates adjacent element pairs by position.
+
+    [MLA-推理] §"两条等价的路径", the worked example's ``rope``: the second-to-
+    last axis of ``x`` is the position t = 0..T-1 and the last axis has R
+    (even) elements. Pair i is (x[2i], x[2i+1]) and its angle is
+    t / base**(2i/R). The rotated pair is (x1 cos - x2 sin, x1 sin + x2 cos),
+    written back interleaved at the same two slots.
+    """
+    x = _f64(x)
+    T, R = x.shape[-2], x.shape[-1]
+    if R % 2:
+        raise ValueError("RoPE width must be even")
+    pos = np.arange(T, dtype=np.float64)[:, None]
+    inv = base ** (np.arange(0, R, 2, dtype=np.float64) / R)
+    ang = pos / inv  # [T, R/2]
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * np.cos(ang) - x2 * np.sin(ang)
+    out[..., 1::2] = x1 * np.sin(ang) + x2 * np.cos(ang)
+    return out
+
+
+def project(h, W_q, W_dkv, W_kr, H: int, nope: int, rope_dim: int):
+    """Projections of the worked example, [MLA-推理] §"两条等价的路径".
+
+    c = h W_dkv (the cached latent), k_r = RoPE(h W_kr) (the RoPE key shared by
+    all heads, cached beside c), q = h W_q viewed per head as [nope | rope],
+    q_n = its first ``nope`` elements, q_r = RoPE of the remaining ones.
+
+    Returns token-major arrays: q_n [T,H,nope], q_r [T,H,rope], c [T,DC],
+    k_r [T,rope].
+    """
+    h = _f64(h)
+    T = h.shape[0]
+    c = h @ _f64(W_dkv)
+    k_r = rope_adjacent(h @ _f64(W_kr))
+    q = (h @ _f64(W_q)).reshape(T, H, nope + rope_dim)
+    q_n = q[..., :nope]
+    # RoPE runs over the position axis, so rotate in [H, T, rope] order.
+    q_r = rope_adjacent(np.transpose(q[..., nope:], (1, 0, 2))).transpose(1, 0, 2)
+    return q_n, q_r, c, k_r
+
+
+def _masked_softmax_rows(s: np.ndarray, allowed: np.ndarray) -> np.ndarray:
+    """Row softmax of s over the entries where ``allowed`` is true (two passes)."""
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def expanded_attention(q_n, q_r, c, k_r, W_uk, W_uv, causal: bool = True) -> np.ndarray:
+    """Path one ("展开"): expand the latent per head, then ordinary MHA.
+
+    [MLA-推理] §"两条等价的路径": k^N = c W_UK[h] per head, concatenated with the
+    shared k^R; v = c W_UV[h]; scores use scale 1/sqrt(nope + rope); the mask
+    is the lower-triangular causal mask over the T tokens.
+    Shapes: q_n [T,H,nope], q_r [T,H,rope], c [T,DC], k_r [T,rope],
+    W_uk [H,DC,nope], W_uv [H,DC,DV]. Returns per-head outputs [T,H,DV].
+    """
+    q_n, q_r, c, k_r = map(_f64, (q_n, q_r, c, k_r))
+    W_uk, W_uv = _f64(W_uk), _f64(W_uv)
+    T, H, nope = q_n.shape
+    rope_dim = q_r.shape[-1]
+    scale = 1.0 / math.sqrt(nope + rope_dim)
+    k_nope = np.einsum("tc,hcd->htd", c, W_uk)  # [H,T,nope]
+    k = np.concatenate([k_nope, np.broadcast_to(k_r, (H, T, rope_dim))], axis=-1)
+    v = np.einsum("tc,hcd->htd", c, W_uv)  # [H,T,DV]
+    q = np.concatenate([q_n, q_r], axis=-1).transpose(1, 0, 2)  # [H,T,nope+rope]
+    s = (q @ k.transpose(0, 2, 1)) * scale  # [H,T,T]
+    allowed = np.tril(np.ones((T, T), dtype=bool)) if causal else np.ones((T, T), dtype=bool)
+    p = _masked_softmax_rows(s, allowed)
+    return (p @ v).transpose(1, 0, 2)  # [T,H,DV]
+
+
+def mla_forward_expanded(h, W_q, W_dkv, W_kr, W_uk, W_uv, W_o, H, nope, rope_dim, causal=True):
+    """Full tiny MLA on path one, output projection included: y = out W_o.
+
+    [MLA-推理] §"两条等价的路径" (worked example, ``out1`` and ``y1``).
+    """
+    q_n, q_r, c, k_r = project(h, W_q, W_dkv, W_kr, H, nope, rope_dim)
+    out = expanded_attention(q_n, q_r, c, k_r, W_uk, W_uv, causal)
+    T = out.shape[0]
+    return out.reshape(T, -1) @ _f64(W_o)
+
+
+def absorb_q(q_n, q_r, W_uk) -> np.ndarray:
+    """Absorbed query q_lat = [W_UK q^N ; q^R].
+
+    [MLA-推理] §"两条等价的路径" (path two: the query moves into latent space,
+    q~ = W_UK q^N, and the RoPE part is carried alongside);
+    [DSV2-MLA] §4.5 (the bmm of q_nope with w_kc before attention).
+    Shapes: q_n [N,H,nope], q_r [N,H,rope], W_uk [H,DC,nope] -> [N,H,DC+rope].
+    """
+    q_n, q_r, W_uk = _f64(q_n), _f64(q_r), _f64(W_uk)
+    lat = np.einsum("nhd,hcd->nhc", q_n, W_uk)
+    return np.concatenate([lat, q_r], axis=-1)
+
+
+def out_uv(o_lat, W_uv) -> np.ndarray:
+    """Per-head up-projection of the latent attention output: o[h] = o_lat[h] W_UV[h].
+
+    [MLA-推理] §"两条等价的路径" (path two multiplies by W_UV last);
+    [DSV2-MLA] §4.5 (the bmm of the attention output with w_vc).
+    Shapes: o_lat [N,H,DC], W_uv [H,DC,DV] -> [N,H,DV].
+    """
+    return np.einsum("nhc,hcd->nhd", _f64(o_lat), _f64(W_uv))
+
+
+def mla_forward_absorbed(h, W_q, W_dkv, W_kr, W_uk, W_uv, W_o, H, nope, rope_dim, causal=True):
+    """Full tiny MLA on path two, through the paged absorbed decode.
+
+    [MLA-推理] §"两条等价的路径" (``out2``/``y2``): every query attends to the
+    cached rows [c ; k_r] with the absorbed query, the weighted sum stays in
+    latent space, and W_UV is applied last. The T tokens are the s_q = T new
+    tokens of one sequence of length T, so the causal mask of the example is
+    the bottom-right mask of ``decode_absorbed``. One page holds all rows.
+    """
+    q_n, q_r, c, k_r = project(h, W_q, W_dkv, W_kr, H, nope, rope_dim)
+    T = c.shape[0]
+    q_lat = absorb_q(q_n, q_r, W_uk)[None]  # [1,T,H,DC+rope]
+    cache = np.concatenate([c, k_r], axis=-1)[None]  # [1 page, T rows, DC+rope]
+    o_lat, _ = decode_absorbed(
+        q_lat, cache, np.zeros((1, 1), np.int64), np.array([T]),
+        scale=1.0 / math.sqrt(nope + rope_dim), causal=causal, dv=c.shape[1])
+    out = out_uv(o_lat[0], W_uv)  # [T,H,DV]
+    return out.reshape(T, -1) @ _f64(W_o)
+
+
+# ---------------------------------------------------------------------------
+# Absorbed decode over a paged latent cache.
+# ---------------------------------------------------------------------------
+
+def gather_tokens(cache, block_table_row, L: int) -> np.ndarray:
+    """Logical token rows 0..L-1 of one sequence from the page pool.
+
+    Token j sits in physical page block_table_row[j // page] at slot j % page
+    ([MLA-推理] §"decode 注意力变成了计算问题": paged KV with pages of 64).
+    Returns [L, Dqk] in float64. Slots at or past L are never read.
+    """
+    page = cache.shape[1]
+    j = np.arange(L)
+    phys = np.asarray(block_table_row)[j // page]
+    return _f64(cache[phys, j % page])
+
+
+def _allowed_count(L: int, s_q: int, i: int, causal: bool) -> int:
+    """Number of keys query i may see: the new tokens are the last s_q of L,
+    so under the causal mask query i sees keys 0..L-s_q+i ([MLA-推理]
+    §"谁快：看新 token 和缓存 token 的数量": pairs = q*k - q(q-1)/2, k counts
+    the new tokens)."""
+    return L - s_q + i + 1 if causal else L
+
+
+def decode_absorbed(q_lat, cache, block_table, seqlens, scale: float, causal: bool, dv: int = 512):
+    """Absorbed-MLA decode: softmax attention of each (query token, head) row
+    over one shared key row and one shared value row per cached token.
+
+    [MLA-推理] §"两条等价的路径" (path two: scores q~ᵀc + q^Rᵀk^R, weighted sum in
+    latent space) and §"decode 注意力变成了计算问题" (the 128 heads share one
+    576-wide key and 512-wide value: an MQA with a wide head);
+    [AI-MTP] Appendix A (the RoPE part only enters the score; the value is the
+    latent alone).
+
+    q_lat [B,s_q,H,Dqk], cache [num_pages,page,Dqk], block_table [B,max_pages],
+    seqlens [B] (L_b, counting the s_q new tokens). The key of token j is the
+    whole cache row; its value is the first ``dv`` elements of that row.
+    For each (b, i, h): s_j = scale * q·K_j over the allowed keys, M = max s,
+    Z = sum exp(s_j - M), o = sum exp(s_j - M)/Z * V_j, lse = M + ln Z
+    (natural log). Two passes over the full row; no online rescaling.
+    Returns o_lat [B,s_q,H,dv] and lse [B,s_q,H], both float64.
+    """
+    q_lat = _f64(q_lat)
+    B, s_q, H, _ = q_lat.shape
+    o = np.zeros((B, s_q, H, dv))
+    lse = np.zeros((B, s_q, H))
+    for b in range(B):
+        L = int(seqlens[b])
+        if L < s_q:
+            raise ValueError("each sequence must hold at least its s_q new tokens")
+        K = gather_tokens(cache, block_table[b], L)
+        for i in range(s_q):
+            n = _allowed_count(L, s_q, i, causal)
+            Kb = K[:n]
+            s = (q_lat[b, i] @ Kb.T) * scale  # [H, n]
+            M = s.max(axis=1, keepdims=True)
+            e = np.exp(s - M)
+            Z = e.sum(axis=1, keepdims=True)
+            o[b, i] = (e / Z) @ Kb[:, :dv]
+            lse[b, i] = (M + np.log(Z))[:, 0]
+    return o, lse
+
+
+def decode_partials(q_lat, cache, block_table, seqlens, scale: float, causal: bool,
+                    chunks, dv: int = 512):
+    """The absorbed decode restricted to token chunks, one partial per chunk.
+
+    [MLA-推理] §"decode 注意力变成了计算问题" (split-KV: split along the KV axis
+    and merge the partial results). ``chunks[b]`` lists half-open token ranges
+    [a, e) of sequence b. A row with no allowed key inside a chunk has
+    o = 0 and lse = -inf, so it drops out of the merge.
+    Returns a list over b of (o_part [n_b,s_q,H,dv], lse_part [n_b,s_q,H]).
+    """
+    q_lat = _f64(q_lat)
+    B, s_q, H, _ = q_lat.shape
+    out = []
+    for b in range(B):
+        L = int(seqlens[b])
+        K = gather_tokens(cache, block_table[b], L)
+        ob = np.zeros((len(chunks[b]), s_q, H, dv))
+        lb = np.full((len(chunks[b]), s_q, H), -np.inf)
+        for k, (a, e_) in enumerate(chunks[b]):
+            for i in range(s_q):
+                n = min(e_, _allowed_count(L, s_q, i, causal))
+                if n <= a:
+                    continue
+                Kc = K[a:n]
+                s = (q_lat[b, i] @ Kc.T) * scale
+                M = s.max(axis=1, keepdims=True)
+                ex = np.exp(s - M)
+                Z = ex.sum(axis=1, keepdims=True)
+                ob[k, i] = (ex / Z) @ Kc[:, :dv]
+                lb[k, i] = (M + np.log(Z))[:, 0]
+        out.append((ob, lb))
+    return out
+
+
+def lse_merge(o_parts, lse_parts):
+    """Merge chunk results by their log-sum-exp.
+
+    [MLA-推理] §"谁快：看新 token 和缓存 token 的数量" (chunk results are merged by
+    LSE, the same merge as in context parallelism) and §"decode 注意力变成了计算
+    问题" (split-KV merges the partial results). With lse_k the natural-log
+    normaliser of chunk k: lse = M + ln sum_k exp(lse_k - M) where
+    M = max_k lse_k, and o = sum_k exp(lse_k - lse) o_k. Chunks with
+    lse_k = -inf add nothing.
+    o_parts [n,...,dv], lse_parts [n,...] -> (o [...,dv], lse [...]).
+    """
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    M = lse_parts.max(axis=0)
+    Mf = np.where(np.isfinite(M), M, 0.0)
+    w = np.exp(lse_parts - Mf)  # exp(-inf) = 0 for empty chunks
+    S = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = Mf + np.log(S)
+    o = np.einsum("k...,k...d->...d", w / np.where(S > 0, S, 1.0), o_parts)
+    return o, lse

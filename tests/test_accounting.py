@@ -1,0 +1,59 @@
+"""FLOP / byte accounting pinned to the numbers the pages print."""
+import math
+
+import pytest
+
+from mla_decode_fwd_amd import accounting as acc
+from conftest import load_golden
+
+
+def test_handbook_flop_script_numbers():
+    g = load_golden("flop_accounting.txt")
+    d = acc.DSV3
+    pn = acc.pair_flops_expanded(d["H"], d["NOPE"], d["ROPE"], d["DV"])
+    pa = acc.pair_flops_absorbed(d["H"], d["DC"], d["ROPE"])
+    assert round(pn / 1e3) == g["pair_flops_expanded_K"]
+    assert round(pa / 1e3) == g["pair_flops_absorbed_K"]
+    assert round(pa / pn, 1) == g["pair_ratio"]
+    assert round(acc.expand_flops_per_key(d["H"], d["NOPE"], d["DV"], d["DC"]) / 1e6, 1) == g["expand_per_key_MFLOP"]
+    assert round(acc.absorb_flops_per_query(d["H"], d["NOPE"], d["DV"], d["DC"]) / 1e6, 1) == g["absorb_per_query_MFLOP"]
+    for key, q, k in [("decode_q1_k8192", 1, 8192), ("prefill_q8192_k8192", 8192, 8192),
+                      ("append_q64_k32832", 64, 32768 + 64), ("append_q512_k33280", 512, 32768 + 512)]:
+        e, a = acc.path_flops(q, k)
+        assert round(e / 1e9, 1) == g[key + "_expanded_GFLOP"], key
+        assert round(a / 1e9, 1) == g[key + "_absorbed_GFLOP"], key
+    assert round(acc.crossover_new_tokens()) == g["crossover_new_tokens"]
+    assert round(acc.mla_decode_ai(d["H"], d["DC"], d["ROPE"])) == g["mla_decode_ai_bf16"]
+    # GQA: 64 query heads over 8 KV heads of width 128, K and V read in bf16.
+    assert round(2 * 64 * 128 * 2 / (8 * 128 * 2 * 2)) == g["gqa_64q_8kv_d128_ai_bf16"]
+    assert round(989e12 / 3.35e12) == g["h800_ridge_flop_per_byte"]
+    assert round(acc.mla_decode_ai(d["H"], d["DC"], d["ROPE"], bytes_per_elem=1.0)) == g["mla_decode_ai_fp8"]
+
+
+def test_appendix_closed_forms():
+    g = load_golden("ai_closed_forms.txt")
+    assert round(acc.mla_decode_ai(128, 512, 64), 1) == g["dsv3_ai"]
+    assert round(acc.mla_decode_ai(96, 512, 64), 1) == g["k3_ai"]
+    # Per head and pair, in multiply-adds: pair FLOPs / (2 H).
+    assert acc.pair_flops_absorbed(1, 512, 64) / 2 == g["pair_absorbed_per_head"]
+    assert acc.pair_flops_expanded(1, 128, 64, 128) / 2 == g["pair_expanded_per_head"]
+    assert acc.expand_flops_per_key(1, 128, 128, 512) / 2 == g["expand_setup_per_key_per_head"]
+    assert round(g["pair_absorbed_per_head"] / g["pair_expanded_per_head"], 1) == g["pair_ratio"]
+    assert round(g["h100_sxm_tflops"] / g["h100_sxm_tbps"]) == g["h100_sxm_balance"]
+    assert round(g["h100_sxm_tflops"] / g["h200_sxm_tbps"]) == g["h200_sxm_balance"]
+    assert round(g["b200_pflops"] * 1e3 / g["b200_tbps"]) == g["b200_balance"]
+
+
+def test_decode_metric_accounting():
+    # One 4096-token sequence, H=128: 2*128*1088*4096 FLOP.
+    assert acc.decode_flops([4096], 1, 128) == 2 * 128 * 1088 * 4096
+    # Two new tokens causal over L: pairs = 2L - 1.
+    assert acc.decode_flops([100], 2, 128) == 2 * 128 * 1088 * 199
+    kv = acc.kv_bytes([4096] * 64)
+    assert kv == 64 * 4096 * 1152
+    b = acc.decode_bytes([4096] * 64, 1, 128)
+    assert b == kv + 64 * 128 * 576 * 2 + 64 * 128 * 512 * 2 + 64 * 128 * 4 + 64 * 64 * 4
+    r = acc.roofline(acc.decode_flops([4096] * 64, 1, 128), b, 40e-6)
+    assert r["bound"] == "hbm" and math.isclose(r["frac"], b / 40e-6 / 8e12)
+    r2 = acc.roofline(1e15, 1e12, 1.0)
+    assert r2["bound"] == "mfma" and math.isclose(r2["frac"], 0.4)

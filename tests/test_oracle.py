@@ -1,0 +1,377 @@
+"""Pins of the fp64 CPU oracle against what the pages and mathematics fix.
+
+Every check below ties the oracle to something other than itself: the
+worked example's printed result, brute force with Python floats, torch's
+scaled-dot-product attention on an unpaged copy of the cache, closed forms
+and invariants. The mutation tests at the end plant plausible mistakes in the
+oracle (on the CPU) and show that a pin catches each one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import mla_oracle as orc
+from mla_inputs import make_decode_case, random_tiny_mla, tiny_mla_weights
+from conftest import load_golden
+
+
+def _np(t):
+    return t.detach().to(torch.float64).numpy() if isinstance(t, torch.Tensor) else np.asarray(t)
+
+
+def _case_arrays(case):
+    return (_np(case.q_lat), _np(case.cache), case.block_table.numpy(),
+            case.seqlens.numpy())
+
+
+# ---------------------------------------------------------------------------
+# Independent references used by the pins
+# ---------------------------------------------------------------------------
+
+def brute_decode(q_lat, cache, table, seqlens, scale, causal, dv):
+    """Python-float loops: one score at a time, math.exp, no numpy reductions."""
+    B, s_q, H, D = q_lat.shape
+    page = cache.shape[1]
+    o = np.zeros((B, s_q, H, dv))
+    lse = np.zeros((B, s_q, H))
+    for b in range(B):
+        L = int(seqlens[b])
+        rows = [cache[int(table[b][j // page])][j % page] for j in range(L)]
+        for i in range(s_q):
+            last = (L - s_q + i) if causal else (L - 1)
+            for h in range(H):
+                q = [float(x) for x in q_lat[b, i, h]]
+                scores = []
+                for j in range(last + 1):
+                    acc = 0.0
+                    for k in range(D):
+                        acc += q[k] * float(rows[j][k])
+                    scores.append(acc * scale)
+                mx = max(scores)
+                w = [math.exp(s - mx) for s in scores]
+                Z = sum(w)
+                for c in range(dv):
+                    acc = 0.0
+                    for j in range(last + 1):
+                        acc += w[j] * float(rows[j][c])
+                    o[b, i, h, c] = acc / Z
+                lse[b, i, h] = mx + math.log(Z)
+    return o, lse
+
+
+def sdpa_decode(q_lat, cache, table, seqlens, scale, causal, dv):
+    """torch SDPA (fp64, CPU) on an unpaged copy: the absorbed decode is an MQA
+    with one shared wide key/value head."""
+    B, s_q, H, D = q_lat.shape
+    page = cache.shape[1]
+    o = np.zeros((B, s_q, H, dv))
+    for b in range(B):
+        L = int(seqlens[b])
+        npg = (L + page - 1) // page
+        flat = torch.from_numpy(cache[table[b, :npg]].reshape(npg * page, D)[:L])
+        q = torch.from_numpy(q_lat[b]).transpose(0, 1)  # [H, s_q, D]
+        k = flat.expand(H, L, D)
+        v = flat[:, :dv].expand(H, L, dv)
+        j = torch.arange(L)[None, :]
+        i = torch.arange(s_q)[:, None]
+        mask = (j <= L - s_q + i) if causal else torch.ones(s_q, L, dtype=torch.bool)
+        out = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+        o[b] = out.transpose(0, 1).numpy()
+    return o
+
+
+# ---------------------------------------------------------------------------
+# Worked example: the page prints that both paths agree (allclose, atol 1e-5).
+# ---------------------------------------------------------------------------
+
+def test_worked_example_matches_printed_output():
+    g = load_golden("worked_example.txt")
+    w = tiny_mla_weights(0)
+    args = (w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["W_uk"], w["W_uv"], w["W_o"],
+            w["H"], w["NOPE"], w["ROPE"])
+    y1 = orc.mla_forward_expanded(*args)
+    y2 = orc.mla_forward_absorbed(*args)
+    assert bool(np.allclose(y1, y2, atol=g["paths_allclose_atol"], rtol=0)) == g["paths_allclose"]
+    # In fp64 the two paths agree to rounding, far inside the printed bound.
+    assert np.max(np.abs(y1 - y2)) <= 1e-12
+    assert np.all(np.isfinite(y1)) and np.abs(y1).max() > 1e-3
+    H, NOPE, ROPE, DV, DC = (int(w[k]) for k in ("H", "NOPE", "ROPE", "DV", "DC"))
+    assert H * (NOPE + ROPE) + H * DV == g["cache_numbers_per_token_mha"]
+    assert DC + ROPE == g["cache_numbers_per_token_mla"]
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("causal", [True, False])
+def test_paths_agree_random_tiny(seed, causal):
+    w = random_tiny_mla(seed, T=4 + seed, H=2 + seed, DC=7 + 3 * seed)
+    args = (w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["W_uk"], w["W_uv"], w["W_o"],
+            w["H"], w["NOPE"], w["ROPE"])
+    y1 = orc.mla_forward_expanded(*args, causal=causal)
+    y2 = orc.mla_forward_absorbed(*args, causal=causal)
+    assert np.max(np.abs(y1 - y2)) <= 1e-12 * max(1.0, np.abs(y1).max())
+
+
+def test_expanded_attention_matches_sdpa():
+    """Path one checked against torch SDPA with the per-head K, V it builds."""
+    w = random_tiny_mla(7, T=7, H=3)
+    q_n, q_r, c, k_r = orc.project(w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["H"], w["NOPE"], w["ROPE"])
+    out = orc.expanded_attention(q_n, q_r, c, k_r, w["W_uk"], w["W_uv"], causal=True)
+    T, H = q_n.shape[:2]
+    kn = torch.einsum("tc,hcd->htd", torch.from_numpy(c), torch.from_numpy(w["W_uk"]))
+    k = torch.cat([kn, torch.from_numpy(k_r).expand(H, T, -1)], -1)
+    v = torch.einsum("tc,hcd->htd", torch.from_numpy(c), torch.from_numpy(w["W_uv"]))
+    q = torch.cat([torch.from_numpy(q_n), torch.from_numpy(q_r)], -1).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                         scale=1 / math.sqrt(w["NOPE"] + w["ROPE"]))
+    assert np.max(np.abs(out - ref.transpose(0, 1).numpy())) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# RoPE: closed forms of the adjacent-pair rotation.
+# ---------------------------------------------------------------------------
+
+def test_rope_closed_forms():
+    T, R = 9, 4
+    x = np.zeros((T, R))
+    x[:, 2] = 1.0  # unit vector on pair 1
+    y = orc.rope_adjacent(x)
+    t = np.arange(T)
+    ang = t / 10000 ** (2 / R)  # pair 1 angle = t / 100
+    assert np.allclose(y[:, 2], np.cos(ang), atol=1e-15)
+    assert np.allclose(y[:, 3], np.sin(ang), atol=1e-15)
+    assert np.allclose(y[:, :2], 0)
+    x = np.zeros((T, R))
+    x[:, 1] = 1.0  # second slot of pair 0, angle t
+    y = orc.rope_adjacent(x)
+    assert np.allclose(y[:, 0], -np.sin(t), atol=1e-15)
+    assert np.allclose(y[:, 1], np.cos(t), atol=1e-15)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((T, 6))
+    y = orc.rope_adjacent(x)
+    assert np.allclose(y[0], x[0])  # position 0 is the identity
+    assert np.allclose(x[:, 0::2] ** 2 + x[:, 1::2] ** 2, y[:, 0::2] ** 2 + y[:, 1::2] ** 2)
+    # Relative position: <rope(a)_t, rope(b)_s> depends on t - s only.
+    a = np.tile(rng.standard_normal(6), (T, 1))
+    b = np.tile(rng.standard_normal(6), (T, 1))
+    ra, rb = orc.rope_adjacent(a), orc.rope_adjacent(b)
+    d1 = ra[5] @ rb[2]
+    d2 = ra[7] @ rb[4]
+    assert abs(d1 - d2) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Absorbed decode against brute force and against SDPA.
+# ---------------------------------------------------------------------------
+
+def _tiny_case(seed, s_q, lens, H=3, d_qk=20):
+    return make_decode_case(lens, s_q=s_q, H=H, seed=seed, dtype=torch.float32,
+                            q_scale=0.4, d_qk=d_qk, scale=0.37)
+
+
+@pytest.mark.parametrize("s_q,lens", [(1, [1, 13]), (2, [2, 70]), (3, [150, 65, 5])])
+def test_decode_matches_brute_force(s_q, lens):
+    case = _tiny_case(11 + s_q, s_q, lens)
+    q, cache, table, L = _case_arrays(case)
+    o, lse = orc.decode_absorbed(q, cache, table, L, case.scale, case.causal, dv=12)
+    ob, lb = brute_decode(q, cache, table, L, case.scale, case.causal, 12)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.max(np.abs(o - ob)) <= 1e-12
+    assert np.max(np.abs(lse - lb)) <= 1e-12
+
+
+@pytest.mark.parametrize("s_q,causal", [(1, False), (2, True), (4, True), (2, False)])
+def test_decode_matches_sdpa_full_width(s_q, causal):
+    case = make_decode_case([300, 64, 129, 7 + s_q], s_q=s_q, H=16, seed=5 + s_q,
+                            dtype=torch.bfloat16, q_scale=1.0, causal=causal)
+    q, cache, table, L = _case_arrays(case)
+    o, _ = orc.decode_absorbed(q, cache, table, L, case.scale, case.causal, dv=512)
+    ref = sdpa_decode(q, cache, table, L, case.scale, case.causal, 512)
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def test_single_key_returns_its_value_and_score():
+    case = make_decode_case([1, 1], s_q=1, H=8, seed=21, dtype=torch.float32, q_scale=1.0)
+    q, cache, table, L = _case_arrays(case)
+    o, lse = orc.decode_absorbed(q, cache, table, L, case.scale, False, dv=512)
+    for b in range(2):
+        row = cache[table[b, 0], 0]
+        assert np.allclose(o[b, 0], np.broadcast_to(row[:512], (8, 512)), atol=0, rtol=0)
+        s = case.scale * (q[b, 0] @ row)
+        assert np.allclose(lse[b, 0], s, atol=1e-12)
+
+
+def test_zero_query_averages_values_and_lse_is_log_count():
+    case = make_decode_case([200, 77], s_q=2, H=4, seed=22, dtype=torch.float32)
+    q, cache, table, L = _case_arrays(case)
+    q = np.zeros_like(q)
+    o, lse = orc.decode_absorbed(q, cache, table, L, case.scale, True, dv=512)
+    for b in range(2):
+        for i in range(2):
+            n = L[b] - 2 + i + 1
+            rows = np.stack([cache[table[b, j // 64], j % 64, :512] for j in range(n)])
+            assert np.allclose(o[b, i], rows.mean(0)[None], atol=1e-13)
+            assert np.allclose(lse[b, i], math.log(n), atol=1e-13)
+
+
+def test_identical_keys_give_that_value():
+    case = make_decode_case([90], s_q=1, H=4, seed=23, dtype=torch.float32, q_scale=1.0)
+    q, cache, table, L = _case_arrays(case)
+    row = cache[table[0, 0], 0].copy()
+    cache = cache.copy()
+    for j in range(90):
+        cache[table[0, j // 64], j % 64] = row
+    o, lse = orc.decode_absorbed(q, cache, table, L, case.scale, False, dv=512)
+    assert np.allclose(o[0, 0], row[None, :512], atol=1e-13)
+    assert np.allclose(lse[0, 0], case.scale * (q[0, 0] @ row) + math.log(90), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def _random_chunks(rng, L, n):
+    cuts = sorted(set(int(x) for x in rng.integers(1, L, size=n - 1))) if L > 1 else []
+    bounds = [0] + cuts + [L]
+    return [(bounds[k], bounds[k + 1]) for k in range(len(bounds) - 1)]
+
+
+def check_split_merge(decode, partials, merge, case, seed):
+    q, cache, table, L = _case_arrays(case)
+    o, lse = decode(q, cache, table, L, case.scale, case.causal, dv=512)
+    rng = np.random.default_rng(seed)
+    chunks = [_random_chunks(rng, int(x), 5) for x in L]
+    parts = partials(q, cache, table, L, case.scale, case.causal, chunks, dv=512)
+    err = 0.0
+    for b, (op, lp) in enumerate(parts):
+        om, lm = merge(op, lp)
+        err = max(err, np.max(np.abs(om - o[b])), np.max(np.abs(lm - lse[b])))
+    return err
+
+
+def test_split_merge_equals_unsplit():
+    case = make_decode_case([500, 130, 3], s_q=3, H=8, seed=31, dtype=torch.bfloat16, q_scale=1.0)
+    err = check_split_merge(orc.decode_absorbed, orc.decode_partials, orc.lse_merge, case, 0)
+    assert err <= 1e-13
+
+
+def test_merge_of_empty_chunk_contributes_nothing():
+    o = np.random.default_rng(1).standard_normal((3, 2, 5))
+    lse = np.array([[0.3, -np.inf], [-np.inf, -np.inf], [1.2, 0.5]])
+    om, lm = orc.lse_merge(o, lse)
+    om2, lm2 = orc.lse_merge(o[[0, 2]], lse[[0, 2]])
+    assert np.allclose(om, om2) and np.allclose(lm, lm2)
+    assert np.all(np.isfinite(om))
+
+
+def test_page_permutation_is_bitwise_invariant():
+    case = make_decode_case([300, 200], s_q=2, H=8, seed=41, dtype=torch.bfloat16, q_scale=1.0)
+    q, cache, table, L = _case_arrays(case)
+    perm = np.random.default_rng(3).permutation(cache.shape[0])
+    cache2 = np.empty_like(cache)
+    cache2[perm] = cache
+    table2 = perm[table]
+    o1, l1 = orc.decode_absorbed(q, cache, table, L, case.scale, True)
+    o2, l2 = orc.decode_absorbed(q, cache2, table2, L, case.scale, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_head_permutation_and_sequence_independence():
+    case = make_decode_case([260, 100], s_q=1, H=16, seed=42, dtype=torch.bfloat16, q_scale=1.0)
+    q, cache, table, L = _case_arrays(case)
+    o1, l1 = orc.decode_absorbed(q, cache, table, L, case.scale, False)
+    hp = np.random.default_rng(4).permutation(16)
+    o2, l2 = orc.decode_absorbed(q[:, :, hp], cache, table, L, case.scale, False)
+    assert np.allclose(o2, o1[:, :, hp], atol=1e-14) and np.allclose(l2, l1[:, :, hp], atol=1e-14)
+    q3, cache3 = q.copy(), cache.copy()
+    q3[1] = -q3[1]
+    cache3[table[1, :2]] *= 3.0
+    o3, l3 = orc.decode_absorbed(q3, cache3, table, L, case.scale, False)
+    assert np.array_equal(o3[0], o1[0]) and np.array_equal(l3[0], l1[0])
+    assert not np.allclose(o3[1], o1[1])
+
+
+def test_absorb_and_out_uv_agree_with_expansion():
+    """q_lat . [c; k_r] equals the expanded per-head score, and o_lat W_UV the
+    expanded per-head value mix (the two associativity steps of path two)."""
+    rng = np.random.default_rng(9)
+    H, NOPE, ROPE, DC, DV, N, T = 3, 5, 4, 11, 6, 4, 7
+    q_n, q_r = rng.standard_normal((N, H, NOPE)), rng.standard_normal((N, H, ROPE))
+    c, k_r = rng.standard_normal((T, DC)), rng.standard_normal((T, ROPE))
+    W_uk, W_uv = rng.standard_normal((H, DC, NOPE)), rng.standard_normal((H, DC, DV))
+    ql = orc.absorb_q(q_n, q_r, W_uk)
+    s_abs = np.einsum("nhc,tc->nht", ql, np.concatenate([c, k_r], 1))
+    kn = np.einsum("tc,hcd->htd", c, W_uk)
+    s_exp = np.einsum("nhd,htd->nht", q_n, kn) + np.einsum("nhr,tr->nht", q_r, k_r)
+    assert np.max(np.abs(s_abs - s_exp)) <= 1e-12
+    p = rng.random((N, H, T))
+    o_lat = np.einsum("nht,tc->nhc", p, c)
+    v = np.einsum("tc,hcd->htd", c, W_uv)
+    assert np.max(np.abs(orc.out_uv(o_lat, W_uv) - np.einsum("nht,htd->nhd", p, v))) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Mutation tests: plausible mistakes planted in the oracle must fail a pin.
+# ---------------------------------------------------------------------------
+
+def test_mutation_causal_off_by_one_is_caught(monkeypatch):
+    case = _tiny_case(12, 2, [2, 70])
+    q, cache, table, L = _case_arrays(case)
+    ob, _ = brute_decode(q, cache, table, L, case.scale, True, 12)
+    monkeypatch.setattr(orc, "_allowed_count", lambda L, s_q, i, c: L - s_q + i if c else L)
+    with np.errstate(all="ignore"):
+        try:
+            o, _ = orc.decode_absorbed(q, cache, table, L, case.scale, True, dv=12)
+        except ValueError:  # an empty row is also a detection
+            return
+    assert not np.allclose(o, ob, atol=1e-6, equal_nan=False)
+
+
+def test_mutation_dropped_rope_term_is_caught(monkeypatch):
+    w = tiny_mla_weights(0)
+    args = (w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["W_uk"], w["W_uv"], w["W_o"],
+            w["H"], w["NOPE"], w["ROPE"])
+    real = orc.absorb_q
+    monkeypatch.setattr(orc, "absorb_q", lambda qn, qr, W: real(qn, np.zeros_like(qr), W))
+    y1 = orc.mla_forward_expanded(*args)
+    y2 = orc.mla_forward_absorbed(*args)
+    assert np.max(np.abs(y1 - y2)) > 1e-6
+
+
+def test_mutation_log2_lse_is_caught(monkeypatch):
+    class _NpLog2:
+        def __getattr__(self, k):
+            return getattr(np, k)
+        log = staticmethod(np.log2)
+    monkeypatch.setattr(orc, "np", _NpLog2())
+    case = make_decode_case([200], s_q=1, H=4, seed=22, dtype=torch.float32)
+    q, cache, table, L = _case_arrays(case)
+    _, lse = orc.decode_absorbed(np.zeros_like(q), cache, table, L, case.scale, False)
+    assert not np.allclose(lse, math.log(200), atol=1e-6)
+
+
+def test_mutation_wrong_value_columns_is_caught():
+    """V taken from the last 512 columns instead of the first 512."""
+    def decode_wrong_v(q, cache, table, L, scale, causal, dv=512):
+        return orc.decode_absorbed(q, cache[..., ::-1].copy(), table, L, scale, causal, dv)
+    case = _tiny_case(13, 1, [1, 13])
+    q, cache, table, L = _case_arrays(case)
+    o, _ = decode_wrong_v(q[..., ::-1].copy(), cache, table, L, case.scale, False, dv=12)
+    ob, _ = brute_decode(q, cache, table, L, case.scale, False, 12)
+    assert np.max(np.abs(o - ob)) > 1e-3
+
+
+def test_mutation_unnormalised_merge_is_caught():
+    def merge_wrong(o_parts, lse_parts):
+        M = lse_parts.max(axis=0)
+        w = np.exp(lse_parts - M)
+        return np.einsum("k...,k...d->...d", w, o_parts), M + np.log(w.sum(0))
+    case = make_decode_case([500, 130], s_q=1, H=4, seed=31, dtype=torch.bfloat16, q_scale=1.0)
+    err = check_split_merge(orc.decode_absorbed, orc.decode_partials, merge_wrong, case, 0)
+    assert err > 1e-3
