@@ -1,0 +1,198 @@
+"""Benchmark of absorbed-MLA decode on one MI355X.
+
+One step = one pass of the whole decode path over one batch: the split-KV
+decode kernel plus the LSE-combine kernel (mla_decode_fwd). The split plan is
+computed once per batch on the host (as a serving engine reuses it across
+layers) and its host time is reported separately.
+
+Workload: batched decode, B=64 sequences x 4096 cached tokens, s_q=1, H=128,
+key 576 (512 latent + 64 RoPE), value 512, bf16, pages of 64 tokens drawn from
+one shuffled pool; seeded synthetic inputs. Two copies of the cache and
+queries alternate between steps so no step finds the previous one's 302 MB of
+KV in the 256 MB last-level cache.
+
+Prints one JSON line. `roofline` describes the dominant kernel (the decode
+kernel): algorithmic bytes per launch over its average duration. That
+duration comes from HIP events on the library's stream: the step's average
+minus the average of the standalone combine kernel on the same partials.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode TFLOP/s & HBM GB/s (% roofline), H=128 d=576/512, B=64 ctx=4k"
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, budget_s: float = 15.0) -> dict:
+    """Time the fp64 oracle on as many whole sequences as fit in ~budget_s."""
+    import numpy as np
+
+    from mla_decode_fwd_amd import accounting as acc
+    from oracle import mla_oracle as orc
+
+    q = case.q_lat.double().numpy()
+    table = case.block_table.numpy()
+    L = case.seqlens.numpy()
+
+    def run(bs):
+        # Hand the oracle only the pages of the sampled sequences (fp64 copy
+        # made outside the timed region).
+        subs = []
+        for b in bs:
+            npg = (int(L[b]) + 63) // 64
+            subs.append((case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None]))
+        t0 = time.perf_counter()
+        for b, (c, t) in zip(bs, subs):
+            orc.decode_absorbed(q[b:b + 1], c, t, L[b:b + 1], case.scale, case.causal, dv=512)
+        return time.perf_counter() - t0
+
+    t1 = run([0])
+    n = int(max(1, min(case.B, budget_s / max(t1, 1e-3))))
+    secs = run(list(range(n)))
+    flops = acc.decode_flops(L[:n], case.s_q, case.H)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # threadpoolctl missing: count the cores we may run on
+        cores = len(os.sched_getaffinity(0))
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {case.B} sequences (ctx {int(L[0])}, H={case.H}), fp64 numpy, {secs:.1f} s",
+            "seconds": secs}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path runs on one MI355X and has no multi-GPU mode "
+              "(a data-parallel deployment gives each GPU its own sequences and caches).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_decode_fwd_amd as mla
+    from mla_decode_fwd_amd import accounting as acc
+    from mla_inputs import config_case
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mla.load_library()
+
+    case = config_case(2)
+    B, s_q, H = case.B, case.s_q, case.H
+    L = case.seqlens.tolist()
+    sets = []
+    npages = case.cache.shape[0]
+    for k in range(2):
+        # The second copy holds the same pages one slot further along the pool.
+        cache = case.cache if k == 0 else case.cache.roll(1, 0)
+        bt = case.block_table if k == 0 else ((case.block_table.long() + 1) % npages).to(torch.int32)
+        sets.append(dict(q=case.q_lat.to(dev), kv=cache.to(dev), bt=bt.to(dev), sl=case.seqlens.to(dev)))
+    t0 = time.perf_counter()
+    plan = mla.decode_plan(L, s_q, H)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    offs = plan.device_offsets(dev)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, s_q, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+
+    def step(i):
+        s = sets[i % 2]
+        mla.mla_decode_fwd(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal,
+                           split_offsets=offs, total_splits=plan.total_splits, workspace=ws, o_lat=o, lse=lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Standalone combine on the same partials: its average is subtracted from
+    # the step to give the decode kernel's own duration.
+    rows = plan.total_splits * s_q * H
+    o_part = ws[: rows * 512 * 4].view(torch.float32).view(plan.total_splits, s_q, H, 512)
+    lse_part = ws[rows * 512 * 4: rows * 513 * 4].view(torch.float32).view(plan.total_splits, s_q, H)
+    o2 = torch.empty_like(o)
+    l2 = torch.empty_like(lse)
+    for _ in range(3):
+        mla.mla_splitkv_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o2, l2)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        mla.mla_splitkv_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o2, l2)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    combine_ms = ev0.elapsed_time(ev1) / args.steps
+    decode_ms = max(step_gpu_ms - combine_ms, 1e-6)
+
+    flops = acc.decode_flops(L, s_q, H)
+    nbytes = acc.decode_bytes(L, s_q, H)
+    step_rf = acc.roofline(flops, nbytes, ms_per_step / 1e3)
+    dec_rf = acc.roofline(flops, nbytes, decode_ms / 1e3)
+    out = {
+        "metric": METRIC,
+        "value": round(step_rf["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=128, d_qk=576, d_v=512, "
+                               "bf16, 64-token pages in a shuffled pool",
+                   "B": B, "ctx": 4096, "s_q": s_q, "H": H, "splits_per_seq": int(plan.num_splits.max()),
+                   "parallelism": "single GPU"},
+        "hbm_gbs": round(step_rf["gbs"], 1),
+        "roofline_frac": round(step_rf["frac"], 4),
+        "roofline_frac_kv_only": round(acc.kv_bytes(L) / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),
+        "roofline": {"bound": dec_rf["bound"], "achieved": round(dec_rf["achieved"], 1),
+                     "peak": dec_rf["peak"], "unit": dec_rf["unit"], "frac": round(dec_rf["frac"], 4),
+                     "traffic": None, "kernel": "mla_decode_bf16_kernel",
+                     "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                     "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},
+        "plan_host_us": round(plan_us, 1),
+        "step_gpu_ms": round(step_gpu_ms, 5),
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

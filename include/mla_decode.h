@@ -1,0 +1,207 @@
+/*
+ * mla_decode.h - C ABI of the MI355X (gfx950) absorbed-MLA decode library.
+ *
+ * Multi-head Latent Attention decode on the weight-absorbed path. Every
+ * query head attends to ONE shared 576-wide key per cached token (the
+ * 512-wide latent c followed by the 64-wide decoupled RoPE key k^R) and ONE
+ * shared 512-wide value (the latent c itself, i.e. the first 512 elements of
+ * the same cache row).
+ *
+ * Sources (by page title and section):
+ *   [MLA-推理]  "MLA 推理：两条计算路径与 FlashMLA"
+ *               - section "两条等价的路径": the absorbed path. The query moves into
+ *                 latent space (q~ = W_UK q^N), the score is q~ᵀc + q^Rᵀk^R, the
+ *                 weighted sum stays in latent space and W_UV is applied last.
+ *                 The cache row per token per layer is 512 + 64 numbers.
+ *               - section "decode 注意力变成了计算问题": all heads share the key
+ *                 and value (an MQA with a very wide head), paged KV with pages of
+ *                 64 tokens, split-KV across compute units with a final merge of
+ *                 the partial results.
+ *               - section "谁快：看新 token 和缓存 token 的数量": new tokens follow
+ *                 the cached ones and the cached count includes them (causal pairs
+ *                 q*k - q(q-1)/2); chunk results are merged by their LSE.
+ *   [DSV2-MLA]  "DeepSeekV2之MLA", section 4.5 (forward_absorb: bmm of q_nope with
+ *               w_kc, attention as an MQA with a 576-wide key and 512-wide value,
+ *               bmm of the attention output with w_vc).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host. All tensors
+ *     are row-major and contiguous. The caller owns every buffer and the
+ *     stream; the library allocates nothing, keeps no state between calls and
+ *     may be called from several host threads at once.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     device work is enqueued on it asynchronously; no call synchronizes.
+ *   - Errors are reported only through the return code. All argument checks
+ *     that the host can make run before any HIP call, so an invalid call
+ *     enqueues nothing. A failed kernel launch returns MLA_ERR_HIP.
+ *   - Device-side data (sequence lengths, block-table entries, split offsets)
+ *     is not read by the host. Out-of-range values there give undefined
+ *     results, but the kernels clamp every index they derive from them, so
+ *     they never read or write outside the buffers the sizes describe.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size    */
+  MLA_ERR_UNSUPPORTED = 2, /* valid but not implemented: dims, dtype, page   */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
+  MLA_ERR_HIP = 4          /* a HIP launch or runtime call failed            */
+} mla_status_t;
+
+typedef enum {
+  MLA_BF16 = 0, /* bf16 storage, fp32 accumulation, bf16 output (RNE)         */
+  MLA_FP32 = 1  /* fp32 storage and arithmetic, fp32 output                   */
+} mla_dtype_t;
+
+/* Fixed shapes of the absorbed DeepSeek-V3 layout. */
+#define MLA_D_QK 576      /* key width: 512 latent + 64 RoPE                  */
+#define MLA_D_V 512       /* value width: the latent                          */
+#define MLA_PAGE_SIZE 64  /* tokens per cache page                            */
+#define MLA_MAX_SPLITS 64 /* most KV chunks one sequence may be split into    */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(mla_status_t status);
+
+/* Library ABI version, currently 1. */
+int mla_abi_version(void);
+
+/*
+ * Bytes of workspace mla_decode_fwd needs for `total_splits` work chunks:
+ * fp32 partial outputs [total_splits, s_q, H, 512] followed by fp32 partial
+ * LSEs [total_splits, s_q, H], rounded up to 256 bytes. Returns 0 for
+ * non-positive sizes.
+ */
+size_t mla_decode_workspace_size(int total_splits, int s_q, int H);
+
+/*
+ * Split planner (host only, no HIP call).
+ *
+ * Chooses how many KV chunks each sequence is cut into ([MLA-推理] section
+ * "decode 注意力变成了计算问题": long contexts and small batches are split along
+ * the KV axis over the compute units). Chunks are whole pages. The plan
+ * balances pages per workgroup over `num_cus` compute units: with P_b pages
+ * in sequence b and R = ceil(s_q*H/128) row groups, it targets about one
+ * wave of workgroups, giving each chunk close to sum(P_b)*R/num_cus pages,
+ * capped at `max_splits` (<= 64) chunks per sequence and at P_b.
+ *
+ *   seqlens_host[B]      L_b, tokens cached for sequence b INCLUDING its s_q
+ *                        new tokens; each must be >= s_q.
+ *   num_cus              compute units to fill (256 on MI355X; <= 0 means 256).
+ *   num_splits_host[B]   out: chunks per sequence, in [1, max_splits].
+ *   split_offsets_host   out: [B+1] exclusive prefix sum of num_splits_host;
+ *                        split_offsets_host[B] is total_splits.
+ *   workspace_bytes      out (may be NULL): mla_decode_workspace_size of the
+ *                        plan, or 0 when no sequence is split.
+ */
+mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H, int num_cus,
+                             int max_splits, int32_t* num_splits_host,
+                             int32_t* split_offsets_host, size_t* workspace_bytes);
+
+/*
+ * Absorbed-MLA decode: o_lat and LSE for every (sequence, new token, head).
+ *
+ * For sequence b with L_b cached tokens (counting its s_q new ones, which
+ * are the last s_q), query token i in [0, s_q) and head h:
+ *   K_j = kv_cache[block_table[b, j/64], j%64, 0:576]     (key of token j)
+ *   V_j = K_j[0:512]                                      (value of token j)
+ *   allowed keys: j < L_b, and j <= L_b - s_q + i if causal
+ *   s_j = softmax_scale * sum_k q_lat[b,i,h,k] * K_j[k]
+ *   o_lat[b,i,h,:] = sum_j softmax(s)_j * V_j
+ *   lse[b,i,h]     = ln sum_j exp(s_j)         (natural log)
+ * ([MLA-推理] sections "两条等价的路径" and "decode 注意力变成了计算问题";
+ *  softmax_scale is 1/sqrt(d_nope + d_rope) = 1/sqrt(192) for DeepSeek-V3.)
+ *
+ *   q_lat            [B, s_q, H, 576] dtype; q_lat[...,0:512] = W_UK q^N,
+ *                    q_lat[...,512:576] = RoPE(q^R) (see mla_absorb_q).
+ *   kv_cache         [num_pages, 64, 576] dtype; row = [c (512) ; k^R (64)],
+ *                    k^R already rotated. Slots no sequence owns are never read.
+ *   block_table      [B, max_pages_per_seq] int32 physical page ids; entries
+ *                    past ceil(L_b/64) are never read. Pages may sit anywhere
+ *                    in the pool and in any order.
+ *   seqlens          [B] int32 L_b (device), each in [s_q, 64*max_pages_per_seq].
+ *   split_offsets    [B+1] int32 (device) from mla_decode_plan, or NULL for one
+ *                    chunk per sequence. Sequence b is cut into
+ *                    n_b = split_offsets[b+1]-split_offsets[b] page-aligned
+ *                    chunks of near-equal page counts.
+ *   total_splits     split_offsets[B] (host copy), or B when split_offsets is NULL.
+ *   d_qk, d_v        must be 576 and 512.  page_size must be 64.
+ *   H                heads, 1..128.  s_q: new tokens per sequence, 1..16.
+ *   causal           nonzero: bottom-right causal mask among the s_q new tokens.
+ *   workspace        device scratch of at least
+ *                    mla_decode_workspace_size(total_splits, s_q, H) bytes when
+ *                    split_offsets != NULL (may be NULL otherwise). Its contents
+ *                    on entry are ignored; on return it holds the per-chunk
+ *                    partials in mla_splitkv_combine's input layout.
+ *   o_lat            out [B, s_q, H, 512] dtype.
+ *   lse              out [B, s_q, H] fp32 (natural log).
+ * Concurrent calls that share a workspace race; give each its own.
+ */
+mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,
+                            const int32_t* seqlens, const int32_t* split_offsets,
+                            int total_splits, int B, int s_q, int H, int d_qk, int d_v,
+                            int page_size, int max_pages_per_seq, int num_pages,
+                            float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes, void* o_lat, float* lse, void* stream);
+
+/*
+ * LSE merge of split-KV partial results ([MLA-推理] sections
+ * "谁快：看新 token 和缓存 token 的数量" and "decode 注意力变成了计算问题":
+ * the chunk results are merged by their log-sum-exp).
+ * For each (b, i, h), over the n_b chunks k of sequence b:
+ *   M = max_k lse_k;  lse = M + ln sum_k exp(lse_k - M);
+ *   o = sum_k exp(lse_k - lse) * o_k
+ * A chunk with lse_k = -inf (no allowed key) contributes nothing.
+ *
+ *   o_part     [total_splits, s_q, H, d_v] fp32, chunk-major: the chunks of
+ *              sequence b are rows split_offsets[b] .. split_offsets[b+1]-1.
+ *   lse_part   [total_splits, s_q, H] fp32, natural log.
+ *   split_offsets [B+1] int32 (device), total_splits = split_offsets[B].
+ *   d_v        must be 512.
+ *   o_lat      out [B, s_q, H, d_v] in out_dtype;  lse: out [B, s_q, H] fp32.
+ */
+mla_status_t mla_splitkv_combine(const float* o_part, const float* lse_part,
+                                 const int32_t* split_offsets, int total_splits, int B, int s_q,
+                                 int H, int d_v, mla_dtype_t out_dtype, void* o_lat, float* lse,
+                                 void* stream);
+
+/*
+ * Query absorption ([MLA-推理] section "两条等价的路径": q~ = W_UK q^N;
+ * [DSV2-MLA] section 4.5: the bmm of q_nope with w_kc):
+ *   q_lat[n,h,0:d_c]          = sum_d q_nope[n,h,d] * w_uk[h,c,d]
+ *   q_lat[n,h,d_c:d_c+d_rope] = q_rope[n,h,:]   (already rotated; copied)
+ *
+ *   q_nope [N, H, d_nope], q_rope [N, H, d_rope], w_uk [H, d_c, d_nope]
+ *   (the per-head latent-to-key matrix, latent rows), all in dtype;
+ *   q_lat out [N, H, d_c + d_rope] in dtype. Accumulation is fp32.
+ *   Sizes: N >= 1, 1 <= H <= 1024, 1 <= d_nope, d_c <= 4096, 0 <= d_rope <= 4096.
+ */
+mla_status_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int N, int H,
+                          int d_nope, int d_rope, int d_c, mla_dtype_t dtype, void* q_lat,
+                          void* stream);
+
+/*
+ * Output un-absorption ([MLA-推理] section "两条等价的路径": W_UV is applied
+ * after the weighted sum in latent space; [DSV2-MLA] section 4.5: the bmm of
+ * the attention output with w_vc):
+ *   out[n,h,e] = sum_c o_lat[n,h,c] * w_uv[h,c,e]
+ *
+ *   o_lat [N, H, d_c], w_uv [H, d_c, d_v], out [N, H, d_v], all in dtype;
+ *   fp32 accumulation. Sizes: N >= 1, 1 <= H <= 1024, 1 <= d_c, d_v <= 4096.
+ */
+mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d_c, int d_v,
+                        mla_dtype_t dtype, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

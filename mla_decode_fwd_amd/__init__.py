@@ -1,0 +1,282 @@
+"""Python binding of the MI355X absorbed-MLA decode library (libmla_decode.so).
+
+Thin ctypes marshalling over the C ABI in include/mla_decode.h: every function
+here checks tensor properties, allocates outputs with torch when the caller
+does not pass them, and calls the library entry point of the same name. All
+computation happens in the library's HIP kernels; there is no fallback. If
+the library is not built, every call raises.
+
+Tensors are torch tensors on the current HIP device (row-major, contiguous);
+work is enqueued on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "MlaError", "library_path", "load_library", "abi_version",
+    "decode_plan", "decode_workspace_size", "mla_decode_fwd", "mla_splitkv_combine",
+    "mla_absorb_q", "mla_out_uv", "DecodePlan",
+    "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS",
+]
+
+D_QK = 576
+D_V = 512
+PAGE_SIZE = 64
+MAX_SPLITS = 64
+
+MLA_BF16 = 0
+MLA_FP32 = 1
+_DTYPES = {torch.bfloat16: MLA_BF16, torch.float32: MLA_FP32}
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
+           3: "workspace missing or too small", 4: "HIP runtime error"}
+
+_LIB = None
+
+
+class MlaError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, 'unknown')} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+
+
+def load_library():
+    """Load libmla_decode.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with mla_decode_fwd_amd.build.build_library() "
+                           "(hipcc, gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "mla_status_string": ([I], ctypes.c_char_p),
+        "mla_abi_version": ([], I),
+        "mla_decode_workspace_size": ([I, I, I], Z),
+        "mla_decode_plan": ([P, I, I, I, I, I, P, P, P], I),
+        "mla_decode_fwd": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, Z, P, P, P], I),
+        "mla_splitkv_combine": ([P, P, P, I, I, I, I, I, I, P, P, P], I),
+        "mla_absorb_q": ([P, P, P, I, I, I, I, I, I, P, P], I),
+        "mla_out_uv": ([P, P, I, I, I, I, I, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().mla_abi_version()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MlaError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def decode_workspace_size(total_splits: int, s_q: int, H: int) -> int:
+    return int(load_library().mla_decode_workspace_size(int(total_splits), int(s_q), int(H)))
+
+
+class DecodePlan:
+    """A split plan: per-sequence chunk counts, their offsets and workspace size."""
+
+    def __init__(self, num_splits: np.ndarray, split_offsets: np.ndarray, workspace_bytes: int, s_q: int, H: int):
+        self.num_splits = num_splits
+        self.split_offsets = split_offsets
+        self.workspace_bytes = int(workspace_bytes)
+        self.s_q = s_q
+        self.H = H
+
+    @property
+    def total_splits(self) -> int:
+        return int(self.split_offsets[-1])
+
+    @property
+    def any_split(self) -> bool:
+        return bool((self.num_splits > 1).any())
+
+    def device_offsets(self, device) -> torch.Tensor:
+        return torch.from_numpy(self.split_offsets).to(device)
+
+
+def decode_plan(seqlens: Sequence[int], s_q: int, H: int, num_cus: int = 256,
+                max_splits: int = MAX_SPLITS) -> DecodePlan:
+    """Host split planner (mla_decode_plan)."""
+    L = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B = int(L.shape[0])
+    ns = np.zeros(B, dtype=np.int32)
+    off = np.zeros(B + 1, dtype=np.int32)
+    ws = ctypes.c_size_t(0)
+    st = load_library().mla_decode_plan(L.ctypes.data_as(ctypes.c_void_p), B, int(s_q), int(H), int(num_cus),
+                                        int(max_splits), ns.ctypes.data_as(ctypes.c_void_p),
+                                        off.ctypes.data_as(ctypes.c_void_p), ctypes.byref(ws))
+    _check("mla_decode_plan", st)
+    return DecodePlan(ns, off, ws.value, s_q, H)
+
+
+def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                   seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                   split_offsets: Optional[torch.Tensor] = None, total_splits: Optional[int] = None,
+                   workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None):
+    """Absorbed-MLA decode (mla_decode_fwd). Returns (o_lat [B,s_q,H,512], lse [B,s_q,H] fp32).
+
+    split_offsets: int32 device [B+1] from ``decode_plan`` (or None for one
+    chunk per sequence); total_splits: its last entry (host int).
+    """
+    if q_lat.dim() != 4 or kv_cache.dim() != 3 or block_table.dim() != 2 or seqlens.dim() != 1:
+        raise ValueError("expected q_lat [B,s_q,H,576], kv_cache [pages,64,576], block_table [B,P], seqlens [B]")
+    dev = q_lat.device
+    dtype = q_lat.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    _need(q_lat, "q_lat", device=dev)
+    _need(kv_cache, "kv_cache", dtype=dtype, device=dev)
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    _need(seqlens, "seqlens", dtype=torch.int32, device=dev)
+    B, s_q, H, dqk = q_lat.shape
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table and seqlens must have B rows")
+    if split_offsets is not None:
+        _need(split_offsets, "split_offsets", dtype=torch.int32, device=dev)
+        if split_offsets.shape[0] != B + 1:
+            raise ValueError("split_offsets must have B+1 entries")
+        if total_splits is None:
+            raise ValueError("total_splits (host copy of split_offsets[B]) is required")
+        if workspace is None:
+            nbytes = decode_workspace_size(total_splits, s_q, H)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    else:
+        total_splits = B
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, D_V), dtype=dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+    _need(o_lat, "o_lat", dtype=dtype, device=dev)
+    _need(lse, "lse", dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().mla_decode_fwd(
+        _ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets),
+        int(total_splits), B, s_q, H, dqk, int(o_lat.shape[-1]), int(kv_cache.shape[1]),
+        int(block_table.shape[1]), int(kv_cache.shape[0]), float(softmax_scale), int(bool(causal)),
+        _DTYPES[dtype], _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
+    _check("mla_decode_fwd", st)
+    return o_lat, lse
+
+
+def mla_splitkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offsets: torch.Tensor,
+                        total_splits: int, B: int, out_dtype: torch.dtype = torch.bfloat16,
+                        o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """LSE merge of chunk partials (mla_splitkv_combine).
+
+    o_part [total_splits, s_q, H, 512] fp32, lse_part [total_splits, s_q, H] fp32.
+    Returns (o_lat [B,s_q,H,512] out_dtype, lse [B,s_q,H] fp32).
+    """
+    dev = o_part.device
+    _need(o_part, "o_part", dtype=torch.float32)
+    _need(lse_part, "lse_part", dtype=torch.float32, device=dev)
+    _need(split_offsets, "split_offsets", dtype=torch.int32, device=dev)
+    if o_part.dim() != 4 or lse_part.shape != o_part.shape[:3] or o_part.shape[0] != total_splits:
+        raise ValueError("o_part must be [total_splits,s_q,H,512] and lse_part [total_splits,s_q,H]")
+    if out_dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {out_dtype}")
+    _, s_q, H, dv = o_part.shape
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, dv), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+    _need(o_lat, "o_lat", dtype=out_dtype, device=dev)
+    _need(lse, "lse", dtype=torch.float32, device=dev)
+    st = load_library().mla_splitkv_combine(_ptr(o_part), _ptr(lse_part), _ptr(split_offsets), int(total_splits),
+                                            int(B), s_q, H, dv, _DTYPES[out_dtype], _ptr(o_lat), _ptr(lse),
+                                            _stream())
+    _check("mla_splitkv_combine", st)
+    return o_lat, lse
+
+
+def mla_absorb_q(q_nope: torch.Tensor, q_rope: Optional[torch.Tensor], w_uk: torch.Tensor,
+                 q_lat: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_lat [N,H,d_c+d_rope] = [W_UK q_nope ; q_rope] (mla_absorb_q). w_uk is [H, d_c, d_nope]."""
+    dtype = q_nope.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    dev = q_nope.device
+    _need(q_nope, "q_nope", device=dev)
+    _need(w_uk, "w_uk", dtype=dtype, device=dev)
+    N, H, dn = q_nope.shape
+    Hw, dc, dn2 = w_uk.shape
+    if Hw != H or dn2 != dn:
+        raise ValueError("w_uk must be [H, d_c, d_nope]")
+    dr = 0
+    if q_rope is not None:
+        _need(q_rope, "q_rope", dtype=dtype, device=dev)
+        if q_rope.shape[:2] != (N, H):
+            raise ValueError("q_rope must be [N, H, d_rope]")
+        dr = q_rope.shape[2]
+    if q_lat is None:
+        q_lat = torch.empty((N, H, dc + dr), dtype=dtype, device=dev)
+    _need(q_lat, "q_lat", dtype=dtype, device=dev)
+    st = load_library().mla_absorb_q(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), N, H, dn, dr, dc,
+                                     _DTYPES[dtype], _ptr(q_lat), _stream())
+    _check("mla_absorb_q", st)
+    return q_lat
+
+
+def mla_out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out [N,H,d_v] = o_lat [N,H,d_c] . W_UV[h] (mla_out_uv). w_uv is [H, d_c, d_v]."""
+    dtype = o_lat.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    dev = o_lat.device
+    _need(o_lat, "o_lat", device=dev)
+    _need(w_uv, "w_uv", dtype=dtype, device=dev)
+    N, H, dc = o_lat.shape
+    if w_uv.shape[0] != H or w_uv.shape[1] != dc:
+        raise ValueError("w_uv must be [H, d_c, d_v]")
+    dv = w_uv.shape[2]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dtype, device=dev)
+    _need(out, "out", dtype=dtype, device=dev)
+    st = load_library().mla_out_uv(_ptr(o_lat), _ptr(w_uv), N, H, dc, dv, _DTYPES[dtype], _ptr(out), _stream())
+    _check("mla_out_uv", st)
+    return out

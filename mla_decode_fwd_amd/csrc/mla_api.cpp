@@ -1,0 +1,186 @@
+// C ABI of the absorbed-MLA decode library: argument checks, split planning
+// and kernel dispatch. Every check that the host can make runs before any HIP
+// call, so a rejected call enqueues nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "mla_decode.h"
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kMaxHeads = 128;
+constexpr int kMaxSq = 16;
+constexpr int kMaxBmmHeads = 1024;
+constexpr int kMaxBmmDim = 4096;
+
+mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+bool known_dtype(mla_dtype_t d) { return d == MLA_BF16 || d == MLA_FP32; }
+
+size_t workspace_size(long long total_splits, long long s_q, long long H) {
+  if (total_splits <= 0 || s_q <= 0 || H <= 0) return 0;
+  const size_t rows = (size_t)total_splits * (size_t)s_q * (size_t)H;
+  const size_t bytes = rows * (size_t)mla::kDv * sizeof(float) + rows * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int mla_abi_version(void) { return 1; }
+
+size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
+  return workspace_size(total_splits, s_q, H);
+}
+
+mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H, int num_cus,
+                             int max_splits, int32_t* num_splits_host,
+                             int32_t* split_offsets_host, size_t* workspace_bytes) {
+  if (!seqlens_host || !num_splits_host || !split_offsets_host) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0) return MLA_ERR_INVALID_ARG;
+  if (max_splits < 1 || max_splits > MLA_MAX_SPLITS) return MLA_ERR_INVALID_ARG;
+  if (num_cus <= 0) num_cus = 256;
+  long long total_pages = 0, max_pages = 0;
+  for (int b = 0; b < B; ++b) {
+    const long long L = seqlens_host[b];
+    if (L < s_q) return MLA_ERR_INVALID_ARG;
+    const long long P = (L + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+    total_pages += P;
+    if (P > max_pages) max_pages = P;
+  }
+  const long long row_groups = ((long long)s_q * H + mla::kRowsPerGroup - 1) / mla::kRowsPerGroup;
+  // Pages per chunk: one wave of workgroups over the compute units, but no
+  // finer than the split cap allows for the longest sequence.
+  long long chunk = (total_pages * row_groups + num_cus - 1) / num_cus;
+  const long long floor_by_cap = (max_pages + max_splits - 1) / max_splits;
+  if (chunk < floor_by_cap) chunk = floor_by_cap;
+  if (chunk < 1) chunk = 1;
+  long long total = 0;
+  bool any_split = false;
+  split_offsets_host[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    const long long P = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+    long long n = (P + chunk - 1) / chunk;
+    if (n < 1) n = 1;
+    if (n > max_splits) n = max_splits;
+    if (n > 1) any_split = true;
+    num_splits_host[b] = (int32_t)n;
+    total += n;
+    if (total > INT_MAX) return MLA_ERR_INVALID_ARG;
+    split_offsets_host[b + 1] = (int32_t)total;
+  }
+  if (workspace_bytes) *workspace_bytes = any_split ? workspace_size(total, s_q, H) : 0;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,
+                            const int32_t* seqlens, const int32_t* split_offsets,
+                            int total_splits, int B, int s_q, int H, int d_qk, int d_v,
+                            int page_size, int max_pages_per_seq, int num_pages,
+                            float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
+  if (!q_lat || !kv_cache || !block_table || !seqlens || !o_lat || !lse) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MLA_ERR_UNSUPPORTED;
+  if (d_qk != MLA_D_QK || d_v != MLA_D_V || page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (H > kMaxHeads || s_q > kMaxSq) return MLA_ERR_UNSUPPORTED;
+  if ((long long)max_pages_per_seq * MLA_PAGE_SIZE > INT_MAX) return MLA_ERR_INVALID_ARG;
+  if (split_offsets == nullptr) {
+    if (total_splits != B) return MLA_ERR_INVALID_ARG;
+  } else {
+    if (total_splits < B || (long long)total_splits > (long long)B * MLA_MAX_SPLITS)
+      return MLA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < workspace_size(total_splits, s_q, H)) return MLA_ERR_WORKSPACE;
+  }
+  mla::DecodeArgs a{};
+  a.q_lat = q_lat;
+  a.kv_cache = kv_cache;
+  a.block_table = block_table;
+  a.seqlens = seqlens;
+  a.split_offsets = split_offsets;
+  a.total_splits = total_splits;
+  a.B = B;
+  a.s_q = s_q;
+  a.H = H;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.scale = softmax_scale;
+  a.causal = causal ? 1 : 0;
+  a.o_lat = o_lat;
+  a.lse = lse;
+  if (split_offsets) {
+    const size_t rows = (size_t)total_splits * s_q * H;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = a.o_part + rows * mla::kDv;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == MLA_BF16 ? mla::launch_decode_bf16(a, st) : mla::launch_decode_fp32(a, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (split_offsets) {
+    e = mla::launch_combine(a.o_part, a.lse_part, split_offsets, total_splits, B, s_q, H, dtype == MLA_BF16,
+                            /*skip_single=*/true, o_lat, lse, st);
+  }
+  return from_hip(e);
+}
+
+mla_status_t mla_splitkv_combine(const float* o_part, const float* lse_part,
+                                 const int32_t* split_offsets, int total_splits, int B, int s_q,
+                                 int H, int d_v, mla_dtype_t out_dtype, void* o_lat, float* lse,
+                                 void* stream) {
+  if (!o_part || !lse_part || !split_offsets || !o_lat || !lse) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0) return MLA_ERR_INVALID_ARG;
+  if (total_splits < B || (long long)total_splits > (long long)B * MLA_MAX_SPLITS)
+    return MLA_ERR_INVALID_ARG;
+  if (!known_dtype(out_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (d_v != MLA_D_V) return MLA_ERR_UNSUPPORTED;
+  if ((long long)s_q * H > 65535LL * 4) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_combine(o_part, lse_part, split_offsets, total_splits, B, s_q, H,
+                                      out_dtype == MLA_BF16, /*skip_single=*/false, o_lat, lse,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int N, int H,
+                          int d_nope, int d_rope, int d_c, mla_dtype_t dtype, void* q_lat,
+                          void* stream) {
+  if (!q_nope || !w_uk || !q_lat || (d_rope > 0 && !q_rope)) return MLA_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || d_nope <= 0 || d_c <= 0 || d_rope < 0) return MLA_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MLA_ERR_UNSUPPORTED;
+  if (H > kMaxBmmHeads || d_nope > kMaxBmmDim || d_c > kMaxBmmDim || d_rope > kMaxBmmDim)
+    return MLA_ERR_UNSUPPORTED;
+  if ((long long)N > 65535LL * 64) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_absorb_q(q_nope, q_rope, w_uk, N, H, d_nope, d_rope, d_c,
+                                       dtype == MLA_BF16, q_lat, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d_c, int d_v,
+                        mla_dtype_t dtype, void* out, void* stream) {
+  if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || d_c <= 0 || d_v <= 0) return MLA_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MLA_ERR_UNSUPPORTED;
+  if (H > kMaxBmmHeads || d_c > kMaxBmmDim || d_v > kMaxBmmDim) return MLA_ERR_UNSUPPORTED;
+  if ((long long)N > 65535LL * 64) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_out_uv(o_lat, w_uv, N, H, d_c, d_v, dtype == MLA_BF16, out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// LSE merge of split-KV partial results, gfx950.
+//
+// "MLA 推理：两条计算路径与 FlashMLA", sections "谁快：看新 token 和缓存 token 的
+// 数量" and "decode 注意力变成了计算问题": chunk results are merged by their
+// log-sum-exp. For one (sequence, token, head) row with chunks k:
+//   M = max_k lse_k, lse = M + ln sum_k exp(lse_k - M),
+//   o = sum_k exp(lse_k - lse) o_k,
+// and a chunk with lse_k = -inf (no allowed key) adds nothing.
+//
+// One wave per row: lane k < n reads lse_k, two wave reductions give M and
+// the sum, then every lane owns 8 of the 512 columns and streams the chunks'
+// partial rows with 16-byte loads.
+
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(64 * kWaves) void combine_kernel(const float* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part,
+                                                              const int32_t* __restrict__ split_offsets,
+                                                              int rows, int total_splits,
+                                                              int skip_single, void* o_lat, float* lse) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x;
+  const int row = blockIdx.y * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  // Clamp so that malformed offsets can never index outside the partials.
+  const int s0 = min(max(split_offsets[b], 0), total_splits);
+  const int n = min(min(max(split_offsets[b + 1] - s0, 0), kMaxSplits), total_splits - s0);
+  if (n == 0 || (skip_single && n == 1)) return;
+
+  const float lk = lane < n ? lse_part[(size_t)(s0 + lane) * rows + row] : -INFINITY;
+  const float M = wave_max(lk);
+  const float Mf = (M == -INFINITY) ? 0.f : M;
+  const float w = (lane < n) ? expf(lk - Mf) : 0.f;
+  const float S = wave_sum(w);
+  const float lse_v = (S > 0.f) ? Mf + logf(S) : -INFINITY;
+  const float wn = (S > 0.f) ? w / S : 0.f;  // exp(lse_k - lse)
+
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n; ++k) {
+    const float wk = __shfl(wn, k, 64);
+    if (wk == 0.f) continue;  // wave-uniform: empty chunk
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(o_part + ((size_t)(s0 + k) * rows + row) * kDv) + 2 * lane;
+    acc0 += wk * src[0];
+    acc1 += wk * src[1];
+  }
+  if (kBf16) {
+    bf16x8_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = (__bf16)acc0[e];
+      v[4 + e] = (__bf16)acc1[e];
+    }
+    *(reinterpret_cast<bf16x8_t*>(reinterpret_cast<__bf16*>(o_lat) + ((size_t)b * rows + row) * kDv) + lane) = v;
+  } else {
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(o_lat) + ((size_t)b * rows + row) * kDv) + 2 * lane;
+    dst[0] = acc0;
+    dst[1] = acc1;
+  }
+  if (lane == 0) lse[(size_t)b * rows + row] = lse_v;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, const int32_t* split_offsets,
+                          int total_splits, int B, int s_q, int H, bool out_bf16, bool skip_single,
+                          void* o_lat, float* lse, hipStream_t stream) {
+  const int rows = s_q * H;
+  const dim3 grid((unsigned)B, (unsigned)((rows + kWaves - 1) / kWaves));
+  if (out_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(64 * kWaves), 0, stream, o_part, lse_part,
+                       split_offsets, rows, total_splits, skip_single ? 1 : 0, o_lat, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(64 * kWaves), 0, stream, o_part, lse_part,
+                       split_offsets, rows, total_splits, skip_single ? 1 : 0, o_lat, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,52 @@
+// Internal launch interfaces of the absorbed-MLA decode library (gfx950).
+// The C ABI (include/mla_decode.h) validates arguments and then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace mla {
+
+constexpr int kDqk = 576;       // key width: latent 512 + RoPE 64
+constexpr int kDv = 512;        // value width: the latent
+constexpr int kPage = 64;       // tokens per cache page
+constexpr int kMaxSplits = 64;  // chunks per sequence at most
+constexpr int kRowsPerGroup = 128;  // query rows (token, head) per workgroup
+
+// Arguments of one decode launch, already validated on the host.
+struct DecodeArgs {
+  const void* q_lat;            // [B, s_q, H, 576]
+  const void* kv_cache;         // [num_pages, 64, 576]
+  const int32_t* block_table;   // [B, max_pages]
+  const int32_t* seqlens;       // [B]
+  const int32_t* split_offsets; // [B+1] or nullptr (one chunk per sequence)
+  int total_splits;
+  int B, s_q, H;
+  int max_pages;
+  int num_pages;
+  float scale;
+  int causal;
+  float* o_part;    // [total_splits, s_q, H, 512] when split, else nullptr
+  float* lse_part;  // [total_splits, s_q, H]
+  void* o_lat;      // [B, s_q, H, 512]
+  float* lse;       // [B, s_q, H]
+};
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_fp32(const DecodeArgs& a, hipStream_t stream);
+
+// LSE merge. skip_single: sequences with one chunk were written directly by
+// the decode kernel and are left alone.
+hipError_t launch_combine(const float* o_part, const float* lse_part, const int32_t* split_offsets,
+                          int total_splits, int B, int s_q, int H, bool out_bf16, bool skip_single,
+                          void* o_lat, float* lse, hipStream_t stream);
+
+// Per-head small-M products. absorb: out[n,h,0:dc] = A[n,h,:] . W[h,c,:] and
+// the RoPE tail copied; out_uv: out[n,h,:] = A[n,h,:] . W[h,:,:].
+hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int N, int H,
+                           int dn, int dr, int dc, bool bf16, void* q_lat, hipStream_t stream);
+hipError_t launch_out_uv(const void* o_lat, const void* w_uv, int N, int H, int dc, int dv,
+                         bool bf16, void* out, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,84 @@
+"""Shared helpers for the GPU parity tests: run a decode case through the
+library and compare it element by element with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mla_decode_fwd_amd as mla
+from oracle import mla_oracle as orc
+
+# Tolerances. bf16 inputs: max-abs 2e-2 and relative L2 5e-3 on o_lat. fp32
+# inputs: 1e-5. The LSE bound is this suite's own: scores are exact products
+# of the bf16 inputs accumulated in fp32, so the LSE carries only fp32
+# rounding (measured ~1e-6), and 1e-4 leaves a wide margin.
+TOL = {
+    torch.bfloat16: dict(max_abs=2e-2, rel_l2=5e-3, lse=1e-4),
+    torch.float32: dict(max_abs=1e-5, rel_l2=1e-5, lse=1e-5),
+}
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def oracle(case, rows=None):
+    """Oracle result for every sequence (or the listed sequence indices)."""
+    q = to_np(case.q_lat)
+    cache = case.cache  # gathered per sequence inside the oracle
+    table = case.block_table.numpy()
+    L = case.seqlens.numpy()
+    idx = range(case.B) if rows is None else rows
+    outs, lses = [], []
+    for b in idx:
+        npg = (int(L[b]) + 63) // 64
+        pages = table[b, :npg]
+        sub_cache = to_np(cache[torch.from_numpy(pages.astype(np.int64))])
+        sub_table = np.arange(npg)[None, :]
+        o, lse = orc.decode_absorbed(q[b:b + 1], sub_cache, sub_table, L[b:b + 1], case.scale, case.causal,
+                                     dv=512)
+        outs.append(o[0])
+        lses.append(lse[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def to_device(case, dev="cuda"):
+    return dict(q_lat=case.q_lat.to(dev), kv_cache=case.cache.to(dev),
+                block_table=case.block_table.to(dev), seqlens=case.seqlens.to(dev))
+
+
+def run(case, plan="auto", dev_inputs=None, num_cus=256, max_splits=64, split_offsets=None):
+    """Decode on the GPU. plan: "auto" (library planner), None (one chunk per
+    sequence) or "custom" with explicit host split_offsets."""
+    d = dev_inputs or to_device(case)
+    kw = {}
+    if plan == "auto":
+        p = mla.decode_plan(case.seqlens.tolist(), case.s_q, case.H, num_cus=num_cus, max_splits=max_splits)
+        if p.any_split:
+            kw = dict(split_offsets=p.device_offsets("cuda"), total_splits=p.total_splits)
+    elif plan == "custom":
+        off = np.asarray(split_offsets, dtype=np.int32)
+        kw = dict(split_offsets=torch.from_numpy(off).cuda(), total_splits=int(off[-1]))
+    o, lse = mla.mla_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale,
+                                case.causal, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
+    """Assert parity; return the error statistics."""
+    o = to_np(o_gpu)
+    lse = to_np(lse_gpu)
+    assert np.all(np.isfinite(o)), f"{label}: non-finite output"
+    assert np.all(np.isfinite(lse)), f"{label}: non-finite lse"
+    diff = o - o_ref
+    max_abs = float(np.max(np.abs(diff)))
+    rel_l2 = float(np.linalg.norm(diff) / max(np.linalg.norm(o_ref), 1e-30))
+    lse_err = float(np.max(np.abs(lse - lse_ref)))
+    t = TOL[dtype]
+    stats = dict(max_abs=max_abs, rel_l2=rel_l2, lse=lse_err)
+    print(f"[parity] {label} max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} lse={lse_err:.3e}", flush=True)
+    assert max_abs <= t["max_abs"], (label, stats)
+    assert rel_l2 <= t["rel_l2"], (label, stats)
+    assert lse_err <= t["lse"], (label, stats)
+    return stats

@@ -1,0 +1,134 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and host-side planning and argument validation behave as the header
+documents. Nothing here launches device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import mla_decode_fwd_amd as mla
+from mla_decode_fwd_amd import accounting
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"mla_decode_fwd", "mla_splitkv_combine", "mla_absorb_q", "mla_out_uv",
+            "mla_decode_plan"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings_and_version(lib):
+    assert mla.abi_version() == 1
+    for code in range(5):
+        assert lib.mla_status_string(code)
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def test_workspace_size(lib):
+    assert mla.decode_workspace_size(256, 1, 128) == 256 * 128 * 513 * 4
+    assert mla.decode_workspace_size(0, 1, 128) == 0
+    assert mla.decode_workspace_size(3, 2, 5) % 256 == 0
+
+
+def test_plan_headline_batch_fills_the_chip():
+    p = mla.decode_plan([4096] * 64, s_q=1, H=128)
+    assert (p.num_splits == 4).all() and p.total_splits == 256
+    assert p.workspace_bytes == mla.decode_workspace_size(256, 1, 128)
+    assert np.array_equal(p.split_offsets, np.arange(65) * 4)
+
+
+def test_plan_long_context_respects_cap_and_balances():
+    lens = [65536, 32768, 16384, 8192, 4096, 2048, 1024, 513]
+    p = mla.decode_plan(lens, s_q=1, H=128)
+    assert p.num_splits.max() <= 64 and p.num_splits.min() >= 1
+    assert p.num_splits[0] == 64
+    pages = [(L + 63) // 64 for L in lens]
+    per_chunk = max(-(-P // n) for P, n in zip(pages, p.num_splits))
+    assert per_chunk == 16  # the longest sequence bounds the chunk size
+    assert p.split_offsets[-1] == p.num_splits.sum()
+
+
+def test_plan_single_short_sequence_is_not_split():
+    p = mla.decode_plan([100], s_q=1, H=128, num_cus=1)
+    assert p.total_splits == 1 and p.workspace_bytes == 0 and not p.any_split
+
+
+def test_plan_invalid_arguments(lib):
+    L = np.array([10, 3], dtype=np.int32)
+    ns = np.zeros(2, np.int32)
+    off = np.zeros(3, np.int32)
+    c = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.mla_decode_plan(c(L), 2, 4, 128, 256, 64, c(ns), c(off), None) == INVALID  # L < s_q
+    assert lib.mla_decode_plan(c(L), 2, 1, 128, 256, 65, c(ns), c(off), None) == INVALID
+    assert lib.mla_decode_plan(c(L), 2, 1, 128, 256, 0, c(ns), c(off), None) == INVALID
+    assert lib.mla_decode_plan(None, 2, 1, 128, 256, 64, c(ns), c(off), None) == INVALID
+    assert lib.mla_decode_plan(c(L), 0, 1, 128, 256, 64, c(ns), c(off), None) == INVALID
+    assert lib.mla_decode_plan(c(L), 2, 1, 128, 256, 64, c(ns), c(off), None) == OK
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, so=None, total=2, B=2, s_q=1, H=128, dqk=576, dv=512,
+             page=64, maxp=4, npages=8, scale=0.0722, causal=0, dtype=0, ws=None, wsb=0, o=FAKE,
+             lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_fwd(a["q"], a["kv"], a["bt"], a["sl"], a["so"], a["total"], a["B"], a["s_q"],
+                              a["H"], a["dqk"], a["dv"], a["page"], a["maxp"], a["npages"], a["scale"],
+                              a["causal"], a["dtype"], a["ws"], a["wsb"], a["o"], a["lse"], None)
+
+
+def test_decode_fwd_validation(lib):
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, lse=None) == INVALID
+    assert _fwd(lib, B=0) == INVALID
+    assert _fwd(lib, npages=0) == INVALID
+    assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, dqk=128) == UNSUPPORTED
+    assert _fwd(lib, dv=128) == UNSUPPORTED
+    assert _fwd(lib, page=16) == UNSUPPORTED
+    assert _fwd(lib, H=129) == UNSUPPORTED
+    assert _fwd(lib, s_q=17) == UNSUPPORTED
+    assert _fwd(lib, dtype=7) == UNSUPPORTED
+    assert _fwd(lib, total=3) == INVALID  # no split offsets: one chunk per sequence
+    assert _fwd(lib, so=FAKE, total=1) == INVALID  # fewer chunks than sequences
+    assert _fwd(lib, so=FAKE, total=129) == INVALID  # more than 64 per sequence
+    assert _fwd(lib, so=FAKE, total=4, ws=None, wsb=1 << 30) == WORKSPACE
+    need = mla.decode_workspace_size(4, 1, 128)
+    assert _fwd(lib, so=FAKE, total=4, ws=FAKE, wsb=need - 1) == WORKSPACE
+
+
+def test_combine_and_bmm_validation(lib):
+    assert lib.mla_splitkv_combine(None, FAKE, FAKE, 2, 2, 1, 128, 512, 0, FAKE, FAKE, None) == INVALID
+    assert lib.mla_splitkv_combine(FAKE, FAKE, FAKE, 1, 2, 1, 128, 512, 0, FAKE, FAKE, None) == INVALID
+    assert lib.mla_splitkv_combine(FAKE, FAKE, FAKE, 2, 2, 1, 128, 256, 0, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.mla_splitkv_combine(FAKE, FAKE, FAKE, 2, 2, 1, 128, 512, 5, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.mla_absorb_q(FAKE, None, FAKE, 4, 128, 128, 64, 512, 0, FAKE, None) == INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 0, 128, 128, 64, 512, 0, FAKE, None) == INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 4, 128, 128, 64, 8192, 0, FAKE, None) == UNSUPPORTED
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 4, 128, 128, 64, 512, 9, FAKE, None) == UNSUPPORTED
+    assert lib.mla_out_uv(FAKE, None, 4, 128, 512, 128, 0, FAKE, None) == INVALID
+    assert lib.mla_out_uv(FAKE, FAKE, 4, 2000, 512, 128, 0, FAKE, None) == UNSUPPORTED

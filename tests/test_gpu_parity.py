@@ -1,0 +1,248 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs. Every unused cache slot is NaN, so any read
+outside a sequence's tokens shows up as a non-finite output."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_decode_fwd_amd as mla
+from mla_inputs import config_case, make_decode_case, tiny_mla_weights
+from oracle import mla_oracle as orc
+from gpu_helpers import TOL, compare, oracle, run, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load_library()
+
+
+# ---------------------------------------------------------------------------
+# Small cases: several pages, ragged tails, every split path.
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # (seqlens, s_q, H)
+    ([1], 1, 128),
+    ([64], 1, 128),
+    ([65], 1, 128),
+    ([300, 64, 129, 7], 1, 128),
+    ([130, 5, 64], 2, 128),
+    ([200, 3, 77], 3, 64),
+    ([513, 100], 4, 32),
+    ([70, 70], 1, 16),
+    ([190], 16, 8),
+    ([33, 250], 1, 1),
+]
+
+
+@pytest.mark.parametrize("plan", ["auto", None])
+@pytest.mark.parametrize("lens,s_q,H", SMALL)
+def test_small_bf16(lens, s_q, H, plan):
+    case = make_decode_case(lens, s_q=s_q, H=H, seed=100 + s_q * 7 + H + len(lens))
+    o, lse = run(case, plan=plan, num_cus=8)
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, f"small {lens} s_q={s_q} H={H} plan={plan}")
+
+
+@pytest.mark.parametrize("lens,s_q,H", [([300, 64, 129, 7], 1, 128), ([130, 5, 64], 2, 128)])
+def test_small_bf16_sharp_softmax(lens, s_q, H):
+    """Unscaled queries: score std ~1.7, so a wrong or missing key shows."""
+    case = make_decode_case(lens, s_q=s_q, H=H, seed=7, q_scale=1.0)
+    o, lse = run(case, plan="auto", num_cus=8)
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, f"sharp {lens}")
+
+
+def test_small_fp32():
+    case = make_decode_case([300, 64, 129, 7], s_q=2, H=16, seed=9, dtype=torch.float32, q_scale=1.0)
+    for plan in ("auto", None):
+        o, lse = run(case, plan=plan, num_cus=8)
+        o_ref, l_ref = oracle(case)
+        compare(o, lse, o_ref, l_ref, torch.float32, f"fp32 plan={plan}")
+
+
+def test_chunks_with_no_pages_and_max_splits():
+    """Explicit offsets: 64 chunks over 3 pages (most empty) and 1-page chunks."""
+    case = make_decode_case([150, 64 * 64], s_q=1, H=128, seed=11)
+    o, lse = run(case, plan="custom", split_offsets=[0, 64, 128])
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, "custom splits")
+
+
+# ---------------------------------------------------------------------------
+# The workload shapes at full size, in the launch configuration the bench uses.
+# ---------------------------------------------------------------------------
+
+def test_single_sequence_4096():
+    case = config_case(1)
+    o, lse = run(case)
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, case.name)
+
+
+def test_batched_64x4096():
+    case = config_case(2)
+    o, lse = run(case)
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, case.name)
+
+
+def test_mtp_two_tokens_sampled():
+    case = config_case(3)
+    o, lse = run(case)
+    L = case.seqlens.numpy()
+    rng = np.random.default_rng(0)
+    sample = sorted(set([int(np.argmax(L)), int(np.argmin(L))] + rng.choice(case.B, 14, replace=False).tolist()))
+    o_ref, l_ref = oracle(case, rows=sample)
+    compare(o[sample], lse[sample], o_ref, l_ref, torch.bfloat16, case.name + f" ({len(sample)} sampled)")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_long_context_varlen():
+    case = config_case(4)
+    o, lse = run(case)
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, case.name)
+
+
+# ---------------------------------------------------------------------------
+# Invariants on the GPU
+# ---------------------------------------------------------------------------
+
+def test_page_permutation_and_determinism_bitwise():
+    case = make_decode_case([700, 333, 64], s_q=2, H=128, seed=21)
+    o1, l1 = run(case)
+    o1b, l1b = run(case)
+    assert torch.equal(o1, o1b) and torch.equal(l1, l1b), "two runs differ"
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(case.cache.shape[0]).astype(np.int64))
+    cache2 = torch.empty_like(case.cache)
+    cache2[perm] = case.cache
+    table2 = perm[case.block_table.long()].to(torch.int32)
+    case2 = make_decode_case([700, 333, 64], s_q=2, H=128, seed=21)
+    case2.cache, case2.block_table = cache2, table2
+    o2, l2 = run(case2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "page permutation changed the output"
+
+
+def test_split_invariance():
+    case = make_decode_case([2000, 1500, 700], s_q=1, H=128, seed=22)
+    o_ref, l_ref = oracle(case)
+    outs = []
+    for num_cus, ms in [(1, 64), (16, 64), (256, 64), (256, 4)]:
+        o, lse = run(case, num_cus=num_cus, max_splits=ms)
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"num_cus={num_cus} max_splits={ms}")
+        outs.append((o.float(), lse))
+    for o, lse in outs[1:]:
+        assert (o - outs[0][0]).abs().max().item() < 4e-3
+        assert (lse - outs[0][1]).abs().max().item() < 1e-4
+
+
+def test_head_permutation_and_sequence_independence():
+    case = make_decode_case([400, 257], s_q=1, H=128, seed=23)
+    o1, l1 = run(case)
+    hp = torch.from_numpy(np.random.default_rng(6).permutation(128))
+    case_p = make_decode_case([400, 257], s_q=1, H=128, seed=23)
+    case_p.q_lat = case.q_lat[:, :, hp].contiguous()
+    o2, l2 = run(case_p)
+    assert torch.equal(o2, o1[:, :, hp]) and torch.equal(l2, l1[:, :, hp])
+    case_s = make_decode_case([400, 257], s_q=1, H=128, seed=23)
+    case_s.q_lat = case.q_lat.clone()
+    case_s.q_lat[1] = -case_s.q_lat[1]
+    o3, l3 = run(case_s, plan=None)
+    o1n, l1n = run(case, plan=None)
+    assert torch.equal(o3[0], o1n[0]) and torch.equal(l3[0], l1n[0])
+
+
+# ---------------------------------------------------------------------------
+# Combine and the bmm helpers
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_splitkv_combine(out_dtype):
+    rng = np.random.default_rng(31)
+    counts = [1, 3, 64, 2]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    S, s_q, H = int(off[-1]), 2, 16
+    o_part = rng.standard_normal((S, s_q, H, 512)).astype(np.float32)
+    lse_part = (rng.standard_normal((S, s_q, H)) * 3).astype(np.float32)
+    lse_part[1, 0, :4] = -np.inf  # empty chunks
+    lse_part[5:9, 1, 3] = -np.inf
+    o_gpu, l_gpu = mla.mla_splitkv_combine(torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda(),
+                                           torch.from_numpy(off).cuda(), S, len(counts), out_dtype)
+    torch.cuda.synchronize()
+    o_ref = np.zeros((len(counts), s_q, H, 512))
+    l_ref = np.zeros((len(counts), s_q, H))
+    for b in range(len(counts)):
+        o_ref[b], l_ref[b] = orc.lse_merge(o_part[off[b]:off[b + 1]], lse_part[off[b]:off[b + 1]])
+    o = to_np(o_gpu)
+    err = np.abs(o - o_ref)
+    if out_dtype == torch.float32:
+        # fp32 sums of up to 64 weighted unit-size partials: ~64 * 2^-24 absolute.
+        assert err.max() <= 1e-5
+    else:
+        # bf16 output: round-to-nearest-even costs at most half an ulp (2^-9 relative).
+        assert np.max(err / (np.abs(o_ref) + 1e-2)) <= 2 ** -8
+    assert np.max(np.abs(to_np(l_gpu) - l_ref)) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_absorb_q_and_out_uv_deepseek_shape(dtype):
+    rng = np.random.default_rng(41)
+    N, H, dn, dr, dc, dv = 64, 128, 128, 64, 512, 128
+    q_n = torch.from_numpy(rng.standard_normal((N, H, dn), dtype=np.float32)).to(dtype)
+    q_r = torch.from_numpy(rng.standard_normal((N, H, dr), dtype=np.float32)).to(dtype)
+    w_uk = torch.from_numpy(rng.standard_normal((H, dc, dn), dtype=np.float32) / 11).to(dtype)
+    w_uv = torch.from_numpy(rng.standard_normal((H, dc, dv), dtype=np.float32) / 22).to(dtype)
+    o_lat = torch.from_numpy(rng.standard_normal((N, H, dc), dtype=np.float32)).to(dtype)
+    ql = mla.mla_absorb_q(q_n.cuda(), q_r.cuda(), w_uk.cuda())
+    ou = mla.mla_out_uv(o_lat.cuda(), w_uv.cuda())
+    torch.cuda.synchronize()
+    ql_ref = orc.absorb_q(to_np(q_n), to_np(q_r), to_np(w_uk))
+    ou_ref = orc.out_uv(to_np(o_lat), to_np(w_uv))
+    for got, ref, name in [(ql, ql_ref, "absorb_q"), (ou, ou_ref, "out_uv")]:
+        g = to_np(got)
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        mx = np.max(np.abs(g - ref))
+        print(f"[parity] {name} {dtype} rel_l2={rel:.3e} max_abs={mx:.3e}", flush=True)
+        if dtype == torch.float32:
+            assert rel < 1e-6 and mx < 1e-4
+        else:
+            assert rel < 5e-3 and mx < 2e-2 * max(1.0, np.abs(ref).max())
+    assert torch.equal(ql[..., dc:].cpu(), q_r)  # the RoPE tail is copied unchanged
+
+
+def test_tiny_full_mla_fp32_end_to_end():
+    """The tiny full MLA of the worked example, absorbed path on the GPU:
+    mla_absorb_q -> mla_decode_fwd (fp32, latent and RoPE zero-padded to
+    512 + 64) -> mla_out_uv, then W_o; against the oracle's expanded path."""
+    w = tiny_mla_weights(0)
+    T, H, NOPE, ROPE, DC = w["T"], w["H"], w["NOPE"], w["ROPE"], w["DC"]
+    q_n, q_r, c, k_r = orc.project(w["h"], w["W_q"], w["W_dkv"], w["W_kr"], H, NOPE, ROPE)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    q_lat_small = mla.mla_absorb_q(f32(q_n), f32(q_r), f32(w["W_uk"]))  # [T,H,DC+ROPE]
+    q_lat = torch.zeros((1, T, H, 576), dtype=torch.float32, device="cuda")
+    q_lat[0, :, :, :DC] = q_lat_small[..., :DC]
+    q_lat[0, :, :, 512:512 + ROPE] = q_lat_small[..., DC:]
+    cache = torch.full((2, 64, 576), float("nan"), dtype=torch.float32, device="cuda")
+    cache[1, :T] = 0.0
+    cache[1, :T, :DC] = f32(c)
+    cache[1, :T, 512:512 + ROPE] = f32(k_r)
+    table = torch.tensor([[1]], dtype=torch.int32, device="cuda")
+    seqlens = torch.tensor([T], dtype=torch.int32, device="cuda")
+    o_lat, lse = mla.mla_decode_fwd(q_lat, cache, table, seqlens, 1 / math.sqrt(NOPE + ROPE), True)
+    o_small = o_lat[0, :, :, :DC].contiguous()
+    out = mla.mla_out_uv(o_small, f32(w["W_uv"]))  # [T,H,DV]
+    torch.cuda.synchronize()
+    y_gpu = to_np(out).reshape(T, -1) @ w["W_o"].astype(np.float64)
+    y_ref = orc.mla_forward_expanded(w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["W_uk"], w["W_uv"], w["W_o"],
+                                     H, NOPE, ROPE)
+    err = np.max(np.abs(y_gpu - y_ref))
+    print(f"[parity] tiny full MLA fp32 max_abs={err:.3e}", flush=True)
+    assert err <= 1e-5
+    assert torch.isfinite(o_lat).all()
