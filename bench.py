@@ -1,9 +1,10 @@
 """Benchmark of absorbed-MLA decode on one MI355X.
 
 One step = one pass of the whole decode path over one batch: the split-KV
-decode kernel plus the LSE-combine kernel (mla_decode_fwd). The split plan is
-computed once per batch on the host (as a serving engine reuses it across
-layers) and its host time is reported separately.
+decode kernel (mla_decode_fwd writing the chunk partials) and the LSE-combine
+kernel (mla_splitkv_combine) that merges them into o_lat and the LSE. The
+split plan is computed once per batch on the host (as a serving engine reuses
+it across layers) and its host time is reported separately.
 
 Workload: batched decode, B=64 sequences x 4096 cached tokens, s_q=1, H=128,
 key 576 (512 latent + 64 RoPE), value 512, bf16, pages of 64 tokens drawn from
@@ -12,11 +13,19 @@ queries alternate between steps so no step finds the previous one's 302 MB of
 KV in the 256 MB last-level cache.
 
 Prints one JSON line. `roofline` describes the dominant kernel (the decode
-kernel): algorithmic bytes per launch over its average duration. That
-duration comes from HIP events on the library's stream: the step's average
-minus the average of the standalone combine kernel on the same partials.
+kernel): algorithmic bytes per launch over its average duration, taken from
+HIP events recorded around each decode launch of the timed steps on the
+stream the library launches on. `traffic` (measured HBM bytes per launch) is
+the scaled FETCH_SIZE + WRITE_SIZE reading kept in
+profiles/mla_decode_bf16_b64_ctx4096.md (made by
+mla_decode_fwd_amd.profile_summary from rocprofv3 counter runs of this
+script); it is null when the decode kernel's source no longer has the hash
+recorded there, i.e. when the kernel changed after the counters were taken.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload on this host's cores.
+
+--copy-mb N adds, after the timed steps, three plain device-to-device copies
+of N MiB: a kernel of known traffic, for scaling the memory counters.
 """
 from __future__ import annotations
 
@@ -37,8 +46,32 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+PROFILE = os.path.join(ROOT, "profiles", "mla_decode_bf16_b64_ctx4096.md")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    from mla_decode_fwd_amd.profile_summary import decode_source_sha256
+
+    if not os.path.exists(PROFILE):
+        return None
+    fields = {}
+    for line in open(PROFILE, encoding="utf-8"):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != decode_source_sha256():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(case, budget_s: float = 15.0) -> dict:
-    """Time the fp64 oracle on as many whole sequences as fit in ~budget_s."""
+    """Time the fp64 oracle on whole sequences of the batch, in order and
+    wrapping around, until about budget_s seconds of work are done."""
     import numpy as np
 
     from mla_decode_fwd_amd import accounting as acc
@@ -48,22 +81,23 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     table = case.block_table.numpy()
     L = case.seqlens.numpy()
 
-    def run(bs):
-        # Hand the oracle only the pages of the sampled sequences (fp64 copy
-        # made outside the timed region).
-        subs = []
-        for b in bs:
-            npg = (int(L[b]) + 63) // 64
-            subs.append((case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None]))
+    # Hand the oracle only the pages of each sequence (fp64 copies made
+    # outside the timed region).
+    subs = []
+    for b in range(case.B):
+        npg = (int(L[b]) + 63) // 64
+        subs.append((case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None]))
+    done = []
+    secs = 0.0
+    while secs < budget_s:
+        b = len(done) % case.B
+        c, t = subs[b]
         t0 = time.perf_counter()
-        for b, (c, t) in zip(bs, subs):
-            orc.decode_absorbed(q[b:b + 1], c, t, L[b:b + 1], case.scale, case.causal, dv=512)
-        return time.perf_counter() - t0
-
-    t1 = run([0])
-    n = int(max(1, min(case.B, budget_s / max(t1, 1e-3))))
-    secs = run(list(range(n)))
-    flops = acc.decode_flops(L[:n], case.s_q, case.H)
+        orc.decode_absorbed(q[b:b + 1], c, t, L[b:b + 1], case.scale, case.causal, dv=512)
+        secs += time.perf_counter() - t0
+        done.append(b)
+    n = len(done)
+    flops = acc.decode_flops(L[done], case.s_q, case.H)
     try:
         from threadpoolctl import threadpool_info
 
@@ -71,7 +105,8 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     except Exception:  # threadpoolctl missing: count the cores we may run on
         cores = len(os.sched_getaffinity(0))
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {case.B} sequences (ctx {int(L[0])}, H={case.H}), fp64 numpy, {secs:.1f} s",
+            "sample": f"{n} sequence decodes ({n / case.B:.2f} passes over the B={case.B} batch, ctx {int(L[0])}, "
+                      f"H={case.H}), fp64 numpy, {secs:.1f} s",
             "seconds": secs}
 
 
@@ -82,6 +117,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-mb", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path runs on one MI355X and has no multi-GPU mode "
@@ -113,47 +149,49 @@ def main():
     plan_us = (time.perf_counter() - t0) * 1e6
     offs = plan.device_offsets(dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    o_part, lse_part = mla.workspace_partials(ws, plan.total_splits, s_q, H)
     o = torch.empty((B, s_q, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()  # the library launches on it
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
-    def step(i):
+    def step(i, events=None):
         s = sets[i % 2]
+        if events:
+            events[0].record(stream)
         mla.mla_decode_fwd(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal,
-                           split_offsets=offs, total_splits=plan.total_splits, workspace=ws, o_lat=o, lse=lse)
+                           split_offsets=offs, total_splits=plan.total_splits, workspace=ws, partials_only=True)
+        if events:
+            events[1].record(stream)
+            events[2].record(stream)
+        mla.mla_splitkv_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o, lse)
+        if events:
+            events[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i, ev[i])
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+    decode_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    combine_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
 
-    # Standalone combine on the same partials: its average is subtracted from
-    # the step to give the decode kernel's own duration.
-    rows = plan.total_splits * s_q * H
-    o_part = ws[: rows * 512 * 4].view(torch.float32).view(plan.total_splits, s_q, H, 512)
-    lse_part = ws[rows * 512 * 4: rows * 513 * 4].view(torch.float32).view(plan.total_splits, s_q, H)
-    o2 = torch.empty_like(o)
-    l2 = torch.empty_like(lse)
-    for _ in range(3):
-        mla.mla_splitkv_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o2, l2)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        mla.mla_splitkv_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o2, l2)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    combine_ms = ev0.elapsed_time(ev1) / args.steps
-    decode_ms = max(step_gpu_ms - combine_ms, 1e-6)
+    if args.copy_mb > 0:
+        n = args.copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        _log(f"copy calibration: 3 device copies of {n} bytes")
 
     flops = acc.decode_flops(L, s_q, H)
     nbytes = acc.decode_bytes(L, s_q, H)
@@ -181,7 +219,7 @@ def main():
         "roofline_frac_kv_only": round(acc.kv_bytes(L) / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),
         "roofline": {"bound": dec_rf["bound"], "achieved": round(dec_rf["achieved"], 1),
                      "peak": dec_rf["peak"], "unit": dec_rf["unit"], "frac": round(dec_rf["frac"], 4),
-                     "traffic": None, "kernel": "mla_decode_bf16_kernel",
+                     "traffic": measured_traffic(), "kernel": "mla_decode_bf16_kernel",
                      "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},

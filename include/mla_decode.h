@@ -123,7 +123,8 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
  *   q_lat            [B, s_q, H, 576] dtype; q_lat[...,0:512] = W_UK q^N,
  *                    q_lat[...,512:576] = RoPE(q^R) (see mla_absorb_q).
  *   kv_cache         [num_pages, 64, 576] dtype; row = [c (512) ; k^R (64)],
- *                    k^R already rotated. Slots no sequence owns are never read.
+ *                    k^R already rotated. Slots no sequence owns never affect
+ *                    the result (the tail of a last page may be loaded, then ignored).
  *   block_table      [B, max_pages_per_seq] int32 physical page ids; entries
  *                    past ceil(L_b/64) are never read. Pages may sit anywhere
  *                    in the pool and in any order.
@@ -140,9 +141,15 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
  *                    mla_decode_workspace_size(total_splits, s_q, H) bytes when
  *                    split_offsets != NULL (may be NULL otherwise). Its contents
  *                    on entry are ignored; on return it holds the per-chunk
- *                    partials in mla_splitkv_combine's input layout.
+ *                    partials in mla_splitkv_combine's input layout: o_part
+ *                    at byte 0, lse_part at byte total_splits*s_q*H*512*4.
  *   o_lat            out [B, s_q, H, 512] dtype.
  *   lse              out [B, s_q, H] fp32 (natural log).
+ *                    o_lat and lse may both be NULL when split_offsets is
+ *                    given: then only the per-chunk partials are written (for
+ *                    every chunk, including sequences with one chunk) and no
+ *                    merge runs; mla_splitkv_combine on the workspace finishes
+ *                    the job. One of the two NULL is MLA_ERR_INVALID_ARG.
  * Concurrent calls that share a workspace race; give each its own.
  */
 mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,

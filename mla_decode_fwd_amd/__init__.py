@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "MlaError", "library_path", "load_library", "abi_version",
     "decode_plan", "decode_workspace_size", "mla_decode_fwd", "mla_splitkv_combine",
-    "mla_absorb_q", "mla_out_uv", "DecodePlan",
+    "mla_absorb_q", "mla_out_uv", "DecodePlan", "workspace_partials",
     "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS",
 ]
 
@@ -156,11 +156,14 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
                    seqlens: torch.Tensor, softmax_scale: float, causal: bool,
                    split_offsets: Optional[torch.Tensor] = None, total_splits: Optional[int] = None,
                    workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None):
+                   lse: Optional[torch.Tensor] = None, partials_only: bool = False):
     """Absorbed-MLA decode (mla_decode_fwd). Returns (o_lat [B,s_q,H,512], lse [B,s_q,H] fp32).
 
     split_offsets: int32 device [B+1] from ``decode_plan`` (or None for one
     chunk per sequence); total_splits: its last entry (host int).
+    partials_only (needs split_offsets): write only the per-chunk partials
+    into ``workspace`` and return (None, None); ``workspace_partials`` views
+    them for ``mla_splitkv_combine``.
     """
     if q_lat.dim() != 4 or kv_cache.dim() != 3 or block_table.dim() != 2 or seqlens.dim() != 1:
         raise ValueError("expected q_lat [B,s_q,H,576], kv_cache [pages,64,576], block_table [B,P], seqlens [B]")
@@ -188,20 +191,36 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
         total_splits = B
     if workspace is not None:
         _need(workspace, "workspace", device=dev)
-    if o_lat is None:
-        o_lat = torch.empty((B, s_q, H, D_V), dtype=dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
-    _need(o_lat, "o_lat", dtype=dtype, device=dev)
-    _need(lse, "lse", dtype=torch.float32, device=dev)
+    if partials_only:
+        if split_offsets is None:
+            raise ValueError("partials_only needs split_offsets")
+        if o_lat is not None or lse is not None:
+            raise ValueError("partials_only writes no o_lat/lse")
+    else:
+        if o_lat is None:
+            o_lat = torch.empty((B, s_q, H, D_V), dtype=dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+        _need(o_lat, "o_lat", dtype=dtype, device=dev)
+        _need(lse, "lse", dtype=torch.float32, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().mla_decode_fwd(
         _ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets),
-        int(total_splits), B, s_q, H, dqk, int(o_lat.shape[-1]), int(kv_cache.shape[1]),
+        int(total_splits), B, s_q, H, dqk, D_V if o_lat is None else int(o_lat.shape[-1]), int(kv_cache.shape[1]),
         int(block_table.shape[1]), int(kv_cache.shape[0]), float(softmax_scale), int(bool(causal)),
         _DTYPES[dtype], _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
     _check("mla_decode_fwd", st)
     return o_lat, lse
+
+
+def workspace_partials(workspace: torch.Tensor, total_splits: int, s_q: int, H: int):
+    """Views (o_part [total_splits,s_q,H,512], lse_part [total_splits,s_q,H]) of a decode workspace."""
+    rows = int(total_splits) * s_q * H
+    need = rows * (D_V + 1) * 4
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace is smaller than the partials of this plan")
+    flat = workspace.view(torch.uint8)[:need].view(torch.float32)
+    return flat[:rows * D_V].view(total_splits, s_q, H, D_V), flat[rows * D_V:].view(total_splits, s_q, H)
 
 
 def mla_splitkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offsets: torch.Tensor,

@@ -97,7 +97,11 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
                             int page_size, int max_pages_per_seq, int num_pages,
                             float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
                             size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
-  if (!q_lat || !kv_cache || !block_table || !seqlens || !o_lat || !lse) return MLA_ERR_INVALID_ARG;
+  if (!q_lat || !kv_cache || !block_table || !seqlens) return MLA_ERR_INVALID_ARG;
+  // Partials only: no outputs, which needs split offsets and a workspace.
+  const bool partials_only = !o_lat && !lse;
+  if (!partials_only && (!o_lat || !lse)) return MLA_ERR_INVALID_ARG;
+  if (partials_only && !split_offsets) return MLA_ERR_INVALID_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
@@ -136,7 +140,7 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == MLA_BF16 ? mla::launch_decode_bf16(a, st) : mla::launch_decode_fp32(a, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  if (split_offsets) {
+  if (split_offsets && !partials_only) {
     e = mla::launch_combine(a.o_part, a.lse_part, split_offsets, total_splits, B, s_q, H, dtype == MLA_BF16,
                             /*skip_single=*/true, o_lat, lse, st);
   }

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * kWaves) void mla_decode_fp32_kernel(DecodeArgs
   const bool any = l > 0.f;
   const float inv = any ? 1.f / l : 0.f;
   const float lse_v = any ? m + logf(l) : -INFINITY;
-  if (n == 1) {
+  if (n == 1 && a.o_lat != nullptr) {
     float* orow = reinterpret_cast<float*>(a.o_lat) + ((size_t)b * rows + row) * kDv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) orow[lane + 64 * e] = o[e] * inv;

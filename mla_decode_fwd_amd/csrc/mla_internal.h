@@ -12,7 +12,7 @@ constexpr int kDqk = 576;       // key width: latent 512 + RoPE 64
 constexpr int kDv = 512;        // value width: the latent
 constexpr int kPage = 64;       // tokens per cache page
 constexpr int kMaxSplits = 64;  // chunks per sequence at most
-constexpr int kRowsPerGroup = 128;  // query rows (token, head) per workgroup
+constexpr int kRowsPerGroup = 64;   // query rows (token, head) per decode workgroup
 
 // Arguments of one decode launch, already validated on the host.
 struct DecodeArgs {
@@ -29,8 +29,8 @@ struct DecodeArgs {
   int causal;
   float* o_part;    // [total_splits, s_q, H, 512] when split, else nullptr
   float* lse_part;  // [total_splits, s_q, H]
-  void* o_lat;      // [B, s_q, H, 512]
-  float* lse;       // [B, s_q, H]
+  void* o_lat;      // [B, s_q, H, 512]; nullptr: write partials for every chunk
+  float* lse;       // [B, s_q, H]; nullptr together with o_lat
 };
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);

@@ -192,6 +192,31 @@ def test_splitkv_combine(out_dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_partials_only_then_combine_matches_one_call(dtype):
+    # Two-phase use: decode writes only the chunk partials (every chunk, also
+    # the sequences with one chunk), the public combine merges them. Both
+    # phases run the same kernels as the one-call path, and a one-chunk merge
+    # is exact (weight exp(0) = 1, lse + ln 1), so the results are identical.
+    case = make_decode_case([300, 64, 1000, 7, 2500], s_q=2, H=128, seed=41, dtype=dtype)
+    d = to_device(case)
+    p = mla.decode_plan(case.seqlens.tolist(), case.s_q, case.H, num_cus=16)
+    assert p.any_split and (p.num_splits == 1).any()
+    offs = p.device_offsets("cuda")
+    o1, l1 = mla.mla_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale,
+                                case.causal, split_offsets=offs, total_splits=p.total_splits)
+    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device="cuda")
+    res = mla.mla_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale, case.causal,
+                             split_offsets=offs, total_splits=p.total_splits, workspace=ws, partials_only=True)
+    assert res == (None, None)
+    o_part, lse_part = mla.workspace_partials(ws, p.total_splits, case.s_q, case.H)
+    o2, l2 = mla.mla_splitkv_combine(o_part, lse_part, offs, p.total_splits, case.B, dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = oracle(case)
+    compare(o2, l2, o_ref, l_ref, dtype, "partials+combine")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_absorb_q_and_out_uv_deepseek_shape(dtype):
     rng = np.random.default_rng(41)
     N, H, dn, dr, dc, dv = 64, 128, 128, 64, 512, 128
