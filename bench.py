@@ -155,16 +155,21 @@ def main():
     stream = torch.cuda.current_stream()  # the library launches on it
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
+    # Both launches are prepared once (checks and argument marshalling done
+    # up front) so that the host enqueues a step faster than the GPU runs it.
+    dec_calls = [mla.prepare_decode(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal, split_offsets=offs,
+                                    total_splits=plan.total_splits, workspace=ws, partials_only=True)[0]
+                 for s in sets]
+    comb_call = mla.prepare_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o, lse)
+
     def step(i, events=None):
-        s = sets[i % 2]
         if events:
             events[0].record(stream)
-        mla.mla_decode_fwd(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal,
-                           split_offsets=offs, total_splits=plan.total_splits, workspace=ws, partials_only=True)
+        dec_calls[i % 2]()
         if events:
             events[1].record(stream)
             events[2].record(stream)
-        mla.mla_splitkv_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o, lse)
+        comb_call()
         if events:
             events[3].record(stream)
 

@@ -118,7 +118,8 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
  *   o_lat[b,i,h,:] = sum_j softmax(s)_j * V_j
  *   lse[b,i,h]     = ln sum_j exp(s_j)         (natural log)
  * ([MLA-推理] sections "两条等价的路径" and "decode 注意力变成了计算问题";
- *  softmax_scale is 1/sqrt(d_nope + d_rope) = 1/sqrt(192) for DeepSeek-V3.)
+ *  softmax_scale is 1/sqrt(d_nope + d_rope) = 1/sqrt(192) for DeepSeek-V3;
+ *  it must be finite and > 0.)
  *
  *   q_lat            [B, s_q, H, 576] dtype; q_lat[...,0:512] = W_UK q^N,
  *                    q_lat[...,512:576] = RoPE(q^R) (see mla_absorb_q).
@@ -142,7 +143,8 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
  *                    split_offsets != NULL (may be NULL otherwise). Its contents
  *                    on entry are ignored; on return it holds the per-chunk
  *                    partials in mla_splitkv_combine's input layout: o_part
- *                    at byte 0, lse_part at byte total_splits*s_q*H*512*4.
+ *                    (in the decode dtype) at byte 0, lse_part (fp32) at byte
+ *                    total_splits*s_q*H*512*4 for either dtype.
  *   o_lat            out [B, s_q, H, 512] dtype.
  *   lse              out [B, s_q, H] fp32 (natural log).
  *                    o_lat and lse may both be NULL when split_offsets is
@@ -168,14 +170,15 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
  *   o = sum_k exp(lse_k - lse) * o_k
  * A chunk with lse_k = -inf (no allowed key) contributes nothing.
  *
- *   o_part     [total_splits, s_q, H, d_v] fp32, chunk-major: the chunks of
+ *   o_part     [total_splits, s_q, H, d_v] in out_dtype (bf16 partials for a
+ *              bf16 output, fp32 for fp32), chunk-major: the chunks of
  *              sequence b are rows split_offsets[b] .. split_offsets[b+1]-1.
  *   lse_part   [total_splits, s_q, H] fp32, natural log.
  *   split_offsets [B+1] int32 (device), total_splits = split_offsets[B].
  *   d_v        must be 512.
  *   o_lat      out [B, s_q, H, d_v] in out_dtype;  lse: out [B, s_q, H] fp32.
  */
-mla_status_t mla_splitkv_combine(const float* o_part, const float* lse_part,
+mla_status_t mla_splitkv_combine(const void* o_part, const float* lse_part,
                                  const int32_t* split_offsets, int total_splits, int B, int s_q,
                                  int H, int d_v, mla_dtype_t out_dtype, void* o_lat, float* lse,
                                  void* stream);

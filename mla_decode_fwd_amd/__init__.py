@@ -22,6 +22,7 @@ __all__ = [
     "MlaError", "library_path", "load_library", "abi_version",
     "decode_plan", "decode_workspace_size", "mla_decode_fwd", "mla_splitkv_combine",
     "mla_absorb_q", "mla_out_uv", "DecodePlan", "workspace_partials",
+    "PreparedCall", "prepare_decode", "prepare_combine",
     "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS",
 ]
 
@@ -156,7 +157,7 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
                    seqlens: torch.Tensor, softmax_scale: float, causal: bool,
                    split_offsets: Optional[torch.Tensor] = None, total_splits: Optional[int] = None,
                    workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, partials_only: bool = False):
+                   lse: Optional[torch.Tensor] = None, partials_only: bool = False, _prepare: bool = False):
     """Absorbed-MLA decode (mla_decode_fwd). Returns (o_lat [B,s_q,H,512], lse [B,s_q,H] fp32).
 
     split_offsets: int32 device [B+1] from ``decode_plan`` (or None for one
@@ -204,23 +205,31 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
         _need(o_lat, "o_lat", dtype=dtype, device=dev)
         _need(lse, "lse", dtype=torch.float32, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().mla_decode_fwd(
-        _ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets),
-        int(total_splits), B, s_q, H, dqk, D_V if o_lat is None else int(o_lat.shape[-1]), int(kv_cache.shape[1]),
-        int(block_table.shape[1]), int(kv_cache.shape[0]), float(softmax_scale), int(bool(causal)),
-        _DTYPES[dtype], _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
-    _check("mla_decode_fwd", st)
+    args = (_ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets),
+            int(total_splits), B, s_q, H, dqk, D_V if o_lat is None else int(o_lat.shape[-1]),
+            int(kv_cache.shape[1]), int(block_table.shape[1]), int(kv_cache.shape[0]), float(softmax_scale),
+            int(bool(causal)), _DTYPES[dtype], _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
+    if _prepare:
+        return PreparedCall("mla_decode_fwd", args), (o_lat, lse)
+    _check("mla_decode_fwd", load_library().mla_decode_fwd(*args))
     return o_lat, lse
 
 
-def workspace_partials(workspace: torch.Tensor, total_splits: int, s_q: int, H: int):
-    """Views (o_part [total_splits,s_q,H,512], lse_part [total_splits,s_q,H]) of a decode workspace."""
+def workspace_partials(workspace: torch.Tensor, total_splits: int, s_q: int, H: int,
+                       dtype: torch.dtype = torch.bfloat16):
+    """Views (o_part [total_splits,s_q,H,512] in the decode dtype, lse_part
+    [total_splits,s_q,H] fp32) of a decode workspace. The o_part region is
+    sized for fp32 whatever the dtype, so lse_part always starts at byte
+    total_splits*s_q*H*512*4."""
     rows = int(total_splits) * s_q * H
     need = rows * (D_V + 1) * 4
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace is smaller than the partials of this plan")
-    flat = workspace.view(torch.uint8)[:need].view(torch.float32)
-    return flat[:rows * D_V].view(total_splits, s_q, H, D_V), flat[rows * D_V:].view(total_splits, s_q, H)
+    raw = workspace.view(torch.uint8)
+    esz = torch.empty((), dtype=dtype).element_size()
+    o_part = raw[:rows * D_V * esz].view(dtype).view(total_splits, s_q, H, D_V)
+    lse_part = raw[rows * D_V * 4:need].view(torch.float32).view(total_splits, s_q, H)
+    return o_part, lse_part
 
 
 def mla_splitkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offsets: torch.Tensor,
@@ -228,11 +237,11 @@ def mla_splitkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offs
                         o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """LSE merge of chunk partials (mla_splitkv_combine).
 
-    o_part [total_splits, s_q, H, 512] fp32, lse_part [total_splits, s_q, H] fp32.
+    o_part [total_splits, s_q, H, 512] in out_dtype, lse_part [total_splits, s_q, H] fp32.
     Returns (o_lat [B,s_q,H,512] out_dtype, lse [B,s_q,H] fp32).
     """
     dev = o_part.device
-    _need(o_part, "o_part", dtype=torch.float32)
+    _need(o_part, "o_part", dtype=out_dtype)
     _need(lse_part, "lse_part", dtype=torch.float32, device=dev)
     _need(split_offsets, "split_offsets", dtype=torch.int32, device=dev)
     if o_part.dim() != 4 or lse_part.shape != o_part.shape[:3] or o_part.shape[0] != total_splits:
@@ -251,6 +260,49 @@ def mla_splitkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offs
                                             _stream())
     _check("mla_splitkv_combine", st)
     return o_lat, lse
+
+
+class PreparedCall:
+    """One library call with its arguments validated and marshalled once.
+
+    Calling it launches the same entry point with the same tensors (by
+    address) on the stream that was current when it was prepared, without
+    re-checking the tensors in Python: the caller keeps them alive and
+    unchanged in shape. For launch-rate-bound loops (a decode step per layer).
+    """
+
+    def __init__(self, fn: str, args: tuple):
+        self.fn = fn
+        self.args = args
+        self._f = getattr(load_library(), fn)
+
+    def __call__(self) -> None:
+        st = self._f(*self.args)
+        if st != 0:
+            raise MlaError(self.fn, st)
+
+
+def prepare_decode(*args, **kwargs):
+    """Like ``mla_decode_fwd`` but returns (PreparedCall, (o_lat, lse)) instead of launching."""
+    return mla_decode_fwd(*args, _prepare=True, **kwargs)
+
+
+def prepare_combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offsets: torch.Tensor,
+                    total_splits: int, B: int, out_dtype: torch.dtype, o_lat: torch.Tensor,
+                    lse: torch.Tensor) -> PreparedCall:
+    """A PreparedCall of ``mla_splitkv_combine`` (same checks, run once)."""
+    _need(o_part, "o_part", dtype=out_dtype)
+    dev = o_part.device
+    _need(lse_part, "lse_part", dtype=torch.float32, device=dev)
+    _need(split_offsets, "split_offsets", dtype=torch.int32, device=dev)
+    _need(o_lat, "o_lat", dtype=out_dtype, device=dev)
+    _need(lse, "lse", dtype=torch.float32, device=dev)
+    if o_part.dim() != 4 or lse_part.shape != o_part.shape[:3] or o_part.shape[0] != total_splits:
+        raise ValueError("o_part must be [total_splits,s_q,H,512] and lse_part [total_splits,s_q,H]")
+    _, s_q, H, dv = o_part.shape
+    return PreparedCall("mla_splitkv_combine",
+                        (_ptr(o_part), _ptr(lse_part), _ptr(split_offsets), int(total_splits), int(B), s_q, H,
+                         dv, _DTYPES[out_dtype], _ptr(o_lat), _ptr(lse), _stream()))
 
 
 def mla_absorb_q(q_nope: torch.Tensor, q_rope: Optional[torch.Tensor], w_uk: torch.Tensor,

@@ -104,7 +104,7 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
   if (partials_only && !split_offsets) return MLA_ERR_INVALID_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
     return MLA_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (!known_dtype(dtype)) return MLA_ERR_UNSUPPORTED;
   if (d_qk != MLA_D_QK || d_v != MLA_D_V || page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
   if (H > kMaxHeads || s_q > kMaxSq) return MLA_ERR_UNSUPPORTED;
@@ -134,8 +134,10 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
   a.lse = lse;
   if (split_offsets) {
     const size_t rows = (size_t)total_splits * s_q * H;
-    a.o_part = static_cast<float*>(workspace);
-    a.lse_part = a.o_part + rows * mla::kDv;
+    // The o_part region is sized for fp32 whatever the dtype, so the LSE
+    // partials always start at the same byte offset.
+    a.o_part = workspace;
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + rows * mla::kDv * sizeof(float));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == MLA_BF16 ? mla::launch_decode_bf16(a, st) : mla::launch_decode_fp32(a, st);
@@ -147,7 +149,7 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
   return from_hip(e);
 }
 
-mla_status_t mla_splitkv_combine(const float* o_part, const float* lse_part,
+mla_status_t mla_splitkv_combine(const void* o_part, const float* lse_part,
                                  const int32_t* split_offsets, int total_splits, int B, int s_q,
                                  int H, int d_v, mla_dtype_t out_dtype, void* o_lat, float* lse,
                                  void* stream) {

@@ -9,7 +9,7 @@
 //
 // One wave per row: lane k < n reads lse_k, two wave reductions give M and
 // the sum, then every lane owns 8 of the 512 columns and streams the chunks'
-// partial rows with 16-byte loads.
+// partial rows (in the output dtype: bf16 or fp32) eight chunks at a time.
 
 #include <hip/hip_runtime.h>
 #include <cmath>
@@ -37,7 +37,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(64 * kWaves) void combine_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(64 * kWaves) void combine_kernel(const void* __restrict__ o_part,
                                                               const float* __restrict__ lse_part,
                                                               const int32_t* __restrict__ split_offsets,
                                                               int rows, int total_splits,
@@ -57,35 +57,52 @@ __global__ __launch_bounds__(64 * kWaves) void combine_kernel(const float* __res
   const float w = (lane < n) ? expf(lk - Mf) : 0.f;
   const float S = wave_sum(w);
   const float lse_v = (S > 0.f) ? Mf + logf(S) : -INFINITY;
-  const float wn = (S > 0.f) ? w / S : 0.f;  // exp(lse_k - lse)
+  const float wn = (S > 0.f) ? w / S : 0.f;  // exp(lse_k - lse); lanes >= n hold 0
 
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n; ++k) {
-    const float wk = __shfl(wn, k, 64);
-    if (wk == 0.f) continue;  // wave-uniform: empty chunk
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(o_part + ((size_t)(s0 + k) * rows + row) * kDv) + 2 * lane;
-    acc0 += wk * src[0];
-    acc1 += wk * src[1];
+  // Lane l owns columns 8l .. 8l+7. The chunks are read eight at a time with
+  // independent loads, so their latencies overlap.
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    float v[8][8];
+    float wk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      wk[j] = __shfl(wn, k & 63, 64);
+      const size_t off = ((size_t)(s0 + min(k, n - 1)) * rows + row) * kDv + 8 * lane;
+      if (kBf16) {
+        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(o_part) + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = (float)x[e];
+      } else {
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(o_part) + off);
+        const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[j][e] = x0[e]; v[j][4 + e] = x1[e]; }
+      }
+      if (k >= n) wk[j] = 0.f;  // re-read of the last chunk, weighted out
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk[j], v[j][e], acc[e]);
   }
   if (kBf16) {
-    bf16x8_t v;
+    bf16x8_t o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = (__bf16)acc0[e];
-      v[4 + e] = (__bf16)acc1[e];
-    }
-    *(reinterpret_cast<bf16x8_t*>(reinterpret_cast<__bf16*>(o_lat) + ((size_t)b * rows + row) * kDv) + lane) = v;
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)acc[e];
+    *(reinterpret_cast<bf16x8_t*>(reinterpret_cast<__bf16*>(o_lat) + ((size_t)b * rows + row) * kDv) + lane) = o;
   } else {
     f32x4_t* dst = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(o_lat) + ((size_t)b * rows + row) * kDv) + 2 * lane;
-    dst[0] = acc0;
-    dst[1] = acc1;
+    dst[0] = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    dst[1] = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
   }
   if (lane == 0) lse[(size_t)b * rows + row] = lse_v;
 }
 
 }  // namespace
 
-hipError_t launch_combine(const float* o_part, const float* lse_part, const int32_t* split_offsets,
+hipError_t launch_combine(const void* o_part, const float* lse_part, const int32_t* split_offsets,
                           int total_splits, int B, int s_q, int H, bool out_bf16, bool skip_single,
                           void* o_lat, float* lse, hipStream_t stream) {
   const int rows = s_q * H;

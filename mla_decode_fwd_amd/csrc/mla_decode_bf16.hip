@@ -4,50 +4,50 @@
 // and "decode 注意力变成了计算问题"): every (query token, head) row attends to
 // one shared 576-wide key per cached token and one shared 512-wide value (the
 // first 512 elements of the same cache row), i.e. an MQA with a very wide
-// head. Rows are the MFMA N dimension, the latent the K dimension.
+// head.
 //
 // Work decomposition
 //   * A row is (query token i, head h), m = i*H + h, so q_lat[b] is an
-//     [s_q*H, 576] matrix. A workgroup holds 64 rows (4 waves x 16 rows, one
-//     wave per SIMD with the whole register file) and walks a range of
-//     64-token pages of one sequence. The workgroups of the other row groups
-//     of the same chunk are mapped to the same XCD and run at the same time,
-//     so the second reader of a page finds it in that XCD's L2.
-//   * Per page, the 73,728-byte page is copied HBM -> LDS with direct 16-byte
-//     loads (global_load_lds_dwordx4), double-buffered so the next page
-//     streams in while the current one is consumed by the four waves.
-//   * QK^T is computed transposed, S^T[token, row] = K . Q^T, with
-//     v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 latent elements read from
-//     LDS, B = Q^T held in registers for the whole walk (18 k-steps). Each
-//     lane then owns one row and 16 of the page's 64 token scores; the row
-//     max and sum take two cross-lane steps (lane ^ 16, lane ^ 32).
-//   * PV is computed transposed too, O^T[col, row] += V^T . P^T: A = V^T read
-//     with ds_read_b64_tr_b16 (a 4x16 -> 16x4 transpose within each 16-lane
-//     group), B = P^T taken straight from the score registers after a bf16
-//     pack. Inside each 32-token k-step the token order is permuted the same
-//     way on both sides, so the score registers need no shuffling.
-//   * Online softmax in base 2 with a lazily updated reference max: the
-//     accumulators are rescaled only when a row's max grows by more than 8
-//     (so P <= 2^8); the result is exact because P, l and O always share the
-//     same reference.
+//     [s_q*H, 576] matrix. A workgroup holds 128 rows (all heads of one new
+//     token at H = 128) and walks a range of 64-token pages of one sequence,
+//     so every page crosses HBM once per chunk and each compute unit has a
+//     page of its own in flight.
+//   * Each page (73,728 bytes) is copied HBM -> LDS with direct 16-byte loads
+//     (global_load_lds_dwordx4), double-buffered: the next page streams in
+//     while the four waves consume the current one.
+//   * Four waves, one per SIMD, 32 rows each. A wave holds Q^T for its rows
+//     in VGPRs (36 k-steps, 144 registers) and O^T for its rows in AGPRs
+//     (16 column tiles of 32x32 fp32, the whole AGPR file): every LDS byte a
+//     wave reads feeds 32 rows, and the waves never exchange data.
+//   * A page is two 32-token tiles. Per tile: S^T = K . Q^T with
+//     v_mfma_f32_32x32x16_bf16 (A = 32 tokens x 16 latent elements from LDS,
+//     B = Q^T), an online softmax on the 16 scores a lane holds (one row,
+//     lanes l and l^32 share a row), then O^T += V^T . P^T (A = V^T read from
+//     the same LDS page with ds_read_b64_tr_b16, a 4x16 -> 16x4 transpose
+//     within each 16-lane group; B = P^T taken straight from the score
+//     registers: the score layout of a 16-token half tile is exactly the B
+//     layout of one k-step with the tokens of the k-step permuted, and the
+//     V^T reads use the same permutation).
+//   * Softmax in base 2 with a lazily updated reference max: O and l are
+//     rescaled only when a row's max grows by more than 8 (so P <= 2^8); the
+//     result is exact because P, l and O always share the reference.
 //   * Split-KV: a workgroup handles chunk k of n_b page-aligned chunks of its
 //     sequence. With n_b = 1 it writes bf16 o_lat and the LSE directly;
-//     otherwise (or when only partials are asked for) fp32 partials that
-//     the combine kernel merges by LSE.
+//     otherwise (or when only partials are asked for) bf16 partials and fp32
+//     LSEs that the combine kernel merges.
 //
 // LDS page layout ("line blocks"): the page is split into 72 blocks of 1 KB.
 // Block 9m + j holds, for the 8 tokens t = 8m .. 8m+7, the 128-byte line j
 // (chunks 8j .. 8j+7 of 8 elements) of each token's row: token t, chunk c
 // sits in 16-byte slot 64*(9*(t>>3) + (c>>3)) + 8*(t&7) + ((c&7) ^ F(t)),
-// F(t) = T[(t>>1)&3] ^ 4*((t>>3)&1), T = {0, 2, 5, 7}. Every direct-load
+// F(t) = ((u&1) << 2) | (u >> 1), u = (t>>1) & 7. Every direct-load
 // instruction therefore reads 8 whole 128-byte lines (fully coalesced), and
 // the XOR keeps the QK reads (16 lanes = 16 tokens of one chunk) and the
-// transposed PV reads (4 lane groups x 4 tokens x 2 chunks) free of LDS bank
-// conflicts.
+// transposed PV reads (2 x 4 tokens x 16 columns per 32 lanes) free of LDS
+// bank conflicts.
 
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
 #include <cmath>
 #include <cstdint>
 
@@ -59,28 +59,26 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-typedef __attribute__((address_space(1))) const void gbl_cvoid_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 16;
-static_assert(kRowsPerWave * kWaves == kRowsPerGroup, "a workgroup covers one row group");
-constexpr int kRowBytes = kDqk * 2;               // 1152: one cache row
-constexpr int kPageBytes = kPage * kRowBytes;     // 73728: one page
-constexpr int kBlocks = kPageBytes / 1024;        // 72 line blocks
-constexpr int kBlocksPerWave = kBlocks / kWaves;  // 18: two token octets per wave
-constexpr int kQSteps = kDqk / 32;                // 18 k-steps of 32
-constexpr int kColTiles = kDv / 16;               // 32 output column tiles
+constexpr int kWaveRows = 32;                      // rows per wave
+static_assert(kWaveRows * kWaves == kRowsPerGroup, "a workgroup covers one row group");
+constexpr int kRowBytes = kDqk * 2;                // 1152: one cache row
+constexpr int kPageBytes = kPage * kRowBytes;      // 73728: one page
+constexpr int kBlocks = kPageBytes / 1024;         // 72 line blocks
+constexpr int kBlocksPerWave = kBlocks / kWaves;   // 18: two token octets per wave
+constexpr int kQSteps = kDqk / 16;                 // 36 k-steps of 16
+constexpr int kColTiles = kDv / 32;                // 16 column tiles of 32
 static_assert(kBlocksPerWave == 18, "each wave loads two token octets");
 // s_waitcnt immediate for gfx9: vmcnt = 0, expcnt and lgkmcnt left at "no wait".
 constexpr int kWaitVmcnt0 = (0xF << 8) | (0x7 << 4);
 
 __device__ __forceinline__ int swz(int t) {
-  const int u = (t >> 1) & 3;
-  const int tbl = (u == 0) ? 0 : (u == 1) ? 2 : (u == 2) ? 5 : 7;
-  return tbl ^ (4 * ((t >> 3) & 1));
+  const int u = (t >> 1) & 7;
+  return ((u & 1) << 2) | (u >> 1);
 }
 __device__ __forceinline__ int slot_bytes(int t, int c) {
   return (64 * (9 * (t >> 3) + (c >> 3)) + 8 * (t & 7) + ((c & 7) ^ swz(t))) * 16;
@@ -107,9 +105,9 @@ __device__ __forceinline__ void dma_line(uint64_t sbase, int voff, uint32_t lds)
 
 // The loads of one page into an LDS buffer. Wave w fills blocks 18w .. 18w+17:
 // token octets 2w and 2w+1, lines j = 0..8 each. Lane l takes token
-// 8m + (l>>3), chunk 8j + ((l&7) ^ F(token)); F depends on the octet's
-// parity, hence two per-lane source offsets. Line n (0..17) of the wave is
-// octet n/9, line n%9.
+// 8m + (l>>3), chunk 8j + ((l&7) ^ F(token)); F depends on the token, hence
+// two per-lane source offsets. Line n (0..17) of the wave is octet n/9, line
+// n%9.
 struct PageLoad {
   uint64_t sbase;  // page address (wave-uniform)
   uint32_t lds;    // LDS address of the wave's first block (wave-uniform)
@@ -143,41 +141,842 @@ __device__ __forceinline__ void issue_page(const PageLoad& p) {
   for (int n = 0; n < kBlocksPerWave; ++n) issue_line(p, n);
 }
 
-// Reductions over the four lane groups of a row (lanes l, l^16, l^32, l^48)
-// with the gfx950 lane-swap instructions (VALU, no LDS round trip). With both
-// operands equal, permlane16_swap yields the values of lanes l and l^16 side
-// by side, permlane32_swap those of l and l^32.
-__device__ __forceinline__ float max4lanes(float v) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// Value of lane l ^ 32 (gfx950 lane swap; VALU, no LDS round trip). With
+// both operands equal, permlane32_swap yields the values of lanes l and l^32.
+__device__ __forceinline__ float other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
-__device__ __forceinline__ float sum4lanes(float v) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+
+// O^T += V^T P^T for one 32x32 column tile, accumulator pinned to AGPRs: the
+// 16 tiles of a wave fill the AGPR file exactly, and the compiler left to
+// itself places some of them in VGPRs and spills Q. The compiler's hazard
+// tracking does not see into this asm, so the caller asks for wait states
+// (kFresh) where B was just written by VALU instructions, and any VALU
+// access to the accumulators goes through agpr_fence() first.
+template <bool kFresh>
+__device__ __forceinline__ void mfma_pv(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if constexpr (kFresh)
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last accumulating MFMA (8 passes) and a VALU
+// read of its AGPRs; the hazard tracker does not see into the asm above.
+__device__ __forceinline__ void agpr_fence() {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
+
+// O *= alpha for the whole accumulator: every AGPR of a lane belongs to the
+// lane's one query row (the column of its O^T tiles), and O occupies the
+// AGPR file alone, so all 256 AGPRs are scaled in place. Done in asm so that
+// no VALU use of the accumulators is visible to the register allocator
+// (which would otherwise stage all of O through VGPRs and spill). Trailing
+// wait states cover the AGPR write -> MFMA srcC hazard.
+__device__ __forceinline__ void scale_accumulators(float alpha) {
+  float t0, t1, t2, t3;
+  asm volatile(
+      "v_accvgpr_read_b32 %0, a0\n\t"
+      "v_accvgpr_read_b32 %1, a1\n\t"
+      "v_accvgpr_read_b32 %2, a2\n\t"
+      "v_accvgpr_read_b32 %3, a3\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a0, %0\n\t"
+      "v_accvgpr_write_b32 a1, %1\n\t"
+      "v_accvgpr_write_b32 a2, %2\n\t"
+      "v_accvgpr_write_b32 a3, %3\n\t"
+      "v_accvgpr_read_b32 %0, a4\n\t"
+      "v_accvgpr_read_b32 %1, a5\n\t"
+      "v_accvgpr_read_b32 %2, a6\n\t"
+      "v_accvgpr_read_b32 %3, a7\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a4, %0\n\t"
+      "v_accvgpr_write_b32 a5, %1\n\t"
+      "v_accvgpr_write_b32 a6, %2\n\t"
+      "v_accvgpr_write_b32 a7, %3\n\t"
+      "v_accvgpr_read_b32 %0, a8\n\t"
+      "v_accvgpr_read_b32 %1, a9\n\t"
+      "v_accvgpr_read_b32 %2, a10\n\t"
+      "v_accvgpr_read_b32 %3, a11\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a8, %0\n\t"
+      "v_accvgpr_write_b32 a9, %1\n\t"
+      "v_accvgpr_write_b32 a10, %2\n\t"
+      "v_accvgpr_write_b32 a11, %3\n\t"
+      "v_accvgpr_read_b32 %0, a12\n\t"
+      "v_accvgpr_read_b32 %1, a13\n\t"
+      "v_accvgpr_read_b32 %2, a14\n\t"
+      "v_accvgpr_read_b32 %3, a15\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a12, %0\n\t"
+      "v_accvgpr_write_b32 a13, %1\n\t"
+      "v_accvgpr_write_b32 a14, %2\n\t"
+      "v_accvgpr_write_b32 a15, %3\n\t"
+      "v_accvgpr_read_b32 %0, a16\n\t"
+      "v_accvgpr_read_b32 %1, a17\n\t"
+      "v_accvgpr_read_b32 %2, a18\n\t"
+      "v_accvgpr_read_b32 %3, a19\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a16, %0\n\t"
+      "v_accvgpr_write_b32 a17, %1\n\t"
+      "v_accvgpr_write_b32 a18, %2\n\t"
+      "v_accvgpr_write_b32 a19, %3\n\t"
+      "v_accvgpr_read_b32 %0, a20\n\t"
+      "v_accvgpr_read_b32 %1, a21\n\t"
+      "v_accvgpr_read_b32 %2, a22\n\t"
+      "v_accvgpr_read_b32 %3, a23\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a20, %0\n\t"
+      "v_accvgpr_write_b32 a21, %1\n\t"
+      "v_accvgpr_write_b32 a22, %2\n\t"
+      "v_accvgpr_write_b32 a23, %3\n\t"
+      "v_accvgpr_read_b32 %0, a24\n\t"
+      "v_accvgpr_read_b32 %1, a25\n\t"
+      "v_accvgpr_read_b32 %2, a26\n\t"
+      "v_accvgpr_read_b32 %3, a27\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a24, %0\n\t"
+      "v_accvgpr_write_b32 a25, %1\n\t"
+      "v_accvgpr_write_b32 a26, %2\n\t"
+      "v_accvgpr_write_b32 a27, %3\n\t"
+      "v_accvgpr_read_b32 %0, a28\n\t"
+      "v_accvgpr_read_b32 %1, a29\n\t"
+      "v_accvgpr_read_b32 %2, a30\n\t"
+      "v_accvgpr_read_b32 %3, a31\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a28, %0\n\t"
+      "v_accvgpr_write_b32 a29, %1\n\t"
+      "v_accvgpr_write_b32 a30, %2\n\t"
+      "v_accvgpr_write_b32 a31, %3\n\t"
+      "v_accvgpr_read_b32 %0, a32\n\t"
+      "v_accvgpr_read_b32 %1, a33\n\t"
+      "v_accvgpr_read_b32 %2, a34\n\t"
+      "v_accvgpr_read_b32 %3, a35\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a32, %0\n\t"
+      "v_accvgpr_write_b32 a33, %1\n\t"
+      "v_accvgpr_write_b32 a34, %2\n\t"
+      "v_accvgpr_write_b32 a35, %3\n\t"
+      "v_accvgpr_read_b32 %0, a36\n\t"
+      "v_accvgpr_read_b32 %1, a37\n\t"
+      "v_accvgpr_read_b32 %2, a38\n\t"
+      "v_accvgpr_read_b32 %3, a39\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a36, %0\n\t"
+      "v_accvgpr_write_b32 a37, %1\n\t"
+      "v_accvgpr_write_b32 a38, %2\n\t"
+      "v_accvgpr_write_b32 a39, %3\n\t"
+      "v_accvgpr_read_b32 %0, a40\n\t"
+      "v_accvgpr_read_b32 %1, a41\n\t"
+      "v_accvgpr_read_b32 %2, a42\n\t"
+      "v_accvgpr_read_b32 %3, a43\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a40, %0\n\t"
+      "v_accvgpr_write_b32 a41, %1\n\t"
+      "v_accvgpr_write_b32 a42, %2\n\t"
+      "v_accvgpr_write_b32 a43, %3\n\t"
+      "v_accvgpr_read_b32 %0, a44\n\t"
+      "v_accvgpr_read_b32 %1, a45\n\t"
+      "v_accvgpr_read_b32 %2, a46\n\t"
+      "v_accvgpr_read_b32 %3, a47\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a44, %0\n\t"
+      "v_accvgpr_write_b32 a45, %1\n\t"
+      "v_accvgpr_write_b32 a46, %2\n\t"
+      "v_accvgpr_write_b32 a47, %3\n\t"
+      "v_accvgpr_read_b32 %0, a48\n\t"
+      "v_accvgpr_read_b32 %1, a49\n\t"
+      "v_accvgpr_read_b32 %2, a50\n\t"
+      "v_accvgpr_read_b32 %3, a51\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a48, %0\n\t"
+      "v_accvgpr_write_b32 a49, %1\n\t"
+      "v_accvgpr_write_b32 a50, %2\n\t"
+      "v_accvgpr_write_b32 a51, %3\n\t"
+      "v_accvgpr_read_b32 %0, a52\n\t"
+      "v_accvgpr_read_b32 %1, a53\n\t"
+      "v_accvgpr_read_b32 %2, a54\n\t"
+      "v_accvgpr_read_b32 %3, a55\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a52, %0\n\t"
+      "v_accvgpr_write_b32 a53, %1\n\t"
+      "v_accvgpr_write_b32 a54, %2\n\t"
+      "v_accvgpr_write_b32 a55, %3\n\t"
+      "v_accvgpr_read_b32 %0, a56\n\t"
+      "v_accvgpr_read_b32 %1, a57\n\t"
+      "v_accvgpr_read_b32 %2, a58\n\t"
+      "v_accvgpr_read_b32 %3, a59\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a56, %0\n\t"
+      "v_accvgpr_write_b32 a57, %1\n\t"
+      "v_accvgpr_write_b32 a58, %2\n\t"
+      "v_accvgpr_write_b32 a59, %3\n\t"
+      "v_accvgpr_read_b32 %0, a60\n\t"
+      "v_accvgpr_read_b32 %1, a61\n\t"
+      "v_accvgpr_read_b32 %2, a62\n\t"
+      "v_accvgpr_read_b32 %3, a63\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a60, %0\n\t"
+      "v_accvgpr_write_b32 a61, %1\n\t"
+      "v_accvgpr_write_b32 a62, %2\n\t"
+      "v_accvgpr_write_b32 a63, %3\n\t"
+      "v_accvgpr_read_b32 %0, a64\n\t"
+      "v_accvgpr_read_b32 %1, a65\n\t"
+      "v_accvgpr_read_b32 %2, a66\n\t"
+      "v_accvgpr_read_b32 %3, a67\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a64, %0\n\t"
+      "v_accvgpr_write_b32 a65, %1\n\t"
+      "v_accvgpr_write_b32 a66, %2\n\t"
+      "v_accvgpr_write_b32 a67, %3\n\t"
+      "v_accvgpr_read_b32 %0, a68\n\t"
+      "v_accvgpr_read_b32 %1, a69\n\t"
+      "v_accvgpr_read_b32 %2, a70\n\t"
+      "v_accvgpr_read_b32 %3, a71\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a68, %0\n\t"
+      "v_accvgpr_write_b32 a69, %1\n\t"
+      "v_accvgpr_write_b32 a70, %2\n\t"
+      "v_accvgpr_write_b32 a71, %3\n\t"
+      "v_accvgpr_read_b32 %0, a72\n\t"
+      "v_accvgpr_read_b32 %1, a73\n\t"
+      "v_accvgpr_read_b32 %2, a74\n\t"
+      "v_accvgpr_read_b32 %3, a75\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a72, %0\n\t"
+      "v_accvgpr_write_b32 a73, %1\n\t"
+      "v_accvgpr_write_b32 a74, %2\n\t"
+      "v_accvgpr_write_b32 a75, %3\n\t"
+      "v_accvgpr_read_b32 %0, a76\n\t"
+      "v_accvgpr_read_b32 %1, a77\n\t"
+      "v_accvgpr_read_b32 %2, a78\n\t"
+      "v_accvgpr_read_b32 %3, a79\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a76, %0\n\t"
+      "v_accvgpr_write_b32 a77, %1\n\t"
+      "v_accvgpr_write_b32 a78, %2\n\t"
+      "v_accvgpr_write_b32 a79, %3\n\t"
+      "v_accvgpr_read_b32 %0, a80\n\t"
+      "v_accvgpr_read_b32 %1, a81\n\t"
+      "v_accvgpr_read_b32 %2, a82\n\t"
+      "v_accvgpr_read_b32 %3, a83\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a80, %0\n\t"
+      "v_accvgpr_write_b32 a81, %1\n\t"
+      "v_accvgpr_write_b32 a82, %2\n\t"
+      "v_accvgpr_write_b32 a83, %3\n\t"
+      "v_accvgpr_read_b32 %0, a84\n\t"
+      "v_accvgpr_read_b32 %1, a85\n\t"
+      "v_accvgpr_read_b32 %2, a86\n\t"
+      "v_accvgpr_read_b32 %3, a87\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a84, %0\n\t"
+      "v_accvgpr_write_b32 a85, %1\n\t"
+      "v_accvgpr_write_b32 a86, %2\n\t"
+      "v_accvgpr_write_b32 a87, %3\n\t"
+      "v_accvgpr_read_b32 %0, a88\n\t"
+      "v_accvgpr_read_b32 %1, a89\n\t"
+      "v_accvgpr_read_b32 %2, a90\n\t"
+      "v_accvgpr_read_b32 %3, a91\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a88, %0\n\t"
+      "v_accvgpr_write_b32 a89, %1\n\t"
+      "v_accvgpr_write_b32 a90, %2\n\t"
+      "v_accvgpr_write_b32 a91, %3\n\t"
+      "v_accvgpr_read_b32 %0, a92\n\t"
+      "v_accvgpr_read_b32 %1, a93\n\t"
+      "v_accvgpr_read_b32 %2, a94\n\t"
+      "v_accvgpr_read_b32 %3, a95\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a92, %0\n\t"
+      "v_accvgpr_write_b32 a93, %1\n\t"
+      "v_accvgpr_write_b32 a94, %2\n\t"
+      "v_accvgpr_write_b32 a95, %3\n\t"
+      "v_accvgpr_read_b32 %0, a96\n\t"
+      "v_accvgpr_read_b32 %1, a97\n\t"
+      "v_accvgpr_read_b32 %2, a98\n\t"
+      "v_accvgpr_read_b32 %3, a99\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a96, %0\n\t"
+      "v_accvgpr_write_b32 a97, %1\n\t"
+      "v_accvgpr_write_b32 a98, %2\n\t"
+      "v_accvgpr_write_b32 a99, %3\n\t"
+      "v_accvgpr_read_b32 %0, a100\n\t"
+      "v_accvgpr_read_b32 %1, a101\n\t"
+      "v_accvgpr_read_b32 %2, a102\n\t"
+      "v_accvgpr_read_b32 %3, a103\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a100, %0\n\t"
+      "v_accvgpr_write_b32 a101, %1\n\t"
+      "v_accvgpr_write_b32 a102, %2\n\t"
+      "v_accvgpr_write_b32 a103, %3\n\t"
+      "v_accvgpr_read_b32 %0, a104\n\t"
+      "v_accvgpr_read_b32 %1, a105\n\t"
+      "v_accvgpr_read_b32 %2, a106\n\t"
+      "v_accvgpr_read_b32 %3, a107\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a104, %0\n\t"
+      "v_accvgpr_write_b32 a105, %1\n\t"
+      "v_accvgpr_write_b32 a106, %2\n\t"
+      "v_accvgpr_write_b32 a107, %3\n\t"
+      "v_accvgpr_read_b32 %0, a108\n\t"
+      "v_accvgpr_read_b32 %1, a109\n\t"
+      "v_accvgpr_read_b32 %2, a110\n\t"
+      "v_accvgpr_read_b32 %3, a111\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a108, %0\n\t"
+      "v_accvgpr_write_b32 a109, %1\n\t"
+      "v_accvgpr_write_b32 a110, %2\n\t"
+      "v_accvgpr_write_b32 a111, %3\n\t"
+      "v_accvgpr_read_b32 %0, a112\n\t"
+      "v_accvgpr_read_b32 %1, a113\n\t"
+      "v_accvgpr_read_b32 %2, a114\n\t"
+      "v_accvgpr_read_b32 %3, a115\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a112, %0\n\t"
+      "v_accvgpr_write_b32 a113, %1\n\t"
+      "v_accvgpr_write_b32 a114, %2\n\t"
+      "v_accvgpr_write_b32 a115, %3\n\t"
+      "v_accvgpr_read_b32 %0, a116\n\t"
+      "v_accvgpr_read_b32 %1, a117\n\t"
+      "v_accvgpr_read_b32 %2, a118\n\t"
+      "v_accvgpr_read_b32 %3, a119\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a116, %0\n\t"
+      "v_accvgpr_write_b32 a117, %1\n\t"
+      "v_accvgpr_write_b32 a118, %2\n\t"
+      "v_accvgpr_write_b32 a119, %3\n\t"
+      "v_accvgpr_read_b32 %0, a120\n\t"
+      "v_accvgpr_read_b32 %1, a121\n\t"
+      "v_accvgpr_read_b32 %2, a122\n\t"
+      "v_accvgpr_read_b32 %3, a123\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a120, %0\n\t"
+      "v_accvgpr_write_b32 a121, %1\n\t"
+      "v_accvgpr_write_b32 a122, %2\n\t"
+      "v_accvgpr_write_b32 a123, %3\n\t"
+      "v_accvgpr_read_b32 %0, a124\n\t"
+      "v_accvgpr_read_b32 %1, a125\n\t"
+      "v_accvgpr_read_b32 %2, a126\n\t"
+      "v_accvgpr_read_b32 %3, a127\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a124, %0\n\t"
+      "v_accvgpr_write_b32 a125, %1\n\t"
+      "v_accvgpr_write_b32 a126, %2\n\t"
+      "v_accvgpr_write_b32 a127, %3\n\t"
+      "v_accvgpr_read_b32 %0, a128\n\t"
+      "v_accvgpr_read_b32 %1, a129\n\t"
+      "v_accvgpr_read_b32 %2, a130\n\t"
+      "v_accvgpr_read_b32 %3, a131\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a128, %0\n\t"
+      "v_accvgpr_write_b32 a129, %1\n\t"
+      "v_accvgpr_write_b32 a130, %2\n\t"
+      "v_accvgpr_write_b32 a131, %3\n\t"
+      "v_accvgpr_read_b32 %0, a132\n\t"
+      "v_accvgpr_read_b32 %1, a133\n\t"
+      "v_accvgpr_read_b32 %2, a134\n\t"
+      "v_accvgpr_read_b32 %3, a135\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a132, %0\n\t"
+      "v_accvgpr_write_b32 a133, %1\n\t"
+      "v_accvgpr_write_b32 a134, %2\n\t"
+      "v_accvgpr_write_b32 a135, %3\n\t"
+      "v_accvgpr_read_b32 %0, a136\n\t"
+      "v_accvgpr_read_b32 %1, a137\n\t"
+      "v_accvgpr_read_b32 %2, a138\n\t"
+      "v_accvgpr_read_b32 %3, a139\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a136, %0\n\t"
+      "v_accvgpr_write_b32 a137, %1\n\t"
+      "v_accvgpr_write_b32 a138, %2\n\t"
+      "v_accvgpr_write_b32 a139, %3\n\t"
+      "v_accvgpr_read_b32 %0, a140\n\t"
+      "v_accvgpr_read_b32 %1, a141\n\t"
+      "v_accvgpr_read_b32 %2, a142\n\t"
+      "v_accvgpr_read_b32 %3, a143\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a140, %0\n\t"
+      "v_accvgpr_write_b32 a141, %1\n\t"
+      "v_accvgpr_write_b32 a142, %2\n\t"
+      "v_accvgpr_write_b32 a143, %3\n\t"
+      "v_accvgpr_read_b32 %0, a144\n\t"
+      "v_accvgpr_read_b32 %1, a145\n\t"
+      "v_accvgpr_read_b32 %2, a146\n\t"
+      "v_accvgpr_read_b32 %3, a147\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a144, %0\n\t"
+      "v_accvgpr_write_b32 a145, %1\n\t"
+      "v_accvgpr_write_b32 a146, %2\n\t"
+      "v_accvgpr_write_b32 a147, %3\n\t"
+      "v_accvgpr_read_b32 %0, a148\n\t"
+      "v_accvgpr_read_b32 %1, a149\n\t"
+      "v_accvgpr_read_b32 %2, a150\n\t"
+      "v_accvgpr_read_b32 %3, a151\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a148, %0\n\t"
+      "v_accvgpr_write_b32 a149, %1\n\t"
+      "v_accvgpr_write_b32 a150, %2\n\t"
+      "v_accvgpr_write_b32 a151, %3\n\t"
+      "v_accvgpr_read_b32 %0, a152\n\t"
+      "v_accvgpr_read_b32 %1, a153\n\t"
+      "v_accvgpr_read_b32 %2, a154\n\t"
+      "v_accvgpr_read_b32 %3, a155\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a152, %0\n\t"
+      "v_accvgpr_write_b32 a153, %1\n\t"
+      "v_accvgpr_write_b32 a154, %2\n\t"
+      "v_accvgpr_write_b32 a155, %3\n\t"
+      "v_accvgpr_read_b32 %0, a156\n\t"
+      "v_accvgpr_read_b32 %1, a157\n\t"
+      "v_accvgpr_read_b32 %2, a158\n\t"
+      "v_accvgpr_read_b32 %3, a159\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a156, %0\n\t"
+      "v_accvgpr_write_b32 a157, %1\n\t"
+      "v_accvgpr_write_b32 a158, %2\n\t"
+      "v_accvgpr_write_b32 a159, %3\n\t"
+      "v_accvgpr_read_b32 %0, a160\n\t"
+      "v_accvgpr_read_b32 %1, a161\n\t"
+      "v_accvgpr_read_b32 %2, a162\n\t"
+      "v_accvgpr_read_b32 %3, a163\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a160, %0\n\t"
+      "v_accvgpr_write_b32 a161, %1\n\t"
+      "v_accvgpr_write_b32 a162, %2\n\t"
+      "v_accvgpr_write_b32 a163, %3\n\t"
+      "v_accvgpr_read_b32 %0, a164\n\t"
+      "v_accvgpr_read_b32 %1, a165\n\t"
+      "v_accvgpr_read_b32 %2, a166\n\t"
+      "v_accvgpr_read_b32 %3, a167\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a164, %0\n\t"
+      "v_accvgpr_write_b32 a165, %1\n\t"
+      "v_accvgpr_write_b32 a166, %2\n\t"
+      "v_accvgpr_write_b32 a167, %3\n\t"
+      "v_accvgpr_read_b32 %0, a168\n\t"
+      "v_accvgpr_read_b32 %1, a169\n\t"
+      "v_accvgpr_read_b32 %2, a170\n\t"
+      "v_accvgpr_read_b32 %3, a171\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a168, %0\n\t"
+      "v_accvgpr_write_b32 a169, %1\n\t"
+      "v_accvgpr_write_b32 a170, %2\n\t"
+      "v_accvgpr_write_b32 a171, %3\n\t"
+      "v_accvgpr_read_b32 %0, a172\n\t"
+      "v_accvgpr_read_b32 %1, a173\n\t"
+      "v_accvgpr_read_b32 %2, a174\n\t"
+      "v_accvgpr_read_b32 %3, a175\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a172, %0\n\t"
+      "v_accvgpr_write_b32 a173, %1\n\t"
+      "v_accvgpr_write_b32 a174, %2\n\t"
+      "v_accvgpr_write_b32 a175, %3\n\t"
+      "v_accvgpr_read_b32 %0, a176\n\t"
+      "v_accvgpr_read_b32 %1, a177\n\t"
+      "v_accvgpr_read_b32 %2, a178\n\t"
+      "v_accvgpr_read_b32 %3, a179\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a176, %0\n\t"
+      "v_accvgpr_write_b32 a177, %1\n\t"
+      "v_accvgpr_write_b32 a178, %2\n\t"
+      "v_accvgpr_write_b32 a179, %3\n\t"
+      "v_accvgpr_read_b32 %0, a180\n\t"
+      "v_accvgpr_read_b32 %1, a181\n\t"
+      "v_accvgpr_read_b32 %2, a182\n\t"
+      "v_accvgpr_read_b32 %3, a183\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a180, %0\n\t"
+      "v_accvgpr_write_b32 a181, %1\n\t"
+      "v_accvgpr_write_b32 a182, %2\n\t"
+      "v_accvgpr_write_b32 a183, %3\n\t"
+      "v_accvgpr_read_b32 %0, a184\n\t"
+      "v_accvgpr_read_b32 %1, a185\n\t"
+      "v_accvgpr_read_b32 %2, a186\n\t"
+      "v_accvgpr_read_b32 %3, a187\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a184, %0\n\t"
+      "v_accvgpr_write_b32 a185, %1\n\t"
+      "v_accvgpr_write_b32 a186, %2\n\t"
+      "v_accvgpr_write_b32 a187, %3\n\t"
+      "v_accvgpr_read_b32 %0, a188\n\t"
+      "v_accvgpr_read_b32 %1, a189\n\t"
+      "v_accvgpr_read_b32 %2, a190\n\t"
+      "v_accvgpr_read_b32 %3, a191\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a188, %0\n\t"
+      "v_accvgpr_write_b32 a189, %1\n\t"
+      "v_accvgpr_write_b32 a190, %2\n\t"
+      "v_accvgpr_write_b32 a191, %3\n\t"
+      "v_accvgpr_read_b32 %0, a192\n\t"
+      "v_accvgpr_read_b32 %1, a193\n\t"
+      "v_accvgpr_read_b32 %2, a194\n\t"
+      "v_accvgpr_read_b32 %3, a195\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a192, %0\n\t"
+      "v_accvgpr_write_b32 a193, %1\n\t"
+      "v_accvgpr_write_b32 a194, %2\n\t"
+      "v_accvgpr_write_b32 a195, %3\n\t"
+      "v_accvgpr_read_b32 %0, a196\n\t"
+      "v_accvgpr_read_b32 %1, a197\n\t"
+      "v_accvgpr_read_b32 %2, a198\n\t"
+      "v_accvgpr_read_b32 %3, a199\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a196, %0\n\t"
+      "v_accvgpr_write_b32 a197, %1\n\t"
+      "v_accvgpr_write_b32 a198, %2\n\t"
+      "v_accvgpr_write_b32 a199, %3\n\t"
+      "v_accvgpr_read_b32 %0, a200\n\t"
+      "v_accvgpr_read_b32 %1, a201\n\t"
+      "v_accvgpr_read_b32 %2, a202\n\t"
+      "v_accvgpr_read_b32 %3, a203\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a200, %0\n\t"
+      "v_accvgpr_write_b32 a201, %1\n\t"
+      "v_accvgpr_write_b32 a202, %2\n\t"
+      "v_accvgpr_write_b32 a203, %3\n\t"
+      "v_accvgpr_read_b32 %0, a204\n\t"
+      "v_accvgpr_read_b32 %1, a205\n\t"
+      "v_accvgpr_read_b32 %2, a206\n\t"
+      "v_accvgpr_read_b32 %3, a207\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a204, %0\n\t"
+      "v_accvgpr_write_b32 a205, %1\n\t"
+      "v_accvgpr_write_b32 a206, %2\n\t"
+      "v_accvgpr_write_b32 a207, %3\n\t"
+      "v_accvgpr_read_b32 %0, a208\n\t"
+      "v_accvgpr_read_b32 %1, a209\n\t"
+      "v_accvgpr_read_b32 %2, a210\n\t"
+      "v_accvgpr_read_b32 %3, a211\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a208, %0\n\t"
+      "v_accvgpr_write_b32 a209, %1\n\t"
+      "v_accvgpr_write_b32 a210, %2\n\t"
+      "v_accvgpr_write_b32 a211, %3\n\t"
+      "v_accvgpr_read_b32 %0, a212\n\t"
+      "v_accvgpr_read_b32 %1, a213\n\t"
+      "v_accvgpr_read_b32 %2, a214\n\t"
+      "v_accvgpr_read_b32 %3, a215\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a212, %0\n\t"
+      "v_accvgpr_write_b32 a213, %1\n\t"
+      "v_accvgpr_write_b32 a214, %2\n\t"
+      "v_accvgpr_write_b32 a215, %3\n\t"
+      "v_accvgpr_read_b32 %0, a216\n\t"
+      "v_accvgpr_read_b32 %1, a217\n\t"
+      "v_accvgpr_read_b32 %2, a218\n\t"
+      "v_accvgpr_read_b32 %3, a219\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a216, %0\n\t"
+      "v_accvgpr_write_b32 a217, %1\n\t"
+      "v_accvgpr_write_b32 a218, %2\n\t"
+      "v_accvgpr_write_b32 a219, %3\n\t"
+      "v_accvgpr_read_b32 %0, a220\n\t"
+      "v_accvgpr_read_b32 %1, a221\n\t"
+      "v_accvgpr_read_b32 %2, a222\n\t"
+      "v_accvgpr_read_b32 %3, a223\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a220, %0\n\t"
+      "v_accvgpr_write_b32 a221, %1\n\t"
+      "v_accvgpr_write_b32 a222, %2\n\t"
+      "v_accvgpr_write_b32 a223, %3\n\t"
+      "v_accvgpr_read_b32 %0, a224\n\t"
+      "v_accvgpr_read_b32 %1, a225\n\t"
+      "v_accvgpr_read_b32 %2, a226\n\t"
+      "v_accvgpr_read_b32 %3, a227\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a224, %0\n\t"
+      "v_accvgpr_write_b32 a225, %1\n\t"
+      "v_accvgpr_write_b32 a226, %2\n\t"
+      "v_accvgpr_write_b32 a227, %3\n\t"
+      "v_accvgpr_read_b32 %0, a228\n\t"
+      "v_accvgpr_read_b32 %1, a229\n\t"
+      "v_accvgpr_read_b32 %2, a230\n\t"
+      "v_accvgpr_read_b32 %3, a231\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a228, %0\n\t"
+      "v_accvgpr_write_b32 a229, %1\n\t"
+      "v_accvgpr_write_b32 a230, %2\n\t"
+      "v_accvgpr_write_b32 a231, %3\n\t"
+      "v_accvgpr_read_b32 %0, a232\n\t"
+      "v_accvgpr_read_b32 %1, a233\n\t"
+      "v_accvgpr_read_b32 %2, a234\n\t"
+      "v_accvgpr_read_b32 %3, a235\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a232, %0\n\t"
+      "v_accvgpr_write_b32 a233, %1\n\t"
+      "v_accvgpr_write_b32 a234, %2\n\t"
+      "v_accvgpr_write_b32 a235, %3\n\t"
+      "v_accvgpr_read_b32 %0, a236\n\t"
+      "v_accvgpr_read_b32 %1, a237\n\t"
+      "v_accvgpr_read_b32 %2, a238\n\t"
+      "v_accvgpr_read_b32 %3, a239\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a236, %0\n\t"
+      "v_accvgpr_write_b32 a237, %1\n\t"
+      "v_accvgpr_write_b32 a238, %2\n\t"
+      "v_accvgpr_write_b32 a239, %3\n\t"
+      "v_accvgpr_read_b32 %0, a240\n\t"
+      "v_accvgpr_read_b32 %1, a241\n\t"
+      "v_accvgpr_read_b32 %2, a242\n\t"
+      "v_accvgpr_read_b32 %3, a243\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a240, %0\n\t"
+      "v_accvgpr_write_b32 a241, %1\n\t"
+      "v_accvgpr_write_b32 a242, %2\n\t"
+      "v_accvgpr_write_b32 a243, %3\n\t"
+      "v_accvgpr_read_b32 %0, a244\n\t"
+      "v_accvgpr_read_b32 %1, a245\n\t"
+      "v_accvgpr_read_b32 %2, a246\n\t"
+      "v_accvgpr_read_b32 %3, a247\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a244, %0\n\t"
+      "v_accvgpr_write_b32 a245, %1\n\t"
+      "v_accvgpr_write_b32 a246, %2\n\t"
+      "v_accvgpr_write_b32 a247, %3\n\t"
+      "v_accvgpr_read_b32 %0, a248\n\t"
+      "v_accvgpr_read_b32 %1, a249\n\t"
+      "v_accvgpr_read_b32 %2, a250\n\t"
+      "v_accvgpr_read_b32 %3, a251\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a248, %0\n\t"
+      "v_accvgpr_write_b32 a249, %1\n\t"
+      "v_accvgpr_write_b32 a250, %2\n\t"
+      "v_accvgpr_write_b32 a251, %3\n\t"
+      "v_accvgpr_read_b32 %0, a252\n\t"
+      "v_accvgpr_read_b32 %1, a253\n\t"
+      "v_accvgpr_read_b32 %2, a254\n\t"
+      "v_accvgpr_read_b32 %3, a255\n\t"
+      "v_mul_f32 %0, %0, %4\n\t"
+      "v_mul_f32 %1, %1, %4\n\t"
+      "v_mul_f32 %2, %2, %4\n\t"
+      "v_mul_f32 %3, %3, %4\n\t"
+      "v_accvgpr_write_b32 a252, %0\n\t"
+      "v_accvgpr_write_b32 a253, %1\n\t"
+      "v_accvgpr_write_b32 a254, %2\n\t"
+      "v_accvgpr_write_b32 a255, %3\n\t"
+      "s_nop 7"
+      : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "v"(alpha)
+      : "memory");
 }
 
 struct WorkItem {
   int b, k, n;  // sequence, chunk index, chunk count
 };
 
-__device__ __forceinline__ WorkItem find_work(const int32_t* split_offsets, int B, int g) {
+// The sequence of chunk g: the largest b with split_offsets[b] <= g. Each
+// round probes 64 evenly spaced entries at once (one load per lane) and
+// narrows the range 64-fold, so B <= 64 takes one round of loads and
+// B <= 4096 two, instead of a chain of dependent loads.
+__device__ __forceinline__ WorkItem find_work(const int32_t* split_offsets, int B, int g, int lane) {
   WorkItem w;
   if (split_offsets == nullptr) {
     w.b = g; w.k = 0; w.n = 1;
     return w;
   }
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {  // largest b with split_offsets[b] <= g
-    const int mid = (lo + hi + 1) >> 1;
-    if (split_offsets[mid] <= g) lo = mid; else hi = mid - 1;
+  int lo = 0, n = B;  // the answer lies in [lo, lo + n)
+  while (n > 64) {
+    const int step = (n + 63) / 64;
+    const bool le = lane * step < n && split_offsets[lo + lane * step] <= g;
+    const int c = max(__popcll(__ballot(le)), 1);
+    lo += (c - 1) * step;
+    n = min(step, n - (c - 1) * step);
   }
-  w.b = lo;
-  w.k = g - split_offsets[lo];
-  w.n = split_offsets[lo + 1] - split_offsets[lo];
+  const bool le = lane < n && split_offsets[lo + lane] <= g;
+  const int b = lo + max(__popcll(__ballot(le)), 1) - 1;
+  w.b = b;
+  w.k = g - split_offsets[b];
+  w.n = split_offsets[b + 1] - split_offsets[b];
   return w;
 }
 
@@ -186,8 +985,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int g16 = lane >> 4;  // lane group: k slice / token quad
-  const int r16 = lane & 15;  // the row this lane owns in MFMA outputs
+  const int r32 = lane & 31;   // the row this lane owns in MFMA outputs
+  const int hi32 = lane >> 5;  // upper half of the wave
 
   // XCD-aware mapping: workgroups x and x+8j run on the same XCD. The row
   // groups of one chunk (which read the same pages) get consecutive j.
@@ -198,7 +997,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int g = (rest / row_groups) * 8 + xcd;
   if (g >= a.total_splits) return;
 
-  const WorkItem wi = find_work(a.split_offsets, a.B, g);
+  const WorkItem wi = find_work(a.split_offsets, a.B, g, lane);
   const int b = wi.b;
   int L = a.seqlens[b];
   L = max(a.s_q, min(L, a.max_pages * kPage));
@@ -208,56 +1007,72 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int pg0 = (int)(((long long)kk * P) / n_chunks);
   const int pg1 = (int)(((long long)(kk + 1) * P) / n_chunks);
 
+  // Rows past the end (H*s_q not a multiple of 32) compute on a clamped row
+  // and write nothing.
   const int rows = a.s_q * a.H;
-  const int wave_row0 = rgrp * kRowsPerGroup + wave * kRowsPerWave;
-  const bool wave_active = wave_row0 < rows;
-  const int row = wave_row0 + r16;
+  const int row = rgrp * kRowsPerGroup + wave * kWaveRows + r32;
   const int row_c = min(row, rows - 1);
   const int qi = row_c / a.H;
   const int n_allowed = a.causal ? (L - a.s_q + qi + 1) : L;
   // Smallest allowed count over all rows (query 0's), the same for every wave.
   const int n_allowed_min = a.causal ? (L - a.s_q + 1) : L;
 
-  // Q^T fragments for the whole walk: k-step s holds q[row][32s + 8*g16 .. +8].
-  bf16x8_t qf[kQSteps];
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q_lat) + ((size_t)b * rows + row_c) * kDqk + 8 * g16;
-#pragma unroll
-    for (int s = 0; s < kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
-  }
-
-  f32x4_t acc_o[kColTiles];
-#pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) acc_o[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // base-2 reference max of this row
-  float l_loc = 0.f;        // this lane's share of the row's sum of P
-  const float sl2 = a.scale * 1.4426950408889634f;
-
   const char* cache = reinterpret_cast<const char*>(a.kv_cache);
   const int32_t* btab = a.block_table + (size_t)b * a.max_pages;
   const int last_phys = a.num_pages - 1;
 
-  // Per-lane LDS byte offsets inside a buffer.
-  // QK A operand for token tile t, k-step s: token 16t + r16, chunk 4s + g16:
-  //   1024*(18t + 9*(r16>>3) + (s>>1)) + 128*(r16&7) + 16*((4*(s&1) + g16) ^ F(r16)).
-  const int qk_base = 1024 * 9 * (r16 >> 3) + 128 * (r16 & 7);
-  const int qk_x0 = 16 * (g16 ^ swz(r16));
-  const int qk_x1 = 16 * ((4 + g16) ^ swz(r16));
-  // PV A operand (transposed read) for k-step u, read rd, column tile ct: lane
-  // group g16 reads tokens 32u + 16rd + 4*g16 + jj (jj = (lane>>2)&3) and the
-  // lane supplies the 4 columns from 16ct + 4*qq (qq = lane&3), i.e. chunk
-  // 2ct + (qq>>1), half-chunk qq&1:
-  //   1024*(9*(4u + 2rd + (g16>>1)) + (ct>>2)) + 128*(4*(g16&1) + jj)
-  //   + 16*((2*(ct&3)) ^ Z) + 8*(qq&1),  Z = (qq>>1) ^ F(token).
-  const int jj = (lane >> 2) & 3;
-  const int qq = lane & 3;
-  const int pv_tok = 4 * g16 + jj;  // token within its 16-token block
-  const int pv_base = 1024 * 9 * (g16 >> 1) + 128 * (4 * (g16 & 1) + jj) + 8 * (qq & 1);
-  const int pv_z = (qq >> 1) ^ swz(pv_tok);
-
+  // Block-table entries are read one page ahead of their use, so that no
+  // page waits on a table read.
+  int phys_ahead = 0;
   if (pg0 < pg1) {
     const int phys = min(max(btab[pg0], 0), last_phys);
     issue_page(make_page_load(cache + (size_t)phys * kPageBytes, smem, wave, lane));
+    phys_ahead = btab[min(pg0 + 1, pg1 - 1)];
+  }
+
+  // Q^T fragments for the whole walk, loaded after the first page's loads
+  // are issued (the block-table chain before them is the longer path):
+  // k-step s holds q[row][16s + 8*hi32 .. +8] (the B layout of
+  // v_mfma_f32_32x32x16_bf16: lane l holds k = 8(l>>5) .. +8 of column l&31).
+  bf16x8_t qf[kQSteps];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q_lat) + ((size_t)b * rows + row_c) * kDqk + 8 * hi32;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
+  }
+
+  f32x16_t acc_o[kColTiles];
+#pragma unroll
+  for (int i = 0; i < kColTiles; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
+  float m_ref = -INFINITY;  // base-2 reference max of this row
+  float l_loc = 0.f;        // this lane's share of the row's sum of P
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  // Per-lane LDS byte offsets inside a page buffer.
+  // QK A operand for token tile T, k-step s: token 32T + r32, chunk 2s + hi32:
+  //   36864T + 1024*(9*(r32>>3) + (s>>2)) + 128*(r32&7) + 16*((2(s&3) + hi32) ^ F(r32)).
+  const int qk_base = 1024 * 9 * (r32 >> 3) + 128 * (r32 & 7);
+  int qk_x[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qk_x[q] = qk_base + 16 * ((2 * q + hi32) ^ swz(r32));
+  // PV A operand (transposed read) for k-step u, read rd, column tile i: lane
+  // group g = lane>>4 reads tokens 16u + 8rd + 4(g>>1) + j (j = (lane>>2)&3)
+  // and supplies the 4 columns from 32i + 16(g&1) + 4q (q = lane&3), i.e.
+  // chunk 4i + 2(g&1) + (q>>1), half-chunk q&1:
+  //   1024*(9*(2u + rd) + (i>>1)) + 128*(4(g>>1) + j)
+  //   + 16*((4(i&1)) ^ Z_rd) + 8*(q&1),  Z_rd = (2(g&1) + (q>>1)) ^ F(token).
+  const int g16 = lane >> 4;
+  const int jj = (lane >> 2) & 3;
+  const int qq = lane & 3;
+  const int pv_base = 128 * (4 * (g16 >> 1) + jj) + 8 * (qq & 1);
+  int pv_x[2][2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int z = (2 * (g16 & 1) + (qq >> 1)) ^ swz(8 * rd + 4 * (g16 >> 1) + jj);
+    pv_x[rd][0] = pv_base + 16 * z;
+    pv_x[rd][1] = pv_base + 16 * (z ^ 4);
   }
 
   for (int pg = pg0; pg < pg1; ++pg) {
@@ -267,15 +1082,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     // and also guarantees every wave is done with the other buffer.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    // An active wave issues the next page's loads one per QK k-step below,
-    // so they drain behind the MFMAs instead of stalling the wave here.
-    // (Built unconditionally, from a clamped table index, so that its bases
-    // stay plain wave-uniform values in SGPRs.)
+    // The next page's loads are issued one per two QK k-steps of the first
+    // tile: early enough to land before the page ends, and behind MFMAs. (Built
+    // unconditionally, from a clamped table index, so that its bases stay
+    // wave-uniform SGPRs.)
     const bool has_next = pg + 1 < pg1;
-    const int phys_next = min(max(btab[min(pg + 1, pg1 - 1)], 0), last_phys);
+    const int phys_next = min(max(phys_ahead, 0), last_phys);
+    phys_ahead = btab[min(pg + 2, pg1 - 1)];
     const PageLoad next = make_page_load(cache + (size_t)phys_next * kPageBytes,
                                          smem + ((pg + 1 - pg0) & 1) * kPageBytes, wave, lane);
-    if (has_next && !wave_active) issue_page(next);
     const int valid = L - pg * kPage;  // tokens of this page that exist
     if (valid < kPage) {
       // Zero the token slots past the end of the sequence: their scores are
@@ -287,141 +1102,148 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       }
       __syncthreads();
     }
-    if (!wave_active) continue;
+    const bool full_page = (pg + 1) * kPage <= n_allowed_min;
 
-    // ---- S^T = K Q^T for the 64 tokens: 4 token tiles x 18 k-steps; the
-    // K fragments of k-step s+1 are read while the MFMAs of step s run. Two
-    // copies (with and without the next page's loads) keep the k-step loop
-    // free of branches.
-    f32x4_t st[4];
-    const char* qa = buf + qk_base;
-    auto qk = [&](auto with_loads) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      bf16x8_t kf[2][4];
+    for (int T = 0; T < 2; ++T) {
+      // ---- S^T = K Q^T for 32 tokens: 36 k-steps, the K fragment of step
+      // s+3 read while the MFMA of step s runs. The schedule is pinned step
+      // by step (sched_barrier): left alone, the compiler sinks each
+      // prefetch to just after the MFMA that frees its registers.
+      f32x16_t st;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kf[0][t] = *reinterpret_cast<const bf16x8_t*>(qa + 1024 * 18 * t + qk_x0);
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      auto k_frag = [&](int s) {
+        return *reinterpret_cast<const bf16x8_t*>(buf + qk_x[s & 3] + 36864 * T + 1024 * (s >> 2));
+      };
+      constexpr int kKDepth = 3;
+      bf16x8_t kf[kKDepth];
+#pragma unroll
+      for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(s);
 #pragma unroll
       for (int s = 0; s < kQSteps; ++s) {
-        if constexpr (decltype(with_loads)::value) issue_line(next, s);
-        if (s + 1 < kQSteps) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            kf[(s + 1) & 1][t] = *reinterpret_cast<const bf16x8_t*>(
-                qa + 1024 * (18 * t + ((s + 1) >> 1)) + (((s + 1) & 1) ? qk_x1 : qk_x0));
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][t], qf[s], st[t], 0, 0, 0);
+        const bf16x8_t cur = kf[s % kKDepth];
+        if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(s + kKDepth);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (T == 0 && has_next && (s & 1) == 0) issue_line(next, s >> 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    if (has_next) qk(std::true_type{}); else qk(std::false_type{});
 
-    // ---- scale, mask, row max (token of st[t][r] = 64pg + 16t + 4g16 + r).
-    // Pages wholly inside every row's allowed range skip the mask.
-    const int tok0 = pg * kPage + 4 * g16;
-    float mx = -INFINITY;
-    if ((pg + 1) * kPage <= n_allowed_min) {
+      // ---- mask, row max. st[r] belongs to token 64pg + 32T + 8(r>>2) +
+      // 4*hi32 + (r&3). The scale is positive, so the max of the raw scores,
+      // scaled, is the max of the scaled scores.
+      if (!full_page) {
+        const int tok0 = pg * kPage + 32 * T + 4 * hi32;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          st[t][r] *= sl2;
-          mx = fmaxf(mx, st[t][r]);
-        }
+        for (int r = 0; r < 16; ++r)
+          if (tok0 + 8 * (r >> 2) + (r & 3) >= n_allowed) st[r] = -INFINITY;
       }
-    } else {
+      float mx[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int r = 0; r < 8; ++r) mx[r] = fmaxf(st[r], st[r + 8]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = (tok0 + 16 * t + r < n_allowed) ? st[t][r] * sl2 : -INFINITY;
-          st[t][r] = v;
-          mx = fmaxf(mx, v);
-        }
+      for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], mx[r + 4]);
+      float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      mt = fmaxf(mt, other_half(mt)) * sl2;
+      const float m_new = (mt > m_ref + 8.0f) ? mt : m_ref;
+      // Rescale O and l when the reference moves (nothing to rescale before
+      // the first allowed key: O and l are still zero).
+      if (__any(m_new > m_ref && m_ref != -INFINITY)) {
+        const float alpha = (m_new > m_ref && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        agpr_fence();
+        scale_accumulators(alpha);
+        l_loc *= alpha;
       }
-    }
-    mx = max4lanes(mx);
-    const float m_new = fmaxf(m_ref, mx);
-    if (__any(m_new > m_ref + 8.0f)) {
-      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_loc *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) acc_o[ct] *= alpha;
       m_ref = m_new;
-    }
-    const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
+      const float neg_ref = (m_ref == -INFINITY) ? 0.f : -m_ref;
 
-    // ---- P = exp2(v - m_ref), packed to bf16 as the PV B operand:
-    // k-step u takes tiles 2u (k 0..3 of each lane group) and 2u+1 (k 4..7).
-    bf16x8_t pf[2];
-    float psum = 0.f;
+      // ---- P = exp2(s*scale - m_ref), packed to bf16 as the PV B operand:
+      // k-step 2T + kk takes scores 8kk .. 8kk+7.
+      bf16x8_t pf[2];
+      float ps[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(st[t][r] - mref);
-        psum += p;
-        pf[t >> 1][4 * (t & 1) + r] = (__bf16)p;
+      for (int r = 0; r < 8; ++r) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, neg_ref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + 8], sl2, neg_ref));
+        pf[0][r] = (__bf16)p0;
+        pf[1][r] = (__bf16)p1;
+        ps[r] = p0 + p1;
       }
-    }
-    l_loc += psum;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ps[r] += ps[r + 4];
+      l_loc += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
-    // ---- O^T += V^T P^T: 2 k-steps of 32 tokens x 32 column tiles; the V^T
-    // fragments run 4 MFMAs ahead of their use.
-    const char* va = buf + pv_base;
-    auto load_v = [&](int i) {
-      const int u = i >> 5, ct = i & 31;
-      bf16x8_t av;
+      // ---- O^T += V^T P^T: 2 k-steps x 16 column tiles, V^T fragments 4
+      // MFMAs ahead.
+      auto v_frag = [&](int u, int i) {
+        bf16x8_t av;
 #pragma unroll
-      for (int rd = 0; rd < 2; ++rd) {
-        const int off = 1024 * (9 * (4 * u + 2 * rd) + (ct >> 2)) + 16 * ((2 * (ct & 3)) ^ pv_z);
-        const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(va + off));
-        av[4 * rd + 0] = v[0];
-        av[4 * rd + 1] = v[1];
-        av[4 * rd + 2] = v[2];
-        av[4 * rd + 3] = v[3];
+        for (int rd = 0; rd < 2; ++rd) {
+          const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4_t*)(buf + pv_x[rd][i & 1] + 1024 * (9 * (2 * u + rd) + (i >> 1))));
+          av[4 * rd + 0] = v[0];
+          av[4 * rd + 1] = v[1];
+          av[4 * rd + 2] = v[2];
+          av[4 * rd + 3] = v[3];
+        }
+        return av;
+      };
+      constexpr int kPvDepth = 4;
+      bf16x8_t vf[kPvDepth];
+#pragma unroll
+      for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(2 * T + (n >> 4), n & 15);
+#pragma unroll
+      for (int n = 0; n < 2 * kColTiles; ++n) {
+        const bf16x8_t cur = vf[n % kPvDepth];
+        if (n + kPvDepth < 2 * kColTiles)
+          vf[n % kPvDepth] = v_frag(2 * T + ((n + kPvDepth) >> 4), (n + kPvDepth) & 15);
+        if ((n & 15) == 0)
+          mfma_pv<true>(acc_o[n & 15], cur, pf[n >> 4]);  // first use of this P fragment
+        else
+          mfma_pv<false>(acc_o[n & 15], cur, pf[n >> 4]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      return av;
-    };
-    constexpr int kPvDepth = 4;
-    bf16x8_t vf[kPvDepth];
-#pragma unroll
-    for (int i = 0; i < kPvDepth; ++i) vf[i] = load_v(i);
-#pragma unroll
-    for (int i = 0; i < 2 * kColTiles; ++i) {
-      const bf16x8_t cur = vf[i % kPvDepth];
-      if (i + kPvDepth < 2 * kColTiles) vf[i % kPvDepth] = load_v(i + kPvDepth);
-      acc_o[i & 31] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pf[i >> 5], acc_o[i & 31], 0, 0, 0);
     }
   }
 
-  if (!wave_active) return;
-
-  // ---- finalize: o = O / l, lse = ln2 * (m_ref + log2 l)
-  const float l_tot = sum4lanes(l_loc);
+  // ---- finalize: o = O / l, lse = ln2 * (m_ref + log2 l); l is split over
+  // the two lanes of a row.
+  agpr_fence();
+  const float l_tot = l_loc + other_half(l_loc);
   const bool any = l_tot > 0.f;
   const float inv = any ? 1.f / l_tot : 0.f;
   const float lse_v = any ? (m_ref + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   if (row >= rows) return;
 
-  // acc_o[ct][r] is O^T[16ct + 4g16 + r][row]: four consecutive columns.
+  // acc_o[i][r] is O^T[32i + 8(r>>2) + 4*hi32 + (r&3)][row]: runs of four
+  // consecutive columns.
   if (n_chunks == 1 && a.o_lat != nullptr) {
-    __bf16* orow = reinterpret_cast<__bf16*>(a.o_lat) + ((size_t)b * rows + row) * kDv + 4 * g16;
+    __bf16* orow = reinterpret_cast<__bf16*>(a.o_lat) + ((size_t)b * rows + row) * kDv + 4 * hi32;
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) {
-      bf16x4_t v;
-      v[0] = (__bf16)(acc_o[ct][0] * inv);
-      v[1] = (__bf16)(acc_o[ct][1] * inv);
-      v[2] = (__bf16)(acc_o[ct][2] * inv);
-      v[3] = (__bf16)(acc_o[ct][3] * inv);
-      *reinterpret_cast<bf16x4_t*>(orow + 16 * ct) = v;
-    }
-    if (g16 == 0) a.lse[(size_t)b * rows + row] = lse_v;
+    for (int i = 0; i < kColTiles; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc_o[i][4 * q4 + e] * inv);
+        *reinterpret_cast<bf16x4_t*>(orow + 32 * i + 8 * q4) = v;
+      }
+    if (hi32 == 0) a.lse[(size_t)b * rows + row] = lse_v;
   } else {
-    float* orow = a.o_part + ((size_t)g * rows + row) * kDv + 4 * g16;
+    // Chunk partials in bf16 like the output (the LSE stays fp32): half the
+    // bytes every workgroup writes at its end and the combine reads back.
+    __bf16* orow = static_cast<__bf16*>(a.o_part) + ((size_t)g * rows + row) * kDv + 4 * hi32;
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) *reinterpret_cast<f32x4_t*>(orow + 16 * ct) = acc_o[ct] * inv;
-    if (g16 == 0) a.lse_part[(size_t)g * rows + row] = lse_v;
+    for (int i = 0; i < kColTiles; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc_o[i][4 * q4 + e] * inv);
+        *reinterpret_cast<bf16x4_t*>(orow + 32 * i + 8 * q4) = v;
+      }
+    if (hi32 == 0) a.lse_part[(size_t)g * rows + row] = lse_v;
   }
 }
 

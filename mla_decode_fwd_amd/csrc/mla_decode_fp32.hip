@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * kWaves) void mla_decode_fp32_kernel(DecodeArgs
     for (int e = 0; e < 8; ++e) orow[lane + 64 * e] = o[e] * inv;
     if (lane == 0) a.lse[(size_t)b * rows + row] = lse_v;
   } else {
-    float* orow = a.o_part + ((size_t)g * rows + row) * kDv;
+    float* orow = static_cast<float*>(a.o_part) + ((size_t)g * rows + row) * kDv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) orow[lane + 64 * e] = o[e] * inv;
     if (lane == 0) a.lse_part[(size_t)g * rows + row] = lse_v;

@@ -12,7 +12,7 @@ constexpr int kDqk = 576;       // key width: latent 512 + RoPE 64
 constexpr int kDv = 512;        // value width: the latent
 constexpr int kPage = 64;       // tokens per cache page
 constexpr int kMaxSplits = 64;  // chunks per sequence at most
-constexpr int kRowsPerGroup = 64;   // query rows (token, head) per decode workgroup
+constexpr int kRowsPerGroup = 128;  // query rows (token, head) per decode workgroup
 
 // Arguments of one decode launch, already validated on the host.
 struct DecodeArgs {
@@ -27,7 +27,7 @@ struct DecodeArgs {
   int num_pages;
   float scale;
   int causal;
-  float* o_part;    // [total_splits, s_q, H, 512] when split, else nullptr
+  void* o_part;     // [total_splits, s_q, H, 512] in the output dtype when split, else nullptr
   float* lse_part;  // [total_splits, s_q, H]
   void* o_lat;      // [B, s_q, H, 512]; nullptr: write partials for every chunk
   float* lse;       // [B, s_q, H]; nullptr together with o_lat
@@ -38,7 +38,8 @@ hipError_t launch_decode_fp32(const DecodeArgs& a, hipStream_t stream);
 
 // LSE merge. skip_single: sequences with one chunk were written directly by
 // the decode kernel and are left alone.
-hipError_t launch_combine(const float* o_part, const float* lse_part, const int32_t* split_offsets,
+// o_part holds the output dtype (bf16 when out_bf16, else fp32).
+hipError_t launch_combine(const void* o_part, const float* lse_part, const int32_t* split_offsets,
                           int total_splits, int B, int s_q, int H, bool out_bf16, bool skip_single,
                           void* o_lat, float* lse, hipStream_t stream);
 

@@ -56,13 +56,13 @@ def test_workspace_size(lib):
 
 
 def test_plan_headline_batch_fills_the_chip():
-    # 128 head rows are two workgroups of 64 rows each, so 64 sequences x 64
-    # pages over 256 compute units give chunks of 32 pages: 2 per sequence,
-    # 128 chunks x 2 row groups = one workgroup per compute unit.
+    # A workgroup covers all 128 head rows, so 64 sequences x 64 pages over
+    # 256 compute units give chunks of 16 pages: 4 per sequence, 256 chunks =
+    # one workgroup per compute unit.
     p = mla.decode_plan([4096] * 64, s_q=1, H=128)
-    assert (p.num_splits == 2).all() and p.total_splits == 128
-    assert p.workspace_bytes == mla.decode_workspace_size(128, 1, 128)
-    assert np.array_equal(p.split_offsets, np.arange(65) * 2)
+    assert (p.num_splits == 4).all() and p.total_splits == 256
+    assert p.workspace_bytes == mla.decode_workspace_size(256, 1, 128)
+    assert np.array_equal(p.split_offsets, np.arange(65) * 4)
 
 
 def test_plan_long_context_respects_cap_and_balances():
@@ -113,6 +113,8 @@ def test_decode_fwd_validation(lib):
     assert _fwd(lib, B=0) == INVALID
     assert _fwd(lib, npages=0) == INVALID
     assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, scale=0.0) == INVALID
+    assert _fwd(lib, scale=-0.07) == INVALID
     assert _fwd(lib, dqk=128) == UNSUPPORTED
     assert _fwd(lib, dv=128) == UNSUPPORTED
     assert _fwd(lib, page=16) == UNSUPPORTED

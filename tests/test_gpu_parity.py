@@ -173,7 +173,11 @@ def test_splitkv_combine(out_dtype):
     lse_part = (rng.standard_normal((S, s_q, H)) * 3).astype(np.float32)
     lse_part[1, 0, :4] = -np.inf  # empty chunks
     lse_part[5:9, 1, 3] = -np.inf
-    o_gpu, l_gpu = mla.mla_splitkv_combine(torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda(),
+    # The partials come in the output dtype; the reference merges the same
+    # (rounded) values in fp64.
+    o_part_t = torch.from_numpy(o_part).to(out_dtype)
+    o_part = o_part_t.to(torch.float64).numpy()
+    o_gpu, l_gpu = mla.mla_splitkv_combine(o_part_t.cuda(), torch.from_numpy(lse_part).cuda(),
                                            torch.from_numpy(off).cuda(), S, len(counts), out_dtype)
     torch.cuda.synchronize()
     o_ref = np.zeros((len(counts), s_q, H, 512))
@@ -208,12 +212,36 @@ def test_partials_only_then_combine_matches_one_call(dtype):
     res = mla.mla_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale, case.causal,
                              split_offsets=offs, total_splits=p.total_splits, workspace=ws, partials_only=True)
     assert res == (None, None)
-    o_part, lse_part = mla.workspace_partials(ws, p.total_splits, case.s_q, case.H)
+    o_part, lse_part = mla.workspace_partials(ws, p.total_splits, case.s_q, case.H, dtype)
     o2, l2 = mla.mla_splitkv_combine(o_part, lse_part, offs, p.total_splits, case.B, dtype)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     o_ref, l_ref = oracle(case)
     compare(o2, l2, o_ref, l_ref, dtype, "partials+combine")
+
+
+def test_prepared_calls_match_plain_calls():
+    # A prepared decode + combine (checked and marshalled once) launches the
+    # same entry points as the plain calls: identical results, repeatably.
+    case = make_decode_case([700, 64, 1500], s_q=1, H=128, seed=43)
+    d = to_device(case)
+    p = mla.decode_plan(case.seqlens.tolist(), case.s_q, case.H, num_cus=16)
+    offs = p.device_offsets("cuda")
+    o1, l1 = mla.mla_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale,
+                                case.causal, split_offsets=offs, total_splits=p.total_splits)
+    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dec, _ = mla.prepare_decode(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale, case.causal,
+                                split_offsets=offs, total_splits=p.total_splits, workspace=ws, partials_only=True)
+    o_part, lse_part = mla.workspace_partials(ws, p.total_splits, case.s_q, case.H)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    comb = mla.prepare_combine(o_part, lse_part, offs, p.total_splits, case.B, torch.bfloat16, o2, l2)
+    for _ in range(2):
+        o2.zero_()
+        dec()
+        comb()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
