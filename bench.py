@@ -13,9 +13,12 @@ queries alternate between steps so no step finds the previous one's 302 MB of
 KV in the 256 MB last-level cache.
 
 Prints one JSON line. `roofline` describes the dominant kernel (the decode
-kernel): algorithmic bytes per launch over its average duration, taken from
-HIP events recorded around each decode launch of the timed steps on the
-stream the library launches on. `traffic` (measured HBM bytes per launch) is
+kernel): algorithmic bytes per launch over its average duration. Three
+timed regions run back to back on the stream the library launches on, each
+bracketed by one pair of HIP events (an event between kernels costs the GPU
+several microseconds, so none sits inside a region): the K steps (this gives
+`value` and `ms_per_step`), then K decode launches alone (the decode kernel's
+average duration), then K merge launches alone. `traffic` (measured HBM bytes per launch) is
 the scaled FETCH_SIZE + WRITE_SIZE reading kept in
 profiles/mla_decode_bf16_b64_ctx4096.md (made by
 mla_decode_fwd_amd.profile_summary from rocprofv3 counter runs of this
@@ -153,7 +156,6 @@ def main():
     o = torch.empty((B, s_q, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()  # the library launches on it
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
     # Both launches are prepared once (checks and argument marshalling done
     # up front) so that the host enqueues a step faster than the GPU runs it.
@@ -162,32 +164,26 @@ def main():
                  for s in sets]
     comb_call = mla.prepare_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o, lse)
 
-    def step(i, events=None):
-        if events:
-            events[0].record(stream)
+    def step(i):
         dec_calls[i % 2]()
-        if events:
-            events[1].record(stream)
-            events[2].record(stream)
         comb_call()
-        if events:
-            events[3].record(stream)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i, ev[i])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    decode_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    combine_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    step_gpu_ms, ms_per_step = timed(step)
+    decode_ms, _ = timed(lambda i: dec_calls[i % 2]())
+    combine_ms, _ = timed(lambda i: comb_call())
 
     if args.copy_mb > 0:
         n = args.copy_mb << 20

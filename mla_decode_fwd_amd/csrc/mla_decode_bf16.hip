@@ -27,7 +27,9 @@
 //     within each 16-lane group; B = P^T taken straight from the score
 //     registers: the score layout of a 16-token half tile is exactly the B
 //     layout of one k-step with the tokens of the k-step permuted, and the
-//     V^T reads use the same permutation).
+//     V^T reads use the same permutation). The two tiles are staggered so
+//     that each tile's exponentials run between the MFMAs of the other
+//     tile's product (MFMA and VALU work of one wave execute together).
 //   * Softmax in base 2 with a lazily updated reference max: O and l are
 //     rescaled only when a row's max grows by more than 8 (so P <= 2^8); the
 //     result is exact because P, l and O always share the reference.
@@ -988,14 +990,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int r32 = lane & 31;   // the row this lane owns in MFMA outputs
   const int hi32 = lane >> 5;  // upper half of the wave
 
-  // XCD-aware mapping: workgroups x and x+8j run on the same XCD. The row
-  // groups of one chunk (which read the same pages) get consecutive j.
+  // XCD-aware mapping: workgroups x and x+8j run on the same XCD (its own
+  // L2). Each XCD takes a contiguous range of chunks, so the chunks of one
+  // sequence (which load the same Q rows) and the row groups of one chunk
+  // (which read the same pages) share an L2.
   const int x = blockIdx.x;
   const int xcd = x & 7;
   const int rest = x >> 3;
   const int rgrp = rest % row_groups;
-  const int g = (rest / row_groups) * 8 + xcd;
-  if (g >= a.total_splits) return;
+  const int per_xcd = (a.total_splits + 7) / 8;
+  const int g = xcd * per_xcd + rest / row_groups;
+  if (rest / row_groups >= per_xcd || g >= a.total_splits) return;
 
   const WorkItem wi = find_work(a.split_offsets, a.B, g, lane);
   const int b = wi.b;
@@ -1104,35 +1109,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     }
     const bool full_page = (pg + 1) * kPage <= n_allowed_min;
 
+    // A page is two 32-token tiles, staggered so that the softmax work of
+    // one tile runs between the MFMAs of the other: QK(T0); QK(T1) with
+    // tile 0's exponentials; PV(T0) with tile 1's exponentials; PV(T1).
+    // Tile 1's P uses a provisional reference taken before PV(T0); O and l
+    // move to it only after PV(T0) has added tile 0 (which used the old one).
+    auto k_frag = [&](int T, int s) {
+      return *reinterpret_cast<const bf16x8_t*>(buf + qk_x[s & 3] + 36864 * T + 1024 * (s >> 2));
+    };
+    auto v_frag = [&](int u, int i) {
+      bf16x8_t av;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      // ---- S^T = K Q^T for 32 tokens: 36 k-steps, the K fragment of step
-      // s+3 read while the MFMA of step s runs. The schedule is pinned step
-      // by step (sched_barrier): left alone, the compiler sinks each
-      // prefetch to just after the MFMA that frees its registers.
-      f32x16_t st;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
-      auto k_frag = [&](int s) {
-        return *reinterpret_cast<const bf16x8_t*>(buf + qk_x[s & 3] + 36864 * T + 1024 * (s >> 2));
-      };
-      constexpr int kKDepth = 3;
-      bf16x8_t kf[kKDepth];
-#pragma unroll
-      for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(s);
-#pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        const bf16x8_t cur = kf[s % kKDepth];
-        if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(s + kKDepth);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (T == 0 && has_next && (s & 1) == 0) issue_line(next, s >> 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int rd = 0; rd < 2; ++rd) {
+        const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)(buf + pv_x[rd][i & 1] + 1024 * (9 * (2 * u + rd) + (i >> 1))));
+        av[4 * rd + 0] = v[0];
+        av[4 * rd + 1] = v[1];
+        av[4 * rd + 2] = v[2];
+        av[4 * rd + 3] = v[3];
       }
-
-      // ---- mask, row max. st[r] belongs to token 64pg + 32T + 8(r>>2) +
-      // 4*hi32 + (r&3). The scale is positive, so the max of the raw scores,
-      // scaled, is the max of the scaled scores.
+      return av;
+    };
+    // Masked scores to -inf, then the base-2 row max over the tile. st[r]
+    // belongs to token 64pg + 32T + 8(r>>2) + 4*hi32 + (r&3). The scale is
+    // positive, so the max of the raw scores, scaled, is the max of the
+    // scaled scores.
+    auto tile_max = [&](f32x16_t& st, int T) {
       if (!full_page) {
         const int tok0 = pg * kPage + 32 * T + 4 * hi32;
 #pragma unroll
@@ -1144,11 +1146,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       for (int r = 0; r < 8; ++r) mx[r] = fmaxf(st[r], st[r + 8]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], mx[r + 4]);
-      float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-      mt = fmaxf(mt, other_half(mt)) * sl2;
-      const float m_new = (mt > m_ref + 8.0f) ? mt : m_ref;
-      // Rescale O and l when the reference moves (nothing to rescale before
-      // the first allowed key: O and l are still zero).
+      const float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      return fmaxf(mt, other_half(mt)) * sl2;
+    };
+    // O and l to a new reference (nothing to rescale before the first
+    // allowed key: O and l are still zero).
+    auto move_reference = [&](float m_new) {
       if (__any(m_new > m_ref && m_ref != -INFINITY)) {
         const float alpha = (m_new > m_ref && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
         agpr_fence();
@@ -1156,52 +1159,100 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         l_loc *= alpha;
       }
       m_ref = m_new;
-      const float neg_ref = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    };
+    // Two P values of a tile (scores e and e+1), packed into the PV operand:
+    // k-step kk of the tile takes scores 8kk .. 8kk+7.
+    auto p_pair = [&](const f32x16_t& st, int e, float neg_ref, bf16x8_t* pf, float& psum) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e], sl2, neg_ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e + 1], sl2, neg_ref));
+      pf[e >> 3][e & 7] = (__bf16)p0;
+      pf[e >> 3][(e & 7) + 1] = (__bf16)p1;
+      psum += p0 + p1;
+    };
+    constexpr int kKDepth = 3;
+    constexpr int kPvDepth = 4;
 
-      // ---- P = exp2(s*scale - m_ref), packed to bf16 as the PV B operand:
-      // k-step 2T + kk takes scores 8kk .. 8kk+7.
-      bf16x8_t pf[2];
-      float ps[8];
+    // ---- QK(T0), with the next page's loads.
+    f32x16_t st0;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, neg_ref));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + 8], sl2, neg_ref));
-        pf[0][r] = (__bf16)p0;
-        pf[1][r] = (__bf16)p1;
-        ps[r] = p0 + p1;
+    for (int r = 0; r < 16; ++r) st0[r] = 0.f;
+    {
+      bf16x8_t kf[kKDepth];
+#pragma unroll
+      for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(0, s);
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) {
+        const bf16x8_t cur = kf[s % kKDepth];
+        if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(0, s + kKDepth);
+        st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (has_next && (s & 1) == 0) issue_line(next, s >> 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ps[r] += ps[r + 4];
-      l_loc += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+    const float mt0 = tile_max(st0, 0);
+    move_reference((mt0 > m_ref + 8.0f) ? mt0 : m_ref);
+    const float neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
 
-      // ---- O^T += V^T P^T: 2 k-steps x 16 column tiles, V^T fragments 4
-      // MFMAs ahead.
-      auto v_frag = [&](int u, int i) {
-        bf16x8_t av;
+    // ---- QK(T1), with tile 0's P (two values every four k-steps).
+    f32x16_t st1;
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-          const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4_t*)(buf + pv_x[rd][i & 1] + 1024 * (9 * (2 * u + rd) + (i >> 1))));
-          av[4 * rd + 0] = v[0];
-          av[4 * rd + 1] = v[1];
-          av[4 * rd + 2] = v[2];
-          av[4 * rd + 3] = v[3];
-        }
-        return av;
-      };
-      constexpr int kPvDepth = 4;
+    for (int r = 0; r < 16; ++r) st1[r] = 0.f;
+    bf16x8_t pf0[2];
+    float psum0 = 0.f;
+    {
+      bf16x8_t kf[kKDepth];
+#pragma unroll
+      for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(1, s);
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) {
+        const bf16x8_t cur = kf[s % kKDepth];
+        if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(1, s + kKDepth);
+        st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st1, 0, 0, 0);
+        if ((s & 3) == 0 && s < 32) p_pair(st0, s >> 1, neg0, pf0, psum0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    l_loc += psum0;
+    const float mt1 = tile_max(st1, 1);
+    const float m1 = (mt1 > m_ref + 8.0f) ? mt1 : m_ref;  // provisional reference of tile 1
+    const float neg1 = (m1 == -INFINITY) ? 0.f : -m1;
+
+    // ---- PV(T0), with tile 1's P.
+    bf16x8_t pf1[2];
+    float psum1 = 0.f;
+    {
       bf16x8_t vf[kPvDepth];
 #pragma unroll
-      for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(2 * T + (n >> 4), n & 15);
+      for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(n >> 4, n & 15);
 #pragma unroll
       for (int n = 0; n < 2 * kColTiles; ++n) {
         const bf16x8_t cur = vf[n % kPvDepth];
-        if (n + kPvDepth < 2 * kColTiles)
-          vf[n % kPvDepth] = v_frag(2 * T + ((n + kPvDepth) >> 4), (n + kPvDepth) & 15);
+        if (n + kPvDepth < 2 * kColTiles) vf[n % kPvDepth] = v_frag((n + kPvDepth) >> 4, (n + kPvDepth) & 15);
         if ((n & 15) == 0)
-          mfma_pv<true>(acc_o[n & 15], cur, pf[n >> 4]);  // first use of this P fragment
+          mfma_pv<true>(acc_o[n & 15], cur, pf0[n >> 4]);  // first use of this P fragment
         else
-          mfma_pv<false>(acc_o[n & 15], cur, pf[n >> 4]);
+          mfma_pv<false>(acc_o[n & 15], cur, pf0[n >> 4]);
+        if ((n & 3) == 0) p_pair(st1, n >> 1, neg1, pf1, psum1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    move_reference(m1);
+    l_loc += psum1;
+
+    // ---- PV(T1).
+    {
+      bf16x8_t vf[kPvDepth];
+#pragma unroll
+      for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(2 + (n >> 4), n & 15);
+#pragma unroll
+      for (int n = 0; n < 2 * kColTiles; ++n) {
+        const bf16x8_t cur = vf[n % kPvDepth];
+        if (n + kPvDepth < 2 * kColTiles) vf[n % kPvDepth] = v_frag(2 + ((n + kPvDepth) >> 4), (n + kPvDepth) & 15);
+        if ((n & 15) == 0)
+          mfma_pv<true>(acc_o[n & 15], cur, pf1[n >> 4]);
+        else
+          mfma_pv<false>(acc_o[n & 15], cur, pf1[n >> 4]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
