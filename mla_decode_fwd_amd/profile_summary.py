@@ -84,6 +84,8 @@ def main():
                     help="the bench command line of the counter runs, without --copy-mb (default: --command)")
     ap.add_argument("--workload", default="batched decode B=64 x ctx 4096, s_q=1, H=128, bf16")
     ap.add_argument("--algorithmic-bytes", type=float, default=None)
+    ap.add_argument("--bench-output", default=None,
+                    help="stdout of the kernel-trace run (bench.py's JSON line), for the event-vs-trace check")
     ap.add_argument("--out", required=True)
     args = ap.parse_args()
 
@@ -107,6 +109,17 @@ def main():
               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
         lines.append(f"| {_short(name)} | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {pct:.1f} |")
+    if args.bench_output:
+        import json
+        rec = None
+        for line in open(args.bench_output, encoding="utf-8", errors="replace"):
+            if line.startswith("{") and '"roofline"' in line:
+                rec = json.loads(line)
+        if rec:
+            ev_us = rec["roofline"]["kernel_us"]
+            tr_us = next(avg for name, _, avg, _, _, _ in stats if DECODE_KERNEL in name) / 1e3
+            lines += ["", f"Cross-check in the same run: bench.py's HIP events give the decode kernel {ev_us:.2f} us "
+                          f"per launch, the kernel trace {tr_us:.2f} us ({100 * (ev_us / tr_us - 1):+.1f}%)."]
     lines += ["", "## HBM traffic per dispatch (memory counters)", "",
               f"Copy calibration: a device copy of {args.copy_mb} MiB reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
               f"WRITE_SIZE = {copy_write:.0f} KiB, so the counters are scaled by {f_fetch:.3f} (fetch) and "
