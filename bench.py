@@ -43,6 +43,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode TFLOP/s & HBM GB/s (% roofline), H=128 d=576/512, B=64 ctx=4k"
+DEFAULT_WORKLOAD_TEXT = ("batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=128, d_qk=576, d_v=512, bf16, "
+                         "64-token pages in a shuffled pool")
+# --workload name -> seeded input recipe (mla_inputs.config_case index, or mtp<s_q>)
+WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8"}
 
 
 def _log(msg):
@@ -121,6 +125,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-mb", type=int, default=0)
+    ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS),
+                    help="batched (default): B=64 x ctx 4096, the measured workload; the others "
+                         "measure the remaining shapes with the same code")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path runs on one MI355X and has no multi-GPU mode "
@@ -131,13 +138,14 @@ def main():
 
     import mla_decode_fwd_amd as mla
     from mla_decode_fwd_amd import accounting as acc
-    from mla_inputs import config_case
+    from mla_inputs import config_case, mtp_case
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mla.load_library()
 
-    case = config_case(2)
+    case = config_case(WORKLOADS[args.workload]) if isinstance(WORKLOADS[args.workload], int) \
+        else mtp_case(int(WORKLOADS[args.workload][3:]))
     B, s_q, H = case.B, case.s_q, case.H
     L = case.seqlens.tolist()
     sets = []
@@ -211,10 +219,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=128, d_qk=576, d_v=512, "
-                               "bf16, 64-token pages in a shuffled pool",
-                   "B": B, "ctx": 4096, "s_q": s_q, "H": H, "splits_per_seq": int(plan.num_splits.max()),
-                   "parallelism": "single GPU"},
+        "config": {"workload": (DEFAULT_WORKLOAD_TEXT if args.workload == "batched" else
+                                f"absorbed-MLA decode, {case.name}, H={H}, d_qk=576, d_v=512, bf16, "
+                                "64-token pages in a shuffled pool"),
+                   "B": B, "ctx": int(max(L)) if args.workload != "batched" else 4096,
+                   "ctx_total": int(sum(L)), "s_q": s_q, "H": H,
+                   "splits_per_seq": int(plan.num_splits.max()), "parallelism": "single GPU"},
         "hbm_gbs": round(step_rf["gbs"], 1),
         "roofline_frac": round(step_rf["frac"], 4),
         "roofline_frac_kv_only": round(acc.kv_bytes(L) / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),

@@ -171,6 +171,16 @@ def config_case(idx: int) -> DecodeCase:
     raise ValueError(f"no decode workload with index {idx}")
 
 
+def mtp_case(s_q: int, B: int = 0, seed: int = 30) -> DecodeCase:
+    """Wider speculative decode: s_q causal new tokens per sequence, H=128,
+    lengths uniform in [1024, 8192] like the two-token workload. B defaults
+    to 256 // s_q sequences (the two-token workload's 256 query rows per
+    head, i.e. B=128 at s_q=2)."""
+    B = B or max(1, 256 // s_q)
+    return make_decode_case(mtp_lengths(B, 1024, 8192, seed + s_q), s_q=s_q, seed=seed + s_q,
+                            name=f"mtp B={B} s_q={s_q} ctx~U[1024,8192]")
+
+
 def tiny_mla_weights(seed: int = 0) -> dict:
     """The tiny full-MLA draws of the handbook chapter's worked example.
 

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import mla_decode_fwd_amd as mla
-from mla_inputs import config_case, make_decode_case, tiny_mla_weights
+from mla_inputs import config_case, make_decode_case, mtp_case, tiny_mla_weights
 from oracle import mla_oracle as orc
 from gpu_helpers import TOL, compare, oracle, run, to_device, to_np
 
@@ -99,6 +99,30 @@ def test_mtp_two_tokens_sampled():
     L = case.seqlens.numpy()
     rng = np.random.default_rng(0)
     sample = sorted(set([int(np.argmax(L)), int(np.argmin(L))] + rng.choice(case.B, 14, replace=False).tolist()))
+    o_ref, l_ref = oracle(case, rows=sample)
+    compare(o[sample], lse[sample], o_ref, l_ref, torch.bfloat16, case.name + f" ({len(sample)} sampled)")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("lens,s_q", [([1000, 300, 2000], 4), ([700, 129], 8), ([64, 65], 8)])
+def test_wider_mtp_small(lens, s_q):
+    # Speculative verify with up to 8 causal new tokens at H=128 (one group of
+    # 128 rows per new token), scaled and unscaled queries.
+    for q_scale in (None, 1.0):
+        kw = {} if q_scale is None else dict(q_scale=q_scale)
+        case = make_decode_case(lens, s_q=s_q, H=128, seed=200 + s_q, **kw)
+        o, lse = run(case, plan="auto", num_cus=32)
+        o_ref, l_ref = oracle(case)
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"mtp {lens} s_q={s_q} q_scale={q_scale}")
+
+
+@pytest.mark.parametrize("s_q", [4, 8])
+def test_wider_mtp_workload_sampled(s_q):
+    case = mtp_case(s_q)
+    o, lse = run(case)
+    L = case.seqlens.numpy()
+    rng = np.random.default_rng(s_q)
+    sample = sorted(set([int(np.argmax(L)), int(np.argmin(L))] + rng.choice(case.B, 6, replace=False).tolist()))
     o_ref, l_ref = oracle(case, rows=sample)
     compare(o[sample], lse[sample], o_ref, l_ref, torch.bfloat16, case.name + f" ({len(sample)} sampled)")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
