@@ -62,6 +62,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kWaves = 4;
@@ -953,32 +954,38 @@ __device__ __forceinline__ void scale_accumulators(float alpha) {
 }
 
 struct WorkItem {
-  int b, k, n;  // sequence, chunk index, chunk count
+  int b, k, n, L;  // sequence, chunk index, chunk count, sequence length
 };
 
-// The sequence of chunk g: the largest b with split_offsets[b] <= g. Each
-// round probes 64 evenly spaced entries at once (one load per lane) and
-// narrows the range 64-fold, so B <= 64 takes one round of loads and
-// B <= 4096 two, instead of a chain of dependent loads.
-__device__ __forceinline__ WorkItem find_work(const int32_t* split_offsets, int B, int g, int lane) {
+// The sequence of chunk g: the largest b with split_offsets[b] <= g. A round
+// probes 64 evenly spaced entries at once (one load per lane) and narrows the
+// range 64-fold until at most 63 sequences remain; the last round loads their
+// offsets and lengths side by side, so that the chunk's offsets and its
+// sequence length come out of registers (readlane) rather than from a chain
+// of dependent loads. B <= 63 takes that one round.
+__device__ __forceinline__ WorkItem find_work(const int32_t* split_offsets, const int32_t* seqlens, int B, int g,
+                                              int lane) {
   WorkItem w;
   if (split_offsets == nullptr) {
-    w.b = g; w.k = 0; w.n = 1;
+    w.b = g; w.k = 0; w.n = 1; w.L = seqlens[g];
     return w;
   }
   int lo = 0, n = B;  // the answer lies in [lo, lo + n)
-  while (n > 64) {
+  while (n > 63) {
     const int step = (n + 63) / 64;
     const bool le = lane * step < n && split_offsets[lo + lane * step] <= g;
     const int c = max(__popcll(__ballot(le)), 1);
     lo += (c - 1) * step;
     n = min(step, n - (c - 1) * step);
   }
-  const bool le = lane < n && split_offsets[lo + lane] <= g;
-  const int b = lo + max(__popcll(__ballot(le)), 1) - 1;
-  w.b = b;
-  w.k = g - split_offsets[b];
-  w.n = split_offsets[b + 1] - split_offsets[b];
+  const int so = lane <= n ? split_offsets[lo + lane] : 0;  // n + 1 <= 64 offsets
+  const int sl = lane < n ? seqlens[lo + lane] : 0;
+  const int j = max(__popcll(__ballot(lane < n && so <= g)), 1) - 1;
+  const int s0 = __builtin_amdgcn_readlane(so, j);
+  w.b = lo + j;
+  w.k = g - s0;
+  w.n = __builtin_amdgcn_readlane(so, j + 1) - s0;
+  w.L = __builtin_amdgcn_readlane(sl, j);
   return w;
 }
 
@@ -986,7 +993,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it in an SGPR
   const int r32 = lane & 31;   // the row this lane owns in MFMA outputs
   const int hi32 = lane >> 5;  // upper half of the wave
 
@@ -1002,15 +1009,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int g = xcd * per_xcd + rest / row_groups;
   if (rest / row_groups >= per_xcd || g >= a.total_splits) return;
 
-  const WorkItem wi = find_work(a.split_offsets, a.B, g, lane);
+  const WorkItem wi = find_work(a.split_offsets, a.seqlens, a.B, g, lane);
   const int b = wi.b;
-  int L = a.seqlens[b];
-  L = max(a.s_q, min(L, a.max_pages * kPage));
+  const int L = max(a.s_q, min(wi.L, a.max_pages * kPage));
   const int P = (L + kPage - 1) / kPage;
-  const int n_chunks = max(wi.n, 1);
+  const int n_chunks = min(max(wi.n, 1), kMaxSplits);
   const int kk = min(max(wi.k, 0), n_chunks - 1);
-  const int pg0 = (int)(((long long)kk * P) / n_chunks);
-  const int pg1 = (int)(((long long)(kk + 1) * P) / n_chunks);
+  // kk * P < 64 * 2^25: exact in 32-bit unsigned arithmetic.
+  const int pg0 = (int)((unsigned)kk * (unsigned)P / (unsigned)n_chunks);
+  const int pg1 = (int)((unsigned)(kk + 1) * (unsigned)P / (unsigned)n_chunks);
 
   // Rows past the end (H*s_q not a multiple of 32) compute on a clamped row
   // and write nothing.
@@ -1026,24 +1033,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int32_t* btab = a.block_table + (size_t)b * a.max_pages;
   const int last_phys = a.num_pages - 1;
 
-  // Block-table entries are read one page ahead of their use, so that no
-  // page waits on a table read.
-  int phys_ahead = 0;
-  if (pg0 < pg1) {
-    const int phys = min(max(btab[pg0], 0), last_phys);
-    issue_page(make_page_load(cache + (size_t)phys * kPageBytes, smem, wave, lane));
-    phys_ahead = btab[min(pg0 + 1, pg1 - 1)];
-  }
+  // The first two block-table entries are requested, then the Q loads are
+  // issued while they travel, then the first page's loads. Later entries are
+  // read one page ahead of their use, so that no page waits on a table read.
+  const int bt0 = btab[max(min(pg0, pg1 - 1), 0)];  // an empty chunk (pg0 == pg1) reads entry 0, unused
+  const int bt1 = btab[max(min(pg0 + 1, pg1 - 1), 0)];
+  asm volatile("" ::: "memory");  // keep the table reads ahead of the Q loads
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Q^T fragments for the whole walk, loaded after the first page's loads
-  // are issued (the block-table chain before them is the longer path):
-  // k-step s holds q[row][16s + 8*hi32 .. +8] (the B layout of
-  // v_mfma_f32_32x32x16_bf16: lane l holds k = 8(l>>5) .. +8 of column l&31).
+  // Q^T fragments for the whole walk: k-step s holds q[row][16s + 8*hi32 .. +8]
+  // (the B layout of v_mfma_f32_32x32x16_bf16: lane l holds k = 8(l>>5) .. +8
+  // of column l&31).
   bf16x8_t qf[kQSteps];
   {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q_lat) + ((size_t)b * rows + row_c) * kDqk + 8 * hi32;
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
+  }
+
+  int phys_ahead = 0;
+  if (pg0 < pg1) {
+    const int phys = min(max(bt0, 0), last_phys);
+    issue_page(make_page_load(cache + (size_t)phys * kPageBytes, smem, wave, lane));
+    phys_ahead = bt1;
   }
 
   f32x16_t acc_o[kColTiles];
@@ -1087,8 +1099,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     // and also guarantees every wave is done with the other buffer.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    // The next page's loads are issued one per two QK k-steps of the first
-    // tile: early enough to land before the page ends, and behind MFMAs. (Built
+    // The next page's 18 loads per wave are issued one per four QK k-steps
+    // over both tiles: in a denser burst the four waves' loads queue up in the
+    // address unit and stall the MFMA stream behind them. (Built
     // unconditionally, from a clamped table index, so that its bases stay
     // wave-uniform SGPRs.)
     const bool has_next = pg + 1 < pg1;
@@ -1172,7 +1185,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     constexpr int kKDepth = 3;
     constexpr int kPvDepth = 4;
 
-    // ---- QK(T0), with the next page's loads.
+    // ---- QK(T0), with half of the next page's loads.
     f32x16_t st0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st0[r] = 0.f;
@@ -1186,7 +1199,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(0, s + kKDepth);
         st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (has_next && (s & 1) == 0) issue_line(next, s >> 1);
+        if (has_next && (s & 3) == 0) issue_line(next, s >> 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1194,7 +1207,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     move_reference((mt0 > m_ref + 8.0f) ? mt0 : m_ref);
     const float neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
 
-    // ---- QK(T1), with tile 0's P (two values every four k-steps).
+    // ---- QK(T1), with tile 0's P (two values every four k-steps) and the
+    // other half of the next page's loads.
     f32x16_t st1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st1[r] = 0.f;
@@ -1210,6 +1224,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(1, s + kKDepth);
         st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st1, 0, 0, 0);
         if ((s & 3) == 0 && s < 32) p_pair(st0, s >> 1, neg0, pf0, psum0);
+        if (has_next && (s & 3) == 2) issue_line(next, 9 + (s >> 2));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1265,36 +1280,49 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const bool any = l_tot > 0.f;
   const float inv = any ? 1.f / l_tot : 0.f;
   const float lse_v = any ? (m_ref + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  if (row >= rows) return;
 
-  // acc_o[i][r] is O^T[32i + 8(r>>2) + 4*hi32 + (r&3)][row]: runs of four
-  // consecutive columns.
-  if (n_chunks == 1 && a.o_lat != nullptr) {
-    __bf16* orow = reinterpret_cast<__bf16*>(a.o_lat) + ((size_t)b * rows + row) * kDv + 4 * hi32;
+  // The rows go out through LDS. acc_o[i][r] is O^T[32i + 8(r>>2) + 4*hi32 +
+  // (r&3)][row], so a lane holds 8-byte pieces of its row and a direct store
+  // would touch 32 rows per instruction, 16 bytes each: partial 128-byte lines
+  // that stay dirty in L2 until the end of the kernel and then cost
+  // microseconds to write back. Staged, every store instruction writes one
+  // whole 1 KB row, non-temporal: nothing reads it again in this kernel. Row r of a wave's 32 KB staging area keeps its 64 16-byte
+  // pieces XOR-permuted by r so that the 32 rows of a write do not fall on the
+  // same LDS banks.
+  __syncthreads();  // every wave is done with the page buffers
+  // The lane position is taken afresh (mbcnt) rather than kept live through
+  // the page loop, where every VGPR is taken.
+  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int r32f = ln & 31, hi32f = ln >> 5;
+  const int rowf = rgrp * kRowsPerGroup + wave * kWaveRows + r32f;
+  char* stage = smem + wave * (kWaveRows * kDv * 2);
 #pragma unroll
-    for (int i = 0; i < kColTiles; ++i)
+  for (int i = 0; i < kColTiles; ++i)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4_t v;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4_t v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc_o[i][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4_t*>(orow + 32 * i + 8 * q4) = v;
-      }
-    if (hi32 == 0) a.lse[(size_t)b * rows + row] = lse_v;
-  } else {
-    // Chunk partials in bf16 like the output (the LSE stays fp32): half the
-    // bytes every workgroup writes at its end and the combine reads back.
-    __bf16* orow = static_cast<__bf16*>(a.o_part) + ((size_t)g * rows + row) * kDv + 4 * hi32;
-#pragma unroll
-    for (int i = 0; i < kColTiles; ++i)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc_o[i][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4_t*>(orow + 32 * i + 8 * q4) = v;
-      }
-    if (hi32 == 0) a.lse_part[(size_t)g * rows + row] = lse_v;
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc_o[i][4 * q4 + e] * inv);
+      const int piece = (4 * i + q4) ^ r32f;  // 16-byte piece of the row, permuted
+      *reinterpret_cast<bf16x4_t*>(stage + r32f * (kDv * 2) + piece * 16 + 8 * hi32f) = v;
+    }
+  __syncthreads();
+
+  const bool direct = n_chunks == 1 && a.o_lat != nullptr;
+  __bf16* const out = direct ? static_cast<__bf16*>(a.o_lat) + (size_t)b * rows * kDv
+                             : static_cast<__bf16*>(a.o_part) + (size_t)g * rows * kDv;
+  const int row0 = rgrp * kRowsPerGroup + wave * kWaveRows;
+#pragma unroll 4
+  for (int r = 0; r < kWaveRows; ++r) {
+    if (row0 + r >= rows) break;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * (kDv * 2) + ((ln ^ r) * 16));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln));
+  }
+  if (hi32f == 0 && rowf < rows) {
+    if (direct)
+      a.lse[(size_t)b * rows + rowf] = lse_v;
+    else
+      a.lse_part[(size_t)g * rows + rowf] = lse_v;
   }
 }
 

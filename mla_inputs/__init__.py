@@ -181,6 +181,25 @@ def mtp_case(s_q: int, B: int = 0, seed: int = 30) -> DecodeCase:
                             name=f"mtp B={B} s_q={s_q} ctx~U[1024,8192]")
 
 
+def ramp_case(seqlens: Sequence[int], s_q: int = 1, growth: float = 0.5, seed: int = 50,
+              H: int = 128) -> DecodeCase:
+    """Scores that keep growing along the sequence: unscaled queries, and the
+    rows of logical page p multiplied by (1 + growth * p) (re-rounded to
+    bf16). The running row max then rises by several units (base 2) every few
+    pages, so a decoder that keeps a running reference must move it and
+    rescale its accumulators many times per sequence. Unowned slots stay NaN."""
+    case = make_decode_case(seqlens, s_q=s_q, H=H, seed=seed, q_scale=1.0,
+                            name=f"ramp {list(seqlens)} s_q={s_q} growth={growth}")
+    cache = case.cache.float()
+    table = case.block_table.numpy()
+    for b, L in enumerate(case.seqlens.tolist()):
+        for p in range((L + PAGE - 1) // PAGE):
+            cache[int(table[b, p])] *= 1.0 + growth * p
+    case.cache = cache.to(case.cache.dtype)
+    case.meta["growth"] = growth
+    return case
+
+
 def tiny_mla_weights(seed: int = 0) -> dict:
     """The tiny full-MLA draws of the handbook chapter's worked example.
 

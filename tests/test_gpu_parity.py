@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import mla_decode_fwd_amd as mla
-from mla_inputs import config_case, make_decode_case, mtp_case, tiny_mla_weights
+from mla_inputs import config_case, make_decode_case, mtp_case, ramp_case, tiny_mla_weights
 from oracle import mla_oracle as orc
 from gpu_helpers import TOL, compare, oracle, run, to_device, to_np
 
@@ -57,6 +57,28 @@ def test_small_bf16_sharp_softmax(lens, s_q, H):
     o, lse = run(case, plan="auto", num_cus=8)
     o_ref, l_ref = oracle(case)
     compare(o, lse, o_ref, l_ref, torch.bfloat16, f"sharp {lens}")
+
+
+@pytest.mark.parametrize("lens,s_q,plan", [([4096, 1500, 700], 1, "auto"), ([4096, 1500, 700], 1, None),
+                                           ([2000, 900, 65], 2, "auto")])
+def test_running_max_rescale(lens, s_q, plan):
+    # Scores that grow page after page (row max up by ~3 in base 2 per page),
+    # so every row moves its softmax reference and rescales O and l dozens of
+    # times inside one chunk (few compute units => long chunks). Outputs and
+    # LSEs are large here (rows scaled up to ~33x), so the absolute bounds are
+    # taken relative to the output's scale: max-abs 2e-2 * max|o_ref| and LSE
+    # 1e-5 relative (fp32 accumulation of 576 products of that size); rel-L2
+    # keeps the usual 5e-3.
+    case = ramp_case(lens, s_q=s_q, growth=0.5)
+    o, lse = run(case, plan=plan, num_cus=8)
+    o_ref, l_ref = oracle(case)
+    og, lg = to_np(o), to_np(lse)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    rel = np.linalg.norm(og - o_ref) / np.linalg.norm(o_ref)
+    mabs = np.max(np.abs(og - o_ref)) / np.max(np.abs(o_ref))
+    lrel = np.max(np.abs(lg - l_ref) / np.maximum(np.abs(l_ref), 1.0))
+    print(f"[parity] {case.name} plan={plan} rel_l2={rel:.3e} max_abs/scale={mabs:.3e} lse_rel={lrel:.3e}")
+    assert rel <= 5e-3 and mabs <= 2e-2 and lrel <= 1e-5, (rel, mabs, lrel)
 
 
 def test_small_fp32():
