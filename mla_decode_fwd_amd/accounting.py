@@ -10,7 +10,8 @@ Sources:
              count, the decode arithmetic intensity).
   [AI-MTP]   "为什么 MLA + MTP 容易吃亏？从 Arithmetic Intensity 看 Attention",
              Appendix A (F = 2HL(2d_c+d_s), B = bL(d_c+d_s), hence
-             AI = H(2d_c+d_s)/(d_c+d_s) for bf16).
+             AI = H(2d_c+d_s)/(d_c+d_s) for bf16) and section 6 (sparse
+             attention: the cost follows the top-k list, not L).
 """
 from __future__ import annotations
 
@@ -88,6 +89,32 @@ def decode_bytes(seqlens: Iterable[int], s_q: int, H: int, elem_bytes: int = 2,
     lse = B * s_q * H * 4
     table = sum(((L + page - 1) // page) * 4 for L in seqlens)
     return float(kv + q + o + lse + table)
+
+
+def sparse_valid_counts(indices, seqlens):
+    """Selected entries per (sequence, query token): positions in [0, L_b)."""
+    import numpy as np
+    idx = np.asarray(indices)
+    L = np.asarray(seqlens, dtype=np.int64).reshape(-1, 1, 1)
+    return ((idx >= 0) & (idx < L)).sum(axis=-1)
+
+
+def sparse_decode_flops(valid_counts, H: int, d_qk: int = 576, d_v: int = 512) -> float:
+    """Algorithmic FLOPs of a top-k decode: 2 H (d_qk + d_v) per selected (row, token)."""
+    import numpy as np
+    return float(2.0 * H * (d_qk + d_v) * np.asarray(valid_counts, dtype=np.float64).sum())
+
+
+def sparse_decode_bytes(valid_counts, B: int, s_q: int, H: int, topk: int, elem_bytes: int = 2,
+                        d_qk: int = 576, d_v: int = 512) -> float:
+    """Algorithmic HBM bytes of a top-k decode: each selected cache row once per
+    query token that selects it (counted per list entry), the index lists, the
+    block-table entries they map through (one per entry), q, o and the LSE."""
+    import numpy as np
+    n = float(np.asarray(valid_counts, dtype=np.float64).sum())
+    rows = n * d_qk * elem_bytes
+    lists = B * s_q * topk * 4 + n * 4
+    return rows + lists + B * s_q * H * (d_qk * elem_bytes + d_v * elem_bytes + 4)
 
 
 def kv_bytes(seqlens: Iterable[int], elem_bytes: int = 2, d_qk: int = 576) -> float:

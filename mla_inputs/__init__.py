@@ -200,6 +200,41 @@ def ramp_case(seqlens: Sequence[int], s_q: int = 1, growth: float = 0.5, seed: i
     return case
 
 
+def topk_indices(seqlens: Sequence[int], s_q: int, topk: int, seed: int, causal: bool = True,
+                 repeat_frac: float = 0.0) -> torch.Tensor:
+    """Selected-token lists [B, s_q, topk] int32, as a top-k selector would
+    return them: for query token i of sequence b, min(topk, n) distinct
+    positions drawn uniformly without replacement from the n positions it may
+    see (n = L_b - s_q + i + 1 when causal, else L_b), in random order, the
+    rest of the row padded with -1. ``repeat_frac`` replaces that fraction of
+    each row's picks by copies of other picks (duplicate entries)."""
+    rng = np.random.default_rng(seed)
+    B = len(seqlens)
+    out = np.full((B, s_q, topk), -1, dtype=np.int32)
+    for b, L in enumerate(seqlens):
+        for i in range(s_q):
+            n = L - s_q + i + 1 if causal else L
+            k = min(topk, n)
+            pick = rng.choice(n, size=k, replace=False)
+            r = int(round(repeat_frac * k))
+            if r and k > 1:
+                pick[:r] = pick[rng.integers(r, k, size=r)] if k > r else pick[:r]
+            rng.shuffle(pick)
+            out[b, i, :k] = pick
+    return torch.from_numpy(out)
+
+
+def sparse_case(seqlens: Sequence[int], s_q: int = 1, topk: int = 2048, seed: int = 60, H: int = 128,
+                q_scale: float = 1.0 / math.sqrt(D_QK), repeat_frac: float = 0.0):
+    """A paged decode problem plus its selected-token lists (seed + 7 for the lists)."""
+    case = make_decode_case(seqlens, s_q=s_q, H=H, seed=seed, q_scale=q_scale,
+                            name=f"sparse B={len(seqlens)} s_q={s_q} topk={topk}")
+    case.meta["indices"] = topk_indices(seqlens, s_q, topk, seed + 7, causal=case.causal or s_q == 1,
+                                        repeat_frac=repeat_frac)
+    case.meta["topk"] = topk
+    return case
+
+
 def tiny_mla_weights(seed: int = 0) -> dict:
     """The tiny full-MLA draws of the handbook chapter's worked example.
 

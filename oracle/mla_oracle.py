@@ -15,6 +15,7 @@ Sources. Each citation names the page by its title and the section:
   [MLA-推理]  "MLA 推理：两条计算路径与 FlashMLA" (AI infra handbook, serving/moe/mla)
   [DSV2-MLA]  "DeepSeekV2之MLA" (blog post with the DeepSeek-V2 equations and SGLang code)
   [AI-MTP]    "为什么 MLA + MTP 容易吃亏？从 Arithmetic Intensity 看 Attention"
+              (section 6 "Sparse attention 把方向反过来" for decode_sparse)
 
 Function list and pins:
   rope_adjacent      RoPE on adjacent pairs                 pinned (rotation identities)
@@ -26,6 +27,8 @@ Function list and pins:
   decode_absorbed    absorbed decode on a paged cache       pinned (brute force, SDPA, closed forms)
   decode_partials    the same over a token chunk            pinned (merge invariant)
   lse_merge          log-sum-exp merge of chunk results     pinned (merge == unsplit)
+  decode_sparse      absorbed decode over top-k token lists pinned (full list == dense, brute
+                                                            force, closed forms)
 No function is left without a pin.
 """
 from __future__ import annotations
@@ -46,6 +49,7 @@ __all__ = [
     "decode_absorbed",
     "decode_partials",
     "lse_merge",
+    "decode_sparse",
 ]
 
 
@@ -304,4 +308,44 @@ def lse_merge(o_parts, lse_parts):
     with np.errstate(divide="ignore"):
         lse = Mf + np.log(S)
     o = np.einsum("k...,k...d->...d", w / np.where(S > 0, S, 1.0), o_parts)
+    return o, lse
+
+
+def decode_sparse(q_lat, cache, block_table, seqlens, indices, scale: float, dv: int = 512):
+    """Absorbed decode over a selected token list per query token.
+
+    [AI-MTP] §6 "Sparse attention 把方向反过来": a light selector scores the
+    history and keeps the top-k tokens (index_topk = 2048 in DeepSeek-V3.2);
+    the latents at the selected indices are gathered and the scores and the
+    weighted sum are taken over those tokens only, so the cost follows k, not L.
+
+    indices [B,s_q,k] int: logical token positions in sequence b's cache
+    (mapped through block_table like every other token). Entries outside
+    [0, L_b) are padding and are skipped; the rest are used in list order, a
+    repeated position counting once per occurrence (the definition is a sum
+    over the list). No causal mask is applied: the list is the key set. A
+    row whose list holds no valid entry gives o = 0 and lse = -inf.
+    Other arguments and the per-row arithmetic are those of decode_absorbed.
+    Returns o_lat [B,s_q,H,dv] and lse [B,s_q,H], float64.
+    """
+    q_lat = _f64(q_lat)
+    B, s_q, H, _ = q_lat.shape
+    indices = np.asarray(indices)
+    o = np.zeros((B, s_q, H, dv))
+    lse = np.full((B, s_q, H), -np.inf)
+    for b in range(B):
+        L = int(seqlens[b])
+        K_all = gather_tokens(cache, block_table[b], L)
+        for i in range(s_q):
+            sel = indices[b, i]
+            sel = sel[(sel >= 0) & (sel < L)]
+            if sel.size == 0:
+                continue
+            K = K_all[sel]
+            s = (q_lat[b, i] @ K.T) * scale  # [H, n]
+            M = s.max(axis=1, keepdims=True)
+            e = np.exp(s - M)
+            Z = e.sum(axis=1, keepdims=True)
+            o[b, i] = (e / Z) @ K[:, :dv]
+            lse[b, i] = (M + np.log(Z))[:, 0]
     return o, lse

@@ -57,3 +57,33 @@ def test_decode_metric_accounting():
     assert r["bound"] == "hbm" and math.isclose(r["frac"], b / 40e-6 / 8e12)
     r2 = acc.roofline(1e15, 1e12, 1.0)
     assert r2["bound"] == "mfma" and math.isclose(r2["frac"], 0.4)
+
+
+def test_sparse_decode_table():
+    # [AI-MTP] section 6: absorbed attention over the 2048 selected tokens
+    # costs the same 0.57 GFLOP at every L; the dense expanded path grows with
+    # L. The table prints 3 significant digits (one unit of the last digit is
+    # the bound here; 275.5 is printed as 275) and integer ratios that were
+    # taken from slightly different unrounded values (ours agree within 0.1%).
+    g = load_golden("sparse_decode_flops.txt")
+    k = int(g["index_topk"])
+    sparse = acc.sparse_decode_flops([[k]], 128)
+    assert round(sparse / 1e9, 2) == g["sparse_absorbed_GFLOP"]
+    for L, key, unit, last in [(2048, "dense_expanded_L2048_GFLOP", 1e9, 0.1),
+                               (8192, "dense_expanded_L8192_GFLOP", 1e9, 1.0),
+                               (32768, "dense_expanded_L32768_TFLOP", 1e12, 0.01),
+                               (131072, "dense_expanded_L131072_TFLOP", 1e12, 0.01)]:
+        dense, _ = acc.path_flops(1, L)
+        assert abs(dense / unit - g[key]) <= last, (L, dense)
+        r = g[f"ratio_L{L}"]
+        assert abs(dense / sparse - r) <= max(0.5, 1e-3 * r), (L, dense / sparse)
+
+
+def test_sparse_counts_and_bytes():
+    import numpy as np
+    idx = np.array([[[0, 5, -1, 9]], [[3, 3, 7, 100]]])  # B=2, s_q=1, k=4
+    counts = acc.sparse_valid_counts(idx, [8, 50])
+    assert counts.tolist() == [[2], [3]]  # 9 >= 8 and 100 >= 50 are padding; 3 counts twice
+    assert acc.sparse_decode_flops(counts, 128) == 5 * 2 * 128 * (576 + 512)
+    b = acc.sparse_decode_bytes(counts, 2, 1, 128, 4)
+    assert b == 5 * 1152 + 2 * 4 * 4 + 5 * 4 + 2 * 128 * (1152 + 1024 + 4)

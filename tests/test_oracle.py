@@ -375,3 +375,87 @@ def test_mutation_unnormalised_merge_is_caught():
     case = make_decode_case([500, 130], s_q=1, H=4, seed=31, dtype=torch.bfloat16, q_scale=1.0)
     err = check_split_merge(orc.decode_absorbed, orc.decode_partials, merge_wrong, case, 0)
     assert err > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Sparse (top-k) decode: [AI-MTP] section 6.
+# ---------------------------------------------------------------------------
+
+def brute_sparse(q_lat, cache, table, seqlens, indices, scale, dv):
+    """Python-float loops over each row's list, skipping entries outside [0, L)."""
+    B, s_q, H, D = q_lat.shape
+    page = cache.shape[1]
+    o = np.zeros((B, s_q, H, dv))
+    lse = np.full((B, s_q, H), -math.inf)
+    for b in range(B):
+        L = int(seqlens[b])
+        for i in range(s_q):
+            sel = [int(j) for j in indices[b, i] if 0 <= int(j) < L]
+            if not sel:
+                continue
+            rows = [cache[int(table[b][j // page])][j % page] for j in sel]
+            for h in range(H):
+                scores = [scale * sum(float(q_lat[b, i, h, k]) * float(r[k]) for k in range(D)) for r in rows]
+                mx = max(scores)
+                w = [math.exp(s - mx) for s in scores]
+                Z = sum(w)
+                for c in range(dv):
+                    o[b, i, h, c] = sum(w[t] * float(rows[t][c]) for t in range(len(rows))) / Z
+                lse[b, i, h] = mx + math.log(Z)
+    return o, lse
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_sparse_full_list_equals_dense(s_q):
+    # Listing every visible position (any order, -1 padding) gives the dense decode.
+    from mla_inputs import topk_indices
+    lens = [300, 64, 129, 7 + s_q]
+    case = make_decode_case(lens, s_q=s_q, H=16, seed=40 + s_q, dtype=torch.bfloat16, q_scale=1.0)
+    q, cache, table, L = _case_arrays(case)
+    idx = topk_indices(lens, s_q, 320, seed=3, causal=True).numpy()
+    o, lse = orc.decode_sparse(q, cache, table, L, idx, case.scale, dv=512)
+    od, ld = orc.decode_absorbed(q, cache, table, L, case.scale, s_q > 1, dv=512)
+    assert np.max(np.abs(o - od)) <= 1e-12 and np.max(np.abs(lse - ld)) <= 1e-12
+
+
+def test_sparse_matches_brute_force():
+    from mla_inputs import topk_indices
+    lens = [40, 70, 3]
+    case = _tiny_case(31, 2, lens)
+    q, cache, table, L = _case_arrays(case)
+    idx = topk_indices(lens, 2, 9, seed=5, causal=True, repeat_frac=0.2).numpy()
+    idx[0, 1, 2] = 500   # out of range: padding
+    idx[2, 0, :] = -1    # a row with nothing selected
+    o, lse = orc.decode_sparse(q, cache, table, L, idx, case.scale, dv=12)
+    ob, lb = brute_sparse(q, cache, table, L, idx, case.scale, 12)
+    assert np.max(np.abs(o - ob)) <= 1e-12
+    fin = np.isfinite(lb)
+    assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - lb[fin])) <= 1e-12
+    assert np.all(o[2, 0] == 0) and np.all(lse[2, 0] == -np.inf)
+
+
+def test_sparse_duplicate_and_order():
+    # A position listed twice: o = its value, lse = its score + ln 2. The list
+    # order never matters.
+    case = make_decode_case([100], s_q=1, H=4, seed=32, dtype=torch.float32, q_scale=1.0)
+    q, cache, table, L = _case_arrays(case)
+    idx = np.array([[[37, 37, -1, -1]]])
+    o, lse = orc.decode_sparse(q, cache, table, L, idx, case.scale, dv=512)
+    row = cache[table[0, 0], 37]
+    assert np.allclose(o[0, 0], row[None, :512], atol=1e-13)
+    assert np.allclose(lse[0, 0], case.scale * (q[0, 0] @ row) + math.log(2), atol=1e-12)
+    idx2 = np.array([[[5, 80, 37, 12, 99]]])
+    a = orc.decode_sparse(q, cache, table, L, idx2, case.scale, dv=512)
+    b = orc.decode_sparse(q, cache, table, L, idx2[..., ::-1].copy(), case.scale, dv=512)
+    assert np.max(np.abs(a[0] - b[0])) <= 1e-13 and np.max(np.abs(a[1] - b[1])) <= 1e-13
+
+
+def test_mutation_sparse_padding_as_token_zero_is_caught(monkeypatch):
+    # Treating the -1 padding as position 0 must fail a pin.
+    real = orc.decode_sparse
+
+    def pad_as_zero(q, cache, table, L, idx, scale, dv=512):
+        return real(q, cache, table, L, np.where(np.asarray(idx) < 0, 0, idx), scale, dv)
+    monkeypatch.setattr(orc, "decode_sparse", pad_as_zero)
+    with pytest.raises(AssertionError):
+        test_sparse_matches_brute_force()
