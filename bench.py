@@ -45,8 +45,10 @@ if ROOT not in sys.path:
 METRIC = "MLA decode TFLOP/s & HBM GB/s (% roofline), H=128 d=576/512, B=64 ctx=4k"
 DEFAULT_WORKLOAD_TEXT = ("batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=128, d_qk=576, d_v=512, bf16, "
                          "64-token pages in a shuffled pool")
-# --workload name -> seeded input recipe (mla_inputs.config_case index, or mtp<s_q>)
-WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8"}
+# --workload name -> seeded input recipe (mla_inputs.config_case index, mtp<s_q>, or the
+# top-k shape: B=64 histories of 16384 tokens, 2048 selected per new token)
+WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8", "topk": "topk"}
+TOPK_SHAPE = dict(B=64, L=16384, topk=2048)
 
 
 def _log(msg):
@@ -89,22 +91,36 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     L = case.seqlens.numpy()
 
     # Hand the oracle only the pages of each sequence (fp64 copies made
-    # outside the timed region).
-    subs = []
-    for b in range(case.B):
+    # outside the timed region, kept while they total under 2 GB).
+    cached = {}
+    keep = sum(int(x) for x in L) * case.cache.shape[-1] * 8 < (2 << 30)
+
+    def sub(b):
+        if b in cached:
+            return cached[b]
         npg = (int(L[b]) + 63) // 64
-        subs.append((case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None]))
+        v = (case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None])
+        if keep:
+            cached[b] = v
+        return v
+    idx = case.meta["indices"].numpy() if "indices" in case.meta else None
     done = []
     secs = 0.0
     while secs < budget_s:
         b = len(done) % case.B
-        c, t = subs[b]
+        c, t = sub(b)
         t0 = time.perf_counter()
-        orc.decode_absorbed(q[b:b + 1], c, t, L[b:b + 1], case.scale, case.causal, dv=512)
+        if idx is None:
+            orc.decode_absorbed(q[b:b + 1], c, t, L[b:b + 1], case.scale, case.causal, dv=512)
+        else:
+            orc.decode_sparse(q[b:b + 1], c, t, L[b:b + 1], idx[b:b + 1], case.scale, dv=512)
         secs += time.perf_counter() - t0
         done.append(b)
     n = len(done)
-    flops = acc.decode_flops(L[done], case.s_q, case.H)
+    if idx is None:
+        flops = acc.decode_flops(L[done], case.s_q, case.H)
+    else:
+        flops = acc.sparse_decode_flops(acc.sparse_valid_counts(idx, L)[done], case.H)
     try:
         from threadpoolctl import threadpool_info
 
@@ -112,8 +128,8 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     except Exception:  # threadpoolctl missing: count the cores we may run on
         cores = len(os.sched_getaffinity(0))
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} sequence decodes ({n / case.B:.2f} passes over the B={case.B} batch, ctx {int(L[0])}, "
-                      f"H={case.H}), fp64 numpy, {secs:.1f} s",
+            "sample": f"{n} sequence {'top-k ' if idx is not None else ''}decodes ({n / case.B:.2f} passes over "
+                      f"the B={case.B} batch, ctx {int(L[0])}, H={case.H}), fp64 numpy, {secs:.1f} s",
             "seconds": secs}
 
 
@@ -138,14 +154,20 @@ def main():
 
     import mla_decode_fwd_amd as mla
     from mla_decode_fwd_amd import accounting as acc
-    from mla_inputs import config_case, mtp_case
+    from mla_inputs import config_case, mtp_case, sparse_case
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mla.load_library()
 
-    case = config_case(WORKLOADS[args.workload]) if isinstance(WORKLOADS[args.workload], int) \
-        else mtp_case(int(WORKLOADS[args.workload][3:]))
+    wl = WORKLOADS[args.workload]
+    topk_mode = wl == "topk"
+    if topk_mode:
+        case = sparse_case([TOPK_SHAPE["L"]] * TOPK_SHAPE["B"], s_q=1, topk=TOPK_SHAPE["topk"], seed=90)
+    elif isinstance(wl, int):
+        case = config_case(wl)
+    else:
+        case = mtp_case(int(wl[3:]))
     B, s_q, H = case.B, case.s_q, case.H
     L = case.seqlens.tolist()
     sets = []
@@ -156,7 +178,7 @@ def main():
         bt = case.block_table if k == 0 else ((case.block_table.long() + 1) % npages).to(torch.int32)
         sets.append(dict(q=case.q_lat.to(dev), kv=cache.to(dev), bt=bt.to(dev), sl=case.seqlens.to(dev)))
     t0 = time.perf_counter()
-    plan = mla.decode_plan(L, s_q, H)
+    plan = mla.sparse_decode_plan(B, case.meta["topk"], s_q, H) if topk_mode else mla.decode_plan(L, s_q, H)
     plan_us = (time.perf_counter() - t0) * 1e6
     offs = plan.device_offsets(dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
@@ -167,9 +189,15 @@ def main():
 
     # Both launches are prepared once (checks and argument marshalling done
     # up front) so that the host enqueues a step faster than the GPU runs it.
-    dec_calls = [mla.prepare_decode(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal, split_offsets=offs,
-                                    total_splits=plan.total_splits, workspace=ws, partials_only=True)[0]
-                 for s in sets]
+    if topk_mode:
+        idx_dev = case.meta["indices"].to(dev)
+        dec_calls = [mla.prepare_sparse_decode(s["q"], s["kv"], s["bt"], s["sl"], idx_dev, case.scale,
+                                               split_offsets=offs, total_splits=plan.total_splits, workspace=ws,
+                                               partials_only=True)[0] for s in sets]
+    else:
+        dec_calls = [mla.prepare_decode(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal,
+                                        split_offsets=offs, total_splits=plan.total_splits, workspace=ws,
+                                        partials_only=True)[0] for s in sets]
     comb_call = mla.prepare_combine(o_part, lse_part, offs, plan.total_splits, B, torch.bfloat16, o, lse)
 
     def step(i):
@@ -202,8 +230,15 @@ def main():
         torch.cuda.synchronize()
         _log(f"copy calibration: 3 device copies of {n} bytes")
 
-    flops = acc.decode_flops(L, s_q, H)
-    nbytes = acc.decode_bytes(L, s_q, H)
+    if topk_mode:
+        counts = acc.sparse_valid_counts(case.meta["indices"].numpy(), L)
+        flops = acc.sparse_decode_flops(counts, H)
+        nbytes = acc.sparse_decode_bytes(counts, B, s_q, H, case.meta["topk"])
+        kv_only = float(counts.sum()) * 1152
+    else:
+        flops = acc.decode_flops(L, s_q, H)
+        nbytes = acc.decode_bytes(L, s_q, H)
+        kv_only = acc.kv_bytes(L)
     step_rf = acc.roofline(flops, nbytes, ms_per_step / 1e3)
     dec_rf = acc.roofline(flops, nbytes, decode_ms / 1e3)
     out = {
@@ -220,6 +255,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (DEFAULT_WORKLOAD_TEXT if args.workload == "batched" else
+                                (f"top-k absorbed-MLA decode, B={B} histories of {TOPK_SHAPE['L']} tokens, "
+                                 f"{TOPK_SHAPE['topk']} selected per new token (uniform, distinct), s_q=1, "
+                                 f"H={H}, d_qk=576, d_v=512, bf16, 64-token pages in a shuffled pool")
+                                if topk_mode else
                                 f"absorbed-MLA decode, {case.name}, H={H}, d_qk=576, d_v=512, bf16, "
                                 "64-token pages in a shuffled pool"),
                    "B": B, "ctx": int(max(L)) if args.workload != "batched" else 4096,
@@ -227,10 +266,11 @@ def main():
                    "splits_per_seq": int(plan.num_splits.max()), "parallelism": "single GPU"},
         "hbm_gbs": round(step_rf["gbs"], 1),
         "roofline_frac": round(step_rf["frac"], 4),
-        "roofline_frac_kv_only": round(acc.kv_bytes(L) / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),
+        "roofline_frac_kv_only": round(kv_only / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),
         "roofline": {"bound": dec_rf["bound"], "achieved": round(dec_rf["achieved"], 1),
                      "peak": dec_rf["peak"], "unit": dec_rf["unit"], "frac": round(dec_rf["frac"], 4),
-                     "traffic": measured_traffic(), "kernel": "mla_decode_bf16_kernel",
+                     "traffic": measured_traffic() if args.workload == "batched" else None,
+                     "kernel": "mla_decode_bf16_kernel<true>" if topk_mode else "mla_decode_bf16_kernel",
                      "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},

@@ -23,6 +23,8 @@
  *   [DSV2-MLA]  "DeepSeekV2之MLA", section 4.5 (forward_absorb: bmm of q_nope with
  *               w_kc, attention as an MQA with a 576-wide key and 512-wide value,
  *               bmm of the attention output with w_vc).
+ *   [AI-MTP]    "为什么 MLA + MTP 容易吃亏？从 Arithmetic Intensity 看 Attention",
+ *               section 6: top-k sparse attention over gathered latents.
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the name ends in _host. All tensors
@@ -71,7 +73,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 1. */
+/* Library ABI version, currently 2 (2 added mla_sparse_decode_fwd). */
 int mla_abi_version(void);
 
 /*
@@ -160,6 +162,39 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
                             int page_size, int max_pages_per_seq, int num_pages,
                             float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
                             size_t workspace_bytes, void* o_lat, float* lse, void* stream);
+
+/*
+ * Top-k (sparse) absorbed-MLA decode ([AI-MTP] section 6 "Sparse attention
+ * 把方向反过来": a selector keeps index_topk = 2048 history tokens per new
+ * token; their latents are gathered by index and the scores and the weighted
+ * sum run over those tokens only, so the cost follows topk, not L).
+ * For sequence b, query token i and head h, with S = the entries e of
+ * indices[b, i, 0:topk] that satisfy 0 <= e < L_b (the others are padding),
+ * taken in list order (a repeated entry counts once per occurrence):
+ *   K_e = kv_cache[block_table[b, e/64], e%64, 0:576],  V_e = K_e[0:512]
+ *   s_e = softmax_scale * sum_k q_lat[b,i,h,k] * K_e[k]          for e in S
+ *   o_lat[b,i,h,:] = sum_e softmax(s)_e * V_e,  lse[b,i,h] = ln sum_e exp(s_e)
+ * No causal mask: the list is the key set. A row with S empty gets o = 0 and
+ * lse = -inf.
+ *
+ *   indices          [B, s_q, topk] int32 (device), logical token positions.
+ *   topk             1..2048.
+ *   H                must be 128 (one workgroup row group per new token);
+ *                    dtype must be MLA_BF16 (else MLA_ERR_UNSUPPORTED).
+ *   seqlens          [B] int32 L_b (device), each in [1, 64*max_pages_per_seq];
+ *                    the rows of positions 0..L_b-1 must hold finite values
+ *                    (padding entries are loaded from position 0, then masked).
+ *   split_offsets    as for mla_decode_fwd, but chunks cut the list: plan with
+ *                    mla_decode_plan(seqlens_host = topk for every sequence).
+ *   Every other argument, the workspace layout, the partials-only mode and
+ *   the error behaviour are those of mla_decode_fwd (causal does not apply).
+ */
+mla_status_t mla_sparse_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,
+                                   const int32_t* seqlens, const int32_t* indices, int topk,
+                                   const int32_t* split_offsets, int total_splits, int B, int s_q, int H,
+                                   int d_qk, int d_v, int page_size, int max_pages_per_seq, int num_pages,
+                                   float softmax_scale, mla_dtype_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* o_lat, float* lse, void* stream);
 
 /*
  * LSE merge of split-KV partial results ([MLA-推理] sections

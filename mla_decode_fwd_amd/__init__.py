@@ -70,6 +70,7 @@ def load_library():
         "mla_decode_workspace_size": ([I, I, I], Z),
         "mla_decode_plan": ([P, I, I, I, I, I, P, P, P], I),
         "mla_decode_fwd": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, Z, P, P, P], I),
+        "mla_sparse_decode_fwd": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P, Z, P, P, P], I),
         "mla_splitkv_combine": ([P, P, P, I, I, I, I, I, I, P, P, P], I),
         "mla_absorb_q": ([P, P, P, I, I, I, I, I, I, P, P], I),
         "mla_out_uv": ([P, P, I, I, I, I, I, P, P], I),
@@ -213,6 +214,45 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
         return PreparedCall("mla_decode_fwd", args), (o_lat, lse)
     _check("mla_decode_fwd", load_library().mla_decode_fwd(*args))
     return o_lat, lse
+
+
+def sparse_decode_plan(B: int, topk: int, s_q: int = 1, H: int = 128, num_cus: int = 256,
+                       max_splits: int = MAX_SPLITS) -> DecodePlan:
+    """Split plan for ``mla_sparse_decode_fwd``: the chunks cut each query
+    token's list of ``topk`` entries, so every sequence plans as length topk."""
+    return decode_plan([int(topk)] * int(B), s_q, H, num_cus=num_cus, max_splits=max_splits)
+
+
+def mla_sparse_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                          seqlens: torch.Tensor, indices: torch.Tensor, softmax_scale: float,
+                          split_offsets: Optional[torch.Tensor] = None, total_splits: Optional[int] = None,
+                          workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, partials_only: bool = False,
+                          _prepare: bool = False):
+    """Top-k decode (mla_sparse_decode_fwd): attention of each (token, head)
+    row over the positions listed in ``indices`` [B, s_q, topk] int32 (entries
+    outside [0, L_b) are padding). bf16, H = 128. Arguments and results as
+    ``mla_decode_fwd``; plan with ``sparse_decode_plan``."""
+    if q_lat.dim() != 4 or indices.dim() != 3:
+        raise ValueError("expected q_lat [B,s_q,H,576] and indices [B,s_q,topk]")
+    B, s_q = q_lat.shape[:2]
+    if tuple(indices.shape[:2]) != (B, s_q):
+        raise ValueError("indices must be [B, s_q, topk]")
+    _need(indices, "indices", dtype=torch.int32, device=q_lat.device)
+    call, outs = mla_decode_fwd(q_lat, kv_cache, block_table, seqlens, softmax_scale, False,
+                                split_offsets=split_offsets, total_splits=total_splits, workspace=workspace,
+                                o_lat=o_lat, lse=lse, partials_only=partials_only, _prepare=True)
+    a = call.args
+    args = a[:4] + (_ptr(indices), int(indices.shape[2])) + a[4:15] + a[16:]
+    if _prepare:
+        return PreparedCall("mla_sparse_decode_fwd", args), outs
+    _check("mla_sparse_decode_fwd", load_library().mla_sparse_decode_fwd(*args))
+    return outs
+
+
+def prepare_sparse_decode(*args, **kwargs):
+    """Like ``mla_sparse_decode_fwd`` but returns (PreparedCall, (o_lat, lse))."""
+    return mla_sparse_decode_fwd(*args, _prepare=True, **kwargs)
 
 
 def workspace_partials(workspace: torch.Tensor, total_splits: int, s_q: int, H: int,

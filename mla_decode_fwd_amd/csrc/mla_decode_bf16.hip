@@ -144,6 +144,51 @@ __device__ __forceinline__ void issue_page(const PageLoad& p) {
   for (int n = 0; n < kBlocksPerWave; ++n) issue_line(p, n);
 }
 
+// Top-k decode: a "page" is 64 listed tokens whose rows sit anywhere in the
+// pool, so each lane carries its own two source addresses (the rows of its
+// two tokens, at its chunk) and the load takes a 64-bit VGPR address. The
+// LDS side is the page layout above, unchanged.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_line_addr(uint64_t vaddr, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(vaddr), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+struct GatherLoad {
+  uint64_t src0, src1;  // per-lane row addresses of the wave's two token octets, at the lane's chunk
+  uint32_t lds;         // LDS address of the wave's first block (wave-uniform)
+};
+
+// row_ids: the 64 physical row numbers (page * 64 + slot) of the listed tokens.
+__device__ __forceinline__ GatherLoad make_gather_load(const char* cache, const int32_t* row_ids, char* lds_buf,
+                                                       int wave, int lane) {
+  GatherLoad p;
+  char* dst = lds_buf + wave * (kBlocksPerWave * 1024);
+  p.lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+  const int t0 = 16 * wave + (lane >> 3);
+  p.src0 = (uint64_t)(uintptr_t)(cache + (size_t)row_ids[t0] * kRowBytes + (((lane & 7) ^ swz(t0)) * 16));
+  p.src1 = (uint64_t)(uintptr_t)(cache + (size_t)row_ids[t0 + 8] * kRowBytes + (((lane & 7) ^ swz(t0 + 8)) * 16));
+  return p;
+}
+
+__device__ __forceinline__ void issue_line(const GatherLoad& p, int n) {
+  const int octet = n / 9, j = n % 9;
+  dma_line_addr((octet ? p.src1 : p.src0) + 128 * j, p.lds + 1024 * (9 * octet + j));
+}
+
+__device__ __forceinline__ void issue_page(const GatherLoad& p) {
+#pragma unroll
+  for (int n = 0; n < kBlocksPerWave; ++n) issue_line(p, n);
+}
+
 // Value of lane l ^ 32 (gfx950 lane swap; VALU, no LDS round trip). With
 // both operands equal, permlane32_swap yields the values of lanes l and l^32.
 __device__ __forceinline__ float other_half(float v) {
@@ -989,8 +1034,17 @@ __device__ __forceinline__ WorkItem find_work(const int32_t* split_offsets, cons
   return w;
 }
 
+// kSparse: top-k decode. The chunk walks "pages" of 64 consecutive entries of
+// the query token's selected-token list instead of the sequence's pages: the
+// prologue resolves the chunk's entries through the block table into
+// physical row numbers (kept in LDS after the page buffers, with one 64-bit
+// validity mask per page), each page is then gathered row by row, and
+// entries outside [0, L_b) are masked out of the softmax (their slot is
+// loaded from the sequence's token 0, so P = 0 meets finite values).
+template <bool kSparse>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a, int row_groups) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
+  constexpr int kSparseBytes = kSparse ? kSparseMaxTopk * 4 + (kSparseMaxTopk / kPage) * 8 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + kSparseBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it in an SGPR
@@ -1011,8 +1065,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
 
   const WorkItem wi = find_work(a.split_offsets, a.seqlens, a.B, g, lane);
   const int b = wi.b;
-  const int L = max(a.s_q, min(wi.L, a.max_pages * kPage));
-  const int P = (L + kPage - 1) / kPage;
+  // Top-k: the chunks split the list (topk entries); positions must be < L.
+  const int L = max(kSparse ? 1 : a.s_q, min(wi.L, a.max_pages * kPage));
+  const int P = ((kSparse ? a.topk : L) + kPage - 1) / kPage;
   const int n_chunks = min(max(wi.n, 1), kMaxSplits);
   const int kk = min(max(wi.k, 0), n_chunks - 1);
   // kk * P < 64 * 2^25: exact in 32-bit unsigned arithmetic.
@@ -1033,11 +1088,35 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int32_t* btab = a.block_table + (size_t)b * a.max_pages;
   const int last_phys = a.num_pages - 1;
 
-  // The first two block-table entries are requested, then the Q loads are
-  // issued while they travel, then the first page's loads. Later entries are
-  // read one page ahead of their use, so that no page waits on a table read.
-  const int bt0 = btab[max(min(pg0, pg1 - 1), 0)];  // an empty chunk (pg0 == pg1) reads entry 0, unused
-  const int bt1 = btab[max(min(pg0 + 1, pg1 - 1), 0)];
+  int32_t* const s_ids = reinterpret_cast<int32_t*>(smem + 2 * kPageBytes);  // top-k only
+  uint64_t* const s_mask = reinterpret_cast<uint64_t*>(smem + 2 * kPageBytes + kSparseMaxTopk * 4);
+
+  // Dense: the first two block-table entries are requested, then the Q loads
+  // are issued while they travel, then the first page's loads. Later entries
+  // are read one page ahead of their use, so that no page waits on a table
+  // read. Top-k: the chunk's list entries, then their table entries, are
+  // requested before the Q loads.
+  constexpr int kIt = kSparseMaxTopk / kThreads;
+  int bt0 = 0, bt1 = 0;
+  int lpos[kSparse ? kIt : 1], lphys[kSparse ? kIt : 1];
+  if constexpr (kSparse) {
+    const int32_t* list = a.indices + ((size_t)b * a.s_q + rgrp) * a.topk;  // H = 128: row group = query token
+    const int n_tok = (pg1 - pg0) * kPage;  // <= kSparseMaxTopk
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int t = it * kThreads + (int)threadIdx.x;
+      const int e = pg0 * kPage + t;
+      lpos[it] = (t < n_tok && e < a.topk) ? list[e] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const bool valid = lpos[it] >= 0 && lpos[it] < L;
+      lphys[it] = btab[(valid ? lpos[it] : 0) >> 6];
+    }
+  } else {
+    bt0 = btab[max(min(pg0, pg1 - 1), 0)];  // an empty chunk (pg0 == pg1) reads entry 0, unused
+    bt1 = btab[max(min(pg0 + 1, pg1 - 1), 0)];
+  }
   asm volatile("" ::: "memory");  // keep the table reads ahead of the Q loads
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1052,7 +1131,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   }
 
   int phys_ahead = 0;
-  if (pg0 < pg1) {
+  if constexpr (kSparse) {
+    // Physical row numbers of the chunk's entries (invalid ones point at the
+    // sequence's token 0) and the per-page validity masks.
+    const int n_tok = (pg1 - pg0) * kPage;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int t = it * kThreads + (int)threadIdx.x;
+      const bool valid = lpos[it] >= 0 && lpos[it] < L;
+      const unsigned long long m = __ballot(valid);  // wave w of round it holds page 4*it + w
+      if (t < n_tok) {
+        s_ids[t] = min(max(lphys[it], 0), last_phys) * kPage + ((valid ? lpos[it] : 0) & (kPage - 1));
+        if (lane == 0) s_mask[t >> 6] = m;
+      }
+    }
+    __syncthreads();
+    if (pg0 < pg1) issue_page(make_gather_load(cache, s_ids, smem, wave, lane));
+  } else if (pg0 < pg1) {
     const int phys = min(max(bt0, 0), last_phys);
     issue_page(make_page_load(cache + (size_t)phys * kPageBytes, smem, wave, lane));
     phys_ahead = bt1;
@@ -1105,22 +1200,35 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     // unconditionally, from a clamped table index, so that its bases stay
     // wave-uniform SGPRs.)
     const bool has_next = pg + 1 < pg1;
-    const int phys_next = min(max(phys_ahead, 0), last_phys);
-    phys_ahead = btab[min(pg + 2, pg1 - 1)];
-    const PageLoad next = make_page_load(cache + (size_t)phys_next * kPageBytes,
-                                         smem + ((pg + 1 - pg0) & 1) * kPageBytes, wave, lane);
-    const int valid = L - pg * kPage;  // tokens of this page that exist
-    if (valid < kPage) {
-      // Zero the token slots past the end of the sequence: their scores are
-      // masked, but 0 * NaN in PV would still poison the sum.
-      for (int idx = threadIdx.x; idx < (kPage - valid) * 72; idx += kThreads) {
-        const int t = valid + idx / 72;
-        const int c = idx % 72;
-        *reinterpret_cast<uint4*>(buf + slot_bytes(t, c)) = make_uint4(0, 0, 0, 0);
+    char* const next_buf = smem + ((pg + 1 - pg0) & 1) * kPageBytes;
+    const auto next = [&]() {
+      if constexpr (kSparse) {
+        return make_gather_load(cache, s_ids + (min(pg + 1, pg1 - 1) - pg0) * kPage, next_buf, wave, lane);
+      } else {
+        const int phys_next = min(max(phys_ahead, 0), last_phys);
+        phys_ahead = btab[min(pg + 2, pg1 - 1)];
+        return make_page_load(cache + (size_t)phys_next * kPageBytes, next_buf, wave, lane);
       }
-      __syncthreads();
+    }();
+    uint64_t page_mask = ~0ull;  // top-k: valid entries of this page
+    if constexpr (kSparse) {
+      const uint64_t m = s_mask[pg - pg0];
+      page_mask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(m >> 32)) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)m);
+    } else {
+      const int valid = L - pg * kPage;  // tokens of this page that exist
+      if (valid < kPage) {
+        // Zero the token slots past the end of the sequence: their scores are
+        // masked, but 0 * NaN in PV would still poison the sum.
+        for (int idx = threadIdx.x; idx < (kPage - valid) * 72; idx += kThreads) {
+          const int t = valid + idx / 72;
+          const int c = idx % 72;
+          *reinterpret_cast<uint4*>(buf + slot_bytes(t, c)) = make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+      }
     }
-    const bool full_page = (pg + 1) * kPage <= n_allowed_min;
+    const bool full_page = kSparse ? page_mask == ~0ull : (pg + 1) * kPage <= n_allowed_min;
 
     // A page is two 32-token tiles, staggered so that the softmax work of
     // one tile runs between the MFMAs of the other: QK(T0); QK(T1) with
@@ -1149,10 +1257,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     // scaled scores.
     auto tile_max = [&](f32x16_t& st, int T) {
       if (!full_page) {
-        const int tok0 = pg * kPage + 32 * T + 4 * hi32;
+        if constexpr (kSparse) {
+          const uint32_t mt = (uint32_t)(page_mask >> (32 * T)) >> (4 * hi32);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (tok0 + 8 * (r >> 2) + (r & 3) >= n_allowed) st[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (!((mt >> (8 * (r >> 2) + (r & 3))) & 1u)) st[r] = -INFINITY;
+        } else {
+          const int tok0 = pg * kPage + 32 * T + 4 * hi32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (tok0 + 8 * (r >> 2) + (r & 3) >= n_allowed) st[r] = -INFINITY;
+        }
       }
       float mx[8];
 #pragma unroll
@@ -1326,15 +1441,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+template <bool kSparse>
+hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   const int rows = a.s_q * a.H;
   const int row_groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
   const int padded = (a.total_splits + 7) / 8 * 8;
   const dim3 grid((unsigned)(padded * row_groups));
-  hipLaunchKernelGGL(mla_decode_bf16_kernel, grid, dim3(kThreads), 0, stream, a, row_groups);
+  hipLaunchKernelGGL(mla_decode_bf16_kernel<kSparse>, grid, dim3(kThreads), 0, stream, a, row_groups);
   return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch<false>(a, stream); }
+hipError_t launch_sparse_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch<true>(a, stream); }
 
 }  // namespace mla

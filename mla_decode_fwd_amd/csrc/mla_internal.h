@@ -31,10 +31,16 @@ struct DecodeArgs {
   float* lse_part;  // [total_splits, s_q, H]
   void* o_lat;      // [B, s_q, H, 512]; nullptr: write partials for every chunk
   float* lse;       // [B, s_q, H]; nullptr together with o_lat
+  const int32_t* indices = nullptr;  // top-k decode: [B, s_q, topk] token positions
+  int topk = 0;
 };
+
+constexpr int kSparseMaxTopk = 2048;  // selected tokens per query token at most
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp32(const DecodeArgs& a, hipStream_t stream);
+// Top-k decode (bf16, H = 128): the same kernel over gathered token rows.
+hipError_t launch_sparse_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 // LSE merge. skip_single: sequences with one chunk were written directly by
 // the decode kernel and are left alone.

@@ -82,3 +82,36 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
     assert rel_l2 <= t["rel_l2"], (label, stats)
     assert lse_err <= t["lse"], (label, stats)
     return stats
+
+
+def oracle_sparse(case, rows=None):
+    """Oracle result of the top-k decode (case.meta["indices"]) for every
+    sequence or the listed sequence indices."""
+    q = to_np(case.q_lat)
+    table = case.block_table.numpy()
+    L = case.seqlens.numpy()
+    idx_all = case.meta["indices"].numpy()
+    outs, lses = [], []
+    for b in (range(case.B) if rows is None else rows):
+        npg = (int(L[b]) + 63) // 64
+        sub_cache = to_np(case.cache[torch.from_numpy(table[b, :npg].astype(np.int64))])
+        o, lse = orc.decode_sparse(q[b:b + 1], sub_cache, np.arange(npg)[None, :], L[b:b + 1],
+                                   idx_all[b:b + 1], case.scale, dv=512)
+        outs.append(o[0])
+        lses.append(lse[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def run_sparse(case, plan="auto", num_cus=256, dev="cuda"):
+    """Top-k decode on the GPU through the C ABI."""
+    d = to_device(case, dev)
+    idx = case.meta["indices"].to(dev)
+    kw = {}
+    if plan == "auto":
+        p = mla.sparse_decode_plan(case.B, case.meta["topk"], case.s_q, case.H, num_cus=num_cus)
+        if p.any_split:
+            kw = dict(split_offsets=p.device_offsets(dev), total_splits=p.total_splits)
+    o, lse = mla.mla_sparse_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], idx,
+                                       case.scale, **kw)
+    torch.cuda.synchronize()
+    return o, lse

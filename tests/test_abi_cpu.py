@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 1
+    assert mla.abi_version() == 2
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -140,3 +140,35 @@ def test_combine_and_bmm_validation(lib):
     assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 4, 128, 128, 64, 512, 9, FAKE, None) == UNSUPPORTED
     assert lib.mla_out_uv(FAKE, None, 4, 128, 512, 128, 0, FAKE, None) == INVALID
     assert lib.mla_out_uv(FAKE, FAKE, 4, 2000, 512, 128, 0, FAKE, None) == UNSUPPORTED
+
+
+def _sparse(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, idx=FAKE, topk=2048, so=None, total=2, B=2, s_q=1, H=128,
+             dqk=576, dv=512, page=64, maxp=4, npages=8, scale=0.0722, dtype=0, ws=None, wsb=0, o=FAKE,
+             lse=FAKE)
+    a.update(kw)
+    return lib.mla_sparse_decode_fwd(a["q"], a["kv"], a["bt"], a["sl"], a["idx"], a["topk"], a["so"], a["total"],
+                                     a["B"], a["s_q"], a["H"], a["dqk"], a["dv"], a["page"], a["maxp"],
+                                     a["npages"], a["scale"], a["dtype"], a["ws"], a["wsb"], a["o"], a["lse"],
+                                     None)
+
+
+def test_sparse_decode_validation(lib):
+    assert _sparse(lib, idx=None) == INVALID
+    assert _sparse(lib, topk=0) == UNSUPPORTED
+    assert _sparse(lib, topk=2049) == UNSUPPORTED
+    assert _sparse(lib, H=64) == UNSUPPORTED  # one row group per new token needs H = 128
+    assert _sparse(lib, dtype=1) == UNSUPPORTED  # bf16 only
+    assert _sparse(lib, dtype=7) == UNSUPPORTED
+    assert _sparse(lib, q=None) == INVALID
+    assert _sparse(lib, scale=0.0) == INVALID
+    assert _sparse(lib, total=3) == INVALID
+    assert _sparse(lib, so=FAKE, total=4, ws=None, wsb=1 << 30) == WORKSPACE
+    assert _sparse(lib, o=None, lse=None) == INVALID
+
+
+def test_sparse_plan_cuts_the_list():
+    p = mla.sparse_decode_plan(64, 2048)
+    assert p.total_splits == 256 and int(p.num_splits.max()) == 4
+    p1 = mla.sparse_decode_plan(1, 2048)
+    assert p1.total_splits == 32  # 32 pages of list, one per chunk at most
