@@ -235,6 +235,32 @@ def sparse_case(seqlens: Sequence[int], s_q: int = 1, topk: int = 2048, seed: in
     return case
 
 
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_case(seqlens: Sequence[int], s_q: int = 1, seed: int = 100, H: int = 128,
+             q_scale: float = 1.0 / math.sqrt(D_QK), name: str = "") -> DecodeCase:
+    """A paged decode problem with an FP8 (e4m3) latent cache and one fp32
+    scale per cache row. The rows are drawn as in ``make_decode_case`` (bf16
+    values), scaled per row by max|row| / 448 and rounded to e4m3 by torch's
+    float8_e4m3fn conversion. ``meta["cache_fp8"]`` holds the codes
+    [pages, 64, 576] uint8 and ``meta["row_scales"]`` [pages, 64] fp32; rows
+    no sequence owns hold NaN codes (0x7F) and NaN scales. ``cache`` keeps
+    the bf16 draw."""
+    case = make_decode_case(seqlens, s_q=s_q, H=H, seed=seed, q_scale=q_scale,
+                            name=name or f"fp8 B={len(seqlens)} s_q={s_q}")
+    x = case.cache.float()
+    owned = ~torch.isnan(x).any(dim=-1)
+    amax = torch.where(owned, x.abs().amax(dim=-1), torch.ones_like(x[..., 0]))
+    scales = torch.where(amax > 0, amax / FP8_E4M3_MAX, torch.ones_like(amax))
+    codes = (x / scales[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes[~owned] = 0x7F
+    scales[~owned] = float("nan")
+    case.meta["cache_fp8"] = codes.contiguous()
+    case.meta["row_scales"] = scales.contiguous()
+    return case
+
+
 def tiny_mla_weights(seed: int = 0) -> dict:
     """The tiny full-MLA draws of the handbook chapter's worked example.
 

@@ -29,6 +29,10 @@ Function list and pins:
   lse_merge          log-sum-exp merge of chunk results     pinned (merge == unsplit)
   decode_sparse      absorbed decode over top-k token lists pinned (full list == dense, brute
                                                             force, closed forms)
+  e4m3_decode        FP8 (e4m3, no infinities) code -> value pinned (all 256 codes vs torch,
+                                                            hand values)
+  decode_absorbed_fp8 absorbed decode on an FP8 cache with  pinned (closed forms, the dequantised
+                     one scale per token row                 cache through decode_absorbed)
 No function is left without a pin.
 """
 from __future__ import annotations
@@ -50,6 +54,8 @@ __all__ = [
     "decode_partials",
     "lse_merge",
     "decode_sparse",
+    "e4m3_decode",
+    "decode_absorbed_fp8",
 ]
 
 
@@ -349,3 +355,37 @@ def decode_sparse(q_lat, cache, block_table, seqlens, indices, scale: float, dv:
             o[b, i] = (e / Z) @ K[:, :dv]
             lse[b, i] = (M + np.log(Z))[:, 0]
     return o, lse
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of FP8 e4m3 codes (the "fn" variant: no infinities), float64.
+
+    Bit layout: sign (bit 7), exponent E (bits 3..6, bias 7), mantissa M
+    (bits 0..2). E = 0 is subnormal: M * 2^-9. Otherwise (1 + M/8) * 2^(E-7).
+    E = 15 with M = 7 is NaN (the only non-finite code); the largest finite
+    magnitude is 448. This is the format the pages name for the FP8 latent
+    cache ([MLA-推理] §"练习" exercise 2 and §"decode 注意力变成了计算问题").
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    E = (c >> 3) & 0xF
+    M = (c & 0x7).astype(np.float64)
+    mag = np.where(E == 0, M * 2.0 ** -9, (1.0 + M / 8.0) * np.exp2(E.astype(np.float64) - 7.0))
+    mag = np.where((E == 15) & (M == 7), np.nan, mag)
+    return sign * mag
+
+
+def decode_absorbed_fp8(q_lat, cache_codes, row_scales, block_table, seqlens, scale: float, causal: bool,
+                        dv: int = 512):
+    """Absorbed decode on an FP8 latent cache.
+
+    [MLA-推理] §"练习" exercise 2: with the latent cache stored in FP8 a cached
+    token is 576 bytes plus its scale factors. The reading used here: every
+    cache row holds 576 e4m3 codes and one fp32 scale, and its value is
+    scale * e4m3_decode(codes); the key is the whole row and the value its
+    first ``dv`` elements, exactly as in decode_absorbed, which runs on the
+    dequantised rows.
+    cache_codes [num_pages, page, 576] uint8, row_scales [num_pages, page].
+    """
+    rows = e4m3_decode(cache_codes) * _f64(row_scales)[..., None]
+    return decode_absorbed(q_lat, rows, block_table, seqlens, scale, causal, dv=dv)

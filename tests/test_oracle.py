@@ -459,3 +459,62 @@ def test_mutation_sparse_padding_as_token_zero_is_caught(monkeypatch):
     monkeypatch.setattr(orc, "decode_sparse", pad_as_zero)
     with pytest.raises(AssertionError):
         test_sparse_matches_brute_force()
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) latent cache.
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decoder_matches_torch_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+def test_e4m3_hand_values():
+    v = orc.e4m3_decode([0x38, 0xB8, 0x7E, 0x01, 0x08, 0x00, 0x80, 0x3C])
+    assert list(v[:5]) == [1.0, -1.0, 448.0, 2.0 ** -9, 2.0 ** -6]
+    assert v[5] == 0.0 and np.signbit(v[6]) and v[7] == 1.5
+
+
+def test_fp8_decode_closed_forms():
+    # One key per sequence: o = its dequantised value, lse = its score. All
+    # rows' codes equal with scales s_j: a softmax over s_j-scaled copies.
+    from mla_inputs import fp8_case
+    case = fp8_case([1, 1], s_q=1, H=8, seed=101, q_scale=1.0)
+    q = _np(case.q_lat)
+    codes = case.meta["cache_fp8"].numpy()
+    sc = case.meta["row_scales"].numpy()
+    table = case.block_table.numpy()
+    o, lse = orc.decode_absorbed_fp8(q, codes, sc, table, case.seqlens.numpy(), case.scale, False)
+    for b in range(2):
+        p = table[b, 0]
+        row = orc.e4m3_decode(codes[p, 0]) * float(sc[p, 0])
+        assert np.allclose(o[b, 0], np.broadcast_to(row[:512], (8, 512)), rtol=0, atol=0)
+        assert np.allclose(lse[b, 0], case.scale * (q[b, 0] @ row), atol=1e-12)
+    # Same codes in every row, scales 1 and 2: o = sum_j w_j s_j r with
+    # w = softmax(s_j * score(r)), lse closed form.
+    case2 = fp8_case([2], s_q=1, H=4, seed=102, q_scale=1.0)
+    q2 = _np(case2.q_lat)
+    codes2 = case2.meta["cache_fp8"].numpy().copy()
+    sc2 = case2.meta["row_scales"].numpy().copy()
+    t2 = case2.block_table.numpy()
+    p = t2[0, 0]
+    codes2[p, 1] = codes2[p, 0]
+    sc2[p, 0], sc2[p, 1] = 1.0, 2.0
+    o2, l2 = orc.decode_absorbed_fp8(q2, codes2, sc2, t2, case2.seqlens.numpy(), case2.scale, False)
+    r = orc.e4m3_decode(codes2[p, 0])
+    s1 = case2.scale * (q2[0, 0] @ r)  # [H]
+    w1, w2 = np.exp(s1), np.exp(2 * s1)
+    assert np.allclose(l2[0, 0], np.log(w1 + w2), atol=1e-12)
+    assert np.allclose(o2[0, 0], ((w1 + 2 * w2) / (w1 + w2))[:, None] * r[None, :512], atol=1e-12)
+
+
+def test_mutation_e4m3_wrong_bias_is_caught(monkeypatch):
+    real = orc.e4m3_decode
+    monkeypatch.setattr(orc, "e4m3_decode", lambda c: real(c) * 2.0)  # bias 6 instead of 7
+    with pytest.raises(AssertionError):
+        test_e4m3_hand_values()
