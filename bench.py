@@ -47,7 +47,8 @@ DEFAULT_WORKLOAD_TEXT = ("batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=
                          "64-token pages in a shuffled pool")
 # --workload name -> seeded input recipe (mla_inputs.config_case index, mtp<s_q>, or the
 # top-k shape: B=64 histories of 16384 tokens, 2048 selected per new token)
-WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8", "topk": "topk"}
+WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8", "topk": "topk",
+             "fp8": "fp8"}
 TOPK_SHAPE = dict(B=64, L=16384, topk=2048)
 
 
@@ -82,6 +83,7 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     """Time the fp64 oracle on whole sequences of the batch, in order and
     wrapping around, until about budget_s seconds of work are done."""
     import numpy as np
+    import torch
 
     from mla_decode_fwd_amd import accounting as acc
     from oracle import mla_oracle as orc
@@ -95,11 +97,18 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     cached = {}
     keep = sum(int(x) for x in L) * case.cache.shape[-1] * 8 < (2 << 30)
 
+    fp8 = "cache_fp8" in case.meta
+
     def sub(b):
         if b in cached:
             return cached[b]
         npg = (int(L[b]) + 63) // 64
-        v = (case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None])
+        if fp8:
+            sel = torch.from_numpy(table[b, :npg].astype(np.int64))
+            v = ((case.meta["cache_fp8"][sel].numpy(), case.meta["row_scales"][sel].double().numpy()),
+                 np.arange(npg)[None])
+        else:
+            v = (case.cache[table[b, :npg]].double().numpy(), np.arange(npg)[None])
         if keep:
             cached[b] = v
         return v
@@ -110,7 +119,9 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
         b = len(done) % case.B
         c, t = sub(b)
         t0 = time.perf_counter()
-        if idx is None:
+        if fp8:
+            orc.decode_absorbed_fp8(q[b:b + 1], c[0], c[1], t, L[b:b + 1], case.scale, case.causal, dv=512)
+        elif idx is None:
             orc.decode_absorbed(q[b:b + 1], c, t, L[b:b + 1], case.scale, case.causal, dv=512)
         else:
             orc.decode_sparse(q[b:b + 1], c, t, L[b:b + 1], idx[b:b + 1], case.scale, dv=512)
@@ -154,7 +165,7 @@ def main():
 
     import mla_decode_fwd_amd as mla
     from mla_decode_fwd_amd import accounting as acc
-    from mla_inputs import config_case, mtp_case, sparse_case
+    from mla_inputs import config_case, fp8_case, mtp_case, sparse_case
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -162,7 +173,10 @@ def main():
 
     wl = WORKLOADS[args.workload]
     topk_mode = wl == "topk"
-    if topk_mode:
+    fp8_mode = wl == "fp8"
+    if fp8_mode:
+        case = fp8_case([4096] * 64, s_q=1, seed=2, name="fp8 batched B=64 ctx=4096")
+    elif topk_mode:
         case = sparse_case([TOPK_SHAPE["L"]] * TOPK_SHAPE["B"], s_q=1, topk=TOPK_SHAPE["topk"], seed=90)
     elif isinstance(wl, int):
         case = config_case(wl)
@@ -174,9 +188,13 @@ def main():
     npages = case.cache.shape[0]
     for k in range(2):
         # The second copy holds the same pages one slot further along the pool.
-        cache = case.cache if k == 0 else case.cache.roll(1, 0)
+        src = case.meta["cache_fp8"] if fp8_mode else case.cache
+        cache = src if k == 0 else src.roll(1, 0)
         bt = case.block_table if k == 0 else ((case.block_table.long() + 1) % npages).to(torch.int32)
         sets.append(dict(q=case.q_lat.to(dev), kv=cache.to(dev), bt=bt.to(dev), sl=case.seqlens.to(dev)))
+        if fp8_mode:
+            sc = case.meta["row_scales"]
+            sets[-1]["sc"] = (sc if k == 0 else sc.roll(1, 0)).to(dev)
     t0 = time.perf_counter()
     plan = mla.sparse_decode_plan(B, case.meta["topk"], s_q, H) if topk_mode else mla.decode_plan(L, s_q, H)
     plan_us = (time.perf_counter() - t0) * 1e6
@@ -189,7 +207,11 @@ def main():
 
     # Both launches are prepared once (checks and argument marshalling done
     # up front) so that the host enqueues a step faster than the GPU runs it.
-    if topk_mode:
+    if fp8_mode:
+        dec_calls = [mla.prepare_decode_fp8(s["q"], s["kv"], s["sc"], s["bt"], s["sl"], case.scale, case.causal,
+                                            split_offsets=offs, total_splits=plan.total_splits, workspace=ws,
+                                            partials_only=True)[0] for s in sets]
+    elif topk_mode:
         idx_dev = case.meta["indices"].to(dev)
         dec_calls = [mla.prepare_sparse_decode(s["q"], s["kv"], s["bt"], s["sl"], idx_dev, case.scale,
                                                split_offsets=offs, total_splits=plan.total_splits, workspace=ws,
@@ -235,6 +257,10 @@ def main():
         flops = acc.sparse_decode_flops(counts, H)
         nbytes = acc.sparse_decode_bytes(counts, B, s_q, H, case.meta["topk"])
         kv_only = float(counts.sum()) * 1152
+    elif fp8_mode:
+        flops = acc.decode_flops(L, s_q, H)
+        nbytes = acc.decode_bytes_fp8(L, s_q, H)
+        kv_only = float(sum(L)) * 580
     else:
         flops = acc.decode_flops(L, s_q, H)
         nbytes = acc.decode_bytes(L, s_q, H)
@@ -259,18 +285,24 @@ def main():
                                  f"{TOPK_SHAPE['topk']} selected per new token (uniform, distinct), s_q=1, "
                                  f"H={H}, d_qk=576, d_v=512, bf16, 64-token pages in a shuffled pool")
                                 if topk_mode else
+                                ("absorbed-MLA decode on an FP8 (e4m3) latent cache with one fp32 scale per row, "
+                                 "B=64 x ctx 4096, s_q=1, H=128, d_qk=576, d_v=512, bf16 queries/outputs, "
+                                 "64-token pages in a shuffled pool")
+                                if fp8_mode else
                                 f"absorbed-MLA decode, {case.name}, H={H}, d_qk=576, d_v=512, bf16, "
                                 "64-token pages in a shuffled pool"),
                    "B": B, "ctx": int(max(L)) if args.workload != "batched" else 4096,
                    "ctx_total": int(sum(L)), "s_q": s_q, "H": H,
-                   "splits_per_seq": int(plan.num_splits.max()), "parallelism": "single GPU"},
+                   "splits_per_seq": int(plan.num_splits.max()), "parallelism": "single GPU",
+                   "cache": "fp8-e4m3 + fp32 row scales" if fp8_mode else "bf16"},
         "hbm_gbs": round(step_rf["gbs"], 1),
         "roofline_frac": round(step_rf["frac"], 4),
         "roofline_frac_kv_only": round(kv_only / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),
         "roofline": {"bound": dec_rf["bound"], "achieved": round(dec_rf["achieved"], 1),
                      "peak": dec_rf["peak"], "unit": dec_rf["unit"], "frac": round(dec_rf["frac"], 4),
                      "traffic": measured_traffic() if args.workload == "batched" else None,
-                     "kernel": "mla_decode_bf16_kernel<true>" if topk_mode else "mla_decode_bf16_kernel",
+                     "kernel": ("mla_decode_bf16_kernel<true>" if topk_mode else
+                                "mla_decode_fp8_kernel" if fp8_mode else "mla_decode_bf16_kernel"),
                      "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},

@@ -73,7 +73,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 2 (2 added mla_sparse_decode_fwd). */
+/* Library ABI version, currently 3 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8). */
 int mla_abi_version(void);
 
 /*
@@ -195,6 +195,31 @@ mla_status_t mla_sparse_decode_fwd(const void* q_lat, const void* kv_cache, cons
                                    int d_qk, int d_v, int page_size, int max_pages_per_seq, int num_pages,
                                    float softmax_scale, mla_dtype_t dtype, void* workspace,
                                    size_t workspace_bytes, void* o_lat, float* lse, void* stream);
+
+/*
+ * Absorbed-MLA decode on an FP8 latent cache ([MLA-推理] section "练习",
+ * exercise 2: with the latent cache in FP8 a cached token is 576 bytes plus
+ * its scale factors, which halves the bytes read per token and doubles the
+ * arithmetic intensity to about 484 FLOP/byte). Each cache row holds 576
+ * e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, NaN = 0x7F/0xFF) and has one fp32 scale; its value is
+ *   row = row_scales[page, slot] * e4m3(kv_cache_e4m3[page, slot, :]).
+ * The result is mla_decode_fwd's on those row values (bf16 q_lat, bf16 o_lat,
+ * fp32 LSE, same split, workspace and partials-only rules; partials in bf16).
+ *
+ *   kv_cache_e4m3    [num_pages, 64, 576] uint8 codes (device).
+ *   row_scales       [num_pages, 64] fp32 (device). Rows no sequence owns may
+ *                    hold anything, NaN included: they never reach a product.
+ *   Every other argument as mla_decode_fwd with dtype MLA_BF16.
+ * Compute: the codes are widened to bf16 on the chip (exactly), the bf16 MFMA
+ * path runs with fp32 accumulation, and each row's scale multiplies its score
+ * and, for the value, its P.
+ */
+mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, const float* row_scales,
+                                const int32_t* block_table, const int32_t* seqlens, const int32_t* split_offsets,
+                                int total_splits, int B, int s_q, int H, int d_qk, int d_v, int page_size,
+                                int max_pages_per_seq, int num_pages, float softmax_scale, int causal,
+                                void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream);
 
 /*
  * LSE merge of split-KV partial results ([MLA-推理] sections

@@ -71,6 +71,7 @@ def load_library():
         "mla_decode_plan": ([P, I, I, I, I, I, P, P, P], I),
         "mla_decode_fwd": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, Z, P, P, P], I),
         "mla_sparse_decode_fwd": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P, Z, P, P, P], I),
+        "mla_decode_fwd_fp8": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, Z, P, P, P], I),
         "mla_splitkv_combine": ([P, P, P, I, I, I, I, I, I, P, P, P], I),
         "mla_absorb_q": ([P, P, P, I, I, I, I, I, I, P, P], I),
         "mla_out_uv": ([P, P, I, I, I, I, I, P, P], I),
@@ -248,6 +249,61 @@ def mla_sparse_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_tab
         return PreparedCall("mla_sparse_decode_fwd", args), outs
     _check("mla_sparse_decode_fwd", load_library().mla_sparse_decode_fwd(*args))
     return outs
+
+
+def mla_decode_fwd_fp8(q_lat: torch.Tensor, kv_cache_e4m3: torch.Tensor, row_scales: torch.Tensor,
+                       block_table: torch.Tensor, seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                       split_offsets: Optional[torch.Tensor] = None, total_splits: Optional[int] = None,
+                       workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, partials_only: bool = False, _prepare: bool = False):
+    """Decode on an FP8 latent cache (mla_decode_fwd_fp8): ``kv_cache_e4m3``
+    [pages, 64, 576] uint8 e4m3 codes, ``row_scales`` [pages, 64] fp32, bf16
+    q_lat and o_lat. Other arguments and results as ``mla_decode_fwd``."""
+    if q_lat.dim() != 4 or kv_cache_e4m3.dim() != 3 or block_table.dim() != 2 or seqlens.dim() != 1:
+        raise ValueError("expected q_lat [B,s_q,H,576], kv_cache_e4m3 [pages,64,576], block_table [B,P], seqlens [B]")
+    dev = q_lat.device
+    _need(q_lat, "q_lat", dtype=torch.bfloat16, device=dev)
+    _need(kv_cache_e4m3, "kv_cache_e4m3", dtype=torch.uint8, device=dev)
+    _need(row_scales, "row_scales", dtype=torch.float32, device=dev)
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    _need(seqlens, "seqlens", dtype=torch.int32, device=dev)
+    if tuple(row_scales.shape) != tuple(kv_cache_e4m3.shape[:2]):
+        raise ValueError("row_scales must be [pages, 64]")
+    B, s_q, H, dqk = q_lat.shape
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table and seqlens must have B rows")
+    if split_offsets is not None:
+        _need(split_offsets, "split_offsets", dtype=torch.int32, device=dev)
+        if split_offsets.shape[0] != B + 1 or total_splits is None:
+            raise ValueError("split_offsets must have B+1 entries and total_splits is required")
+        if workspace is None:
+            workspace = torch.empty(decode_workspace_size(total_splits, s_q, H), dtype=torch.uint8, device=dev)
+    else:
+        total_splits = B
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+    if partials_only:
+        if split_offsets is None or o_lat is not None or lse is not None:
+            raise ValueError("partials_only needs split_offsets and no o_lat/lse")
+    else:
+        o_lat = torch.empty((B, s_q, H, D_V), dtype=torch.bfloat16, device=dev) if o_lat is None else o_lat
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev) if lse is None else lse
+        _need(o_lat, "o_lat", dtype=torch.bfloat16, device=dev)
+        _need(lse, "lse", dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q_lat), _ptr(kv_cache_e4m3), _ptr(row_scales), _ptr(block_table), _ptr(seqlens),
+            _ptr(split_offsets), int(total_splits), B, s_q, H, dqk, D_V, int(kv_cache_e4m3.shape[1]),
+            int(block_table.shape[1]), int(kv_cache_e4m3.shape[0]), float(softmax_scale), int(bool(causal)),
+            _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
+    if _prepare:
+        return PreparedCall("mla_decode_fwd_fp8", args), (o_lat, lse)
+    _check("mla_decode_fwd_fp8", load_library().mla_decode_fwd_fp8(*args))
+    return o_lat, lse
+
+
+def prepare_decode_fp8(*args, **kwargs):
+    """Like ``mla_decode_fwd_fp8`` but returns (PreparedCall, (o_lat, lse))."""
+    return mla_decode_fwd_fp8(*args, _prepare=True, **kwargs)
 
 
 def prepare_sparse_decode(*args, **kwargs):

@@ -117,6 +117,18 @@ def sparse_decode_bytes(valid_counts, B: int, s_q: int, H: int, topk: int, elem_
     return rows + lists + B * s_q * H * (d_qk * elem_bytes + d_v * elem_bytes + 4)
 
 
+def decode_bytes_fp8(seqlens: Iterable[int], s_q: int, H: int, d_qk: int = 576, d_v: int = 512,
+                     page: int = 64) -> float:
+    """Algorithmic HBM bytes of one decode call on an FP8 latent cache: each
+    cached row once as d_qk one-byte codes plus its fp32 scale; bf16 q and o,
+    the fp32 LSE and the block-table entries in use."""
+    seqlens = [int(L) for L in seqlens]
+    B = len(seqlens)
+    kv = sum(L * (d_qk + 4) for L in seqlens)
+    table = sum(((L + page - 1) // page) * 4 for L in seqlens)
+    return float(kv + B * s_q * H * (d_qk * 2 + d_v * 2 + 4) + table)
+
+
 def kv_bytes(seqlens: Iterable[int], elem_bytes: int = 2, d_qk: int = 576) -> float:
     return float(sum(int(L) * d_qk * elem_bytes for L in seqlens))
 

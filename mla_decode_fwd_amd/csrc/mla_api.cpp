@@ -45,7 +45,7 @@ const char* mla_status_string(mla_status_t status) {
   return "unknown status";
 }
 
-int mla_abi_version(void) { return 2; }
+int mla_abi_version(void) { return 3; }
 
 size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
   return workspace_size(total_splits, s_q, H);
@@ -94,8 +94,8 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
 namespace {
 
 // Shared by the dense and the top-k entry points (indices == nullptr: dense).
-mla_status_t run_decode(const void* q_lat, const void* kv_cache, const int32_t* block_table,
-                        const int32_t* seqlens, const int32_t* indices, int topk,
+mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* row_scales,
+                        const int32_t* block_table, const int32_t* seqlens, const int32_t* indices, int topk,
                         const int32_t* split_offsets, int total_splits, int B, int s_q, int H, int d_qk,
                         int d_v, int page_size, int max_pages_per_seq, int num_pages, float softmax_scale,
                         int causal, mla_dtype_t dtype, void* workspace, size_t workspace_bytes, void* o_lat,
@@ -137,6 +137,7 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const int32_t* 
   a.lse = lse;
   a.indices = indices;
   a.topk = topk;
+  a.row_scales = row_scales;
   if (split_offsets) {
     const size_t rows = (size_t)total_splits * s_q * H;
     // The o_part region is sized for fp32 whatever the dtype, so the LSE
@@ -145,8 +146,9 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const int32_t* 
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + rows * mla::kDv * sizeof(float));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = indices ? mla::launch_sparse_decode_bf16(a, st)
-                         : (dtype == MLA_BF16 ? mla::launch_decode_bf16(a, st) : mla::launch_decode_fp32(a, st));
+  hipError_t e = indices      ? mla::launch_sparse_decode_bf16(a, st)
+                 : row_scales ? mla::launch_decode_fp8(a, st)
+                 : (dtype == MLA_BF16 ? mla::launch_decode_bf16(a, st) : mla::launch_decode_fp32(a, st));
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (split_offsets && !partials_only) {
     e = mla::launch_combine(a.o_part, a.lse_part, split_offsets, total_splits, B, s_q, H, dtype == MLA_BF16,
@@ -163,7 +165,7 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
                             int page_size, int max_pages_per_seq, int num_pages,
                             float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
                             size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
-  return run_decode(q_lat, kv_cache, block_table, seqlens, nullptr, 0, split_offsets, total_splits, B, s_q, H,
+  return run_decode(q_lat, kv_cache, nullptr, block_table, seqlens, nullptr, 0, split_offsets, total_splits, B, s_q, H,
                     d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, dtype, workspace,
                     workspace_bytes, o_lat, lse, stream);
 }
@@ -178,8 +180,19 @@ mla_status_t mla_sparse_decode_fwd(const void* q_lat, const void* kv_cache, cons
   if (topk < 1 || topk > mla::kSparseMaxTopk) return MLA_ERR_UNSUPPORTED;
   if (!known_dtype(dtype)) return MLA_ERR_UNSUPPORTED;
   if (dtype != MLA_BF16 || H != mla::kRowsPerGroup) return MLA_ERR_UNSUPPORTED;
-  return run_decode(q_lat, kv_cache, block_table, seqlens, indices, topk, split_offsets, total_splits, B, s_q,
+  return run_decode(q_lat, kv_cache, nullptr, block_table, seqlens, indices, topk, split_offsets, total_splits, B, s_q,
                     H, d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, /*causal=*/0, dtype,
+                    workspace, workspace_bytes, o_lat, lse, stream);
+}
+
+mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, const float* row_scales,
+                                const int32_t* block_table, const int32_t* seqlens, const int32_t* split_offsets,
+                                int total_splits, int B, int s_q, int H, int d_qk, int d_v, int page_size,
+                                int max_pages_per_seq, int num_pages, float softmax_scale, int causal,
+                                void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
+  if (!row_scales) return MLA_ERR_INVALID_ARG;
+  return run_decode(q_lat, kv_cache_e4m3, row_scales, block_table, seqlens, nullptr, 0, split_offsets, total_splits,
+                    B, s_q, H, d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, MLA_BF16,
                     workspace, workspace_bytes, o_lat, lse, stream);
 }
 

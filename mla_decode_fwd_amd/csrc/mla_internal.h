@@ -33,6 +33,7 @@ struct DecodeArgs {
   float* lse;       // [B, s_q, H]; nullptr together with o_lat
   const int32_t* indices = nullptr;  // top-k decode: [B, s_q, topk] token positions
   int topk = 0;
+  const float* row_scales = nullptr;  // FP8 cache: [num_pages, 64] fp32, one per cache row
 };
 
 constexpr int kSparseMaxTopk = 2048;  // selected tokens per query token at most
@@ -41,6 +42,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp32(const DecodeArgs& a, hipStream_t stream);
 // Top-k decode (bf16, H = 128): the same kernel over gathered token rows.
 hipError_t launch_sparse_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// FP8 (e4m3) cache with per-row fp32 scales, bf16 queries and outputs.
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 
 // LSE merge. skip_single: sequences with one chunk were written directly by
 // the decode kernel and are left alone.

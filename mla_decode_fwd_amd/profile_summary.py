@@ -25,7 +25,7 @@ import os
 import statistics
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DECODE_SOURCES = ("csrc/mla_decode_bf16.hip", "csrc/mla_internal.h")
+DECODE_SOURCES = ("csrc/mla_decode_bf16.hip", "csrc/mla_decode_common.h", "csrc/mla_internal.h")
 DECODE_KERNEL = "mla_decode_bf16_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 

@@ -65,8 +65,11 @@ def run(case, plan="auto", dev_inputs=None, num_cus=256, max_splits=64, split_of
     return o, lse
 
 
-def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
-    """Assert parity; return the error statistics."""
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label="", abs_relative=False):
+    """Assert parity; return the error statistics. abs_relative: the max-abs
+    bound is taken relative to max(1, max|o_ref|) (sharp-softmax cases, whose
+    outputs approach single value rows of magnitude ~4, where one bf16 output
+    rounding alone is up to 1.6e-2)."""
     o = to_np(o_gpu)
     lse = to_np(lse_gpu)
     assert np.all(np.isfinite(o)), f"{label}: non-finite output"
@@ -78,7 +81,8 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
     t = TOL[dtype]
     stats = dict(max_abs=max_abs, rel_l2=rel_l2, lse=lse_err)
     print(f"[parity] {label} max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} lse={lse_err:.3e}", flush=True)
-    assert max_abs <= t["max_abs"], (label, stats)
+    bound = t["max_abs"] * (max(1.0, float(np.max(np.abs(o_ref)))) if abs_relative else 1.0)
+    assert max_abs <= bound, (label, stats)
     assert rel_l2 <= t["rel_l2"], (label, stats)
     assert lse_err <= t["lse"], (label, stats)
     return stats
@@ -113,5 +117,38 @@ def run_sparse(case, plan="auto", num_cus=256, dev="cuda"):
             kw = dict(split_offsets=p.device_offsets(dev), total_splits=p.total_splits)
     o, lse = mla.mla_sparse_decode_fwd(d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], idx,
                                        case.scale, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_fp8(case, rows=None):
+    """Oracle result of the FP8-cache decode (case.meta["cache_fp8"] codes and
+    case.meta["row_scales"]) for every sequence or the listed ones."""
+    q = to_np(case.q_lat)
+    table = case.block_table.numpy()
+    L = case.seqlens.numpy()
+    codes = case.meta["cache_fp8"]
+    scales = case.meta["row_scales"]
+    outs, lses = [], []
+    for b in (range(case.B) if rows is None else rows):
+        npg = (int(L[b]) + 63) // 64
+        sel = torch.from_numpy(table[b, :npg].astype(np.int64))
+        o, lse = orc.decode_absorbed_fp8(q[b:b + 1], codes[sel].numpy(), scales[sel].numpy().astype(np.float64),
+                                         np.arange(npg)[None, :], L[b:b + 1], case.scale, case.causal, dv=512)
+        outs.append(o[0])
+        lses.append(lse[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def run_fp8(case, plan="auto", num_cus=256, dev="cuda"):
+    """FP8-cache decode on the GPU through the C ABI."""
+    d = to_device(case, dev)
+    kw = {}
+    if plan == "auto":
+        p = mla.decode_plan(case.seqlens.tolist(), case.s_q, case.H, num_cus=num_cus)
+        if p.any_split:
+            kw = dict(split_offsets=p.device_offsets(dev), total_splits=p.total_splits)
+    o, lse = mla.mla_decode_fwd_fp8(d["q_lat"], case.meta["cache_fp8"].to(dev), case.meta["row_scales"].to(dev),
+                                    d["block_table"], d["seqlens"], case.scale, case.causal, **kw)
     torch.cuda.synchronize()
     return o, lse

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 2
+    assert mla.abi_version() == 3
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -172,3 +172,19 @@ def test_sparse_plan_cuts_the_list():
     assert p.total_splits == 256 and int(p.num_splits.max()) == 4
     p1 = mla.sparse_decode_plan(1, 2048)
     assert p1.total_splits == 32  # 32 pages of list, one per chunk at most
+
+
+def test_fp8_decode_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, kv=FAKE, sc=FAKE, bt=FAKE, sl=FAKE, so=None, total=2, B=2, s_q=1, H=128, dqk=576,
+                 dv=512, page=64, maxp=4, npages=8, scale=0.0722, causal=0, ws=None, wsb=0, o=FAKE, lse=FAKE)
+        a.update(kw)
+        return lib.mla_decode_fwd_fp8(a["q"], a["kv"], a["sc"], a["bt"], a["sl"], a["so"], a["total"], a["B"],
+                                      a["s_q"], a["H"], a["dqk"], a["dv"], a["page"], a["maxp"], a["npages"],
+                                      a["scale"], a["causal"], a["ws"], a["wsb"], a["o"], a["lse"], None)
+    assert call(sc=None) == INVALID
+    assert call(kv=None) == INVALID
+    assert call(dqk=512) == UNSUPPORTED
+    assert call(scale=-1.0) == INVALID
+    assert call(so=FAKE, total=4, ws=None, wsb=0) == WORKSPACE
+    assert call(o=None) == INVALID

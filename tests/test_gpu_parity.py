@@ -408,3 +408,54 @@ def test_sparse_dsa_shape_sampled():
     o_ref, l_ref = oracle_sparse(case, rows=sample)
     compare(o[sample], lse[sample], o_ref, l_ref, torch.bfloat16, case.name + " (4 sampled)")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) latent cache
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("plan", ["auto", None])
+@pytest.mark.parametrize("lens,s_q,q_scale", [([300, 64, 129, 7], 1, None), ([300, 64, 129, 7], 1, 1.0),
+                                              ([1000, 130, 5], 2, 1.0), ([700, 129], 8, None)])
+def test_fp8_small(lens, s_q, q_scale, plan):
+    # Rows no sequence owns hold NaN codes and NaN scales; sequence tails end
+    # inside pages; causal among the new tokens for s_q > 1.
+    from gpu_helpers import oracle_fp8, run_fp8
+    from mla_inputs import fp8_case
+    kw = {} if q_scale is None else dict(q_scale=q_scale)
+    case = fp8_case(lens, s_q=s_q, seed=110 + s_q, **kw)
+    o, lse = run_fp8(case, plan=plan, num_cus=32)
+    o_ref, l_ref = oracle_fp8(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, f"{case.name} {lens} q_scale={q_scale} plan={plan}",
+            abs_relative=q_scale is not None)
+
+
+def test_fp8_batched_64x4096_sampled():
+    from gpu_helpers import oracle_fp8, run_fp8
+    from mla_inputs import fp8_case
+    case = fp8_case([4096] * 64, s_q=1, seed=120, name="fp8 batched B=64 ctx=4096")
+    o, lse = run_fp8(case)
+    sample = [0, 17, 40, 63]
+    o_ref, l_ref = oracle_fp8(case, rows=sample)
+    compare(o[sample], lse[sample], o_ref, l_ref, torch.bfloat16, case.name + " (4 sampled)")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_fp8_partials_then_combine_matches_one_call():
+    from gpu_helpers import run_fp8
+    from mla_inputs import fp8_case
+    case = fp8_case([2000, 700, 64], s_q=1, seed=121)
+    d = to_device(case)
+    p = mla.decode_plan(case.seqlens.tolist(), 1, 128, num_cus=16)
+    offs = p.device_offsets("cuda")
+    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device="cuda")
+    codes, scales = case.meta["cache_fp8"].cuda(), case.meta["row_scales"].cuda()
+    mla.mla_decode_fwd_fp8(d["q_lat"], codes, scales, d["block_table"], d["seqlens"], case.scale, False,
+                           split_offsets=offs, total_splits=p.total_splits, workspace=ws, partials_only=True)
+    o_part, lse_part = mla.workspace_partials(ws, p.total_splits, 1, 128)
+    o1, l1 = mla.mla_splitkv_combine(o_part, lse_part, offs, p.total_splits, case.B)
+    o2, l2 = mla.mla_decode_fwd_fp8(d["q_lat"], codes, scales, d["block_table"], d["seqlens"], case.scale, False,
+                                    split_offsets=offs, total_splits=p.total_splits)
+    torch.cuda.synchronize()
+    multi = torch.from_numpy(p.num_splits > 1)
+    assert torch.equal(o1[multi], o2[multi]) and torch.equal(l1[multi], l2[multi])
