@@ -33,6 +33,11 @@ Function list and pins:
                                                             hand values)
   decode_absorbed_fp8 absorbed decode on an FP8 cache with  pinned (closed forms, the dequantised
                      one scale per token row                 cache through decode_absorbed)
+  prefill_expanded   path one on a paged latent cache: new   pinned (== absorb_q + decode_absorbed
+                     tokens after a prefix, per-head K, V    + out_uv; worked example)
+  prefill_chunked    the same over prefix chunks + LSE merge pinned (== unchunked)
+  crossover_tokens   new-token count where the paths' FLOPs  pinned (the chapter's printed 171)
+                     cross, for a given key count
 No function is left without a pin.
 """
 from __future__ import annotations
@@ -56,6 +61,9 @@ __all__ = [
     "decode_sparse",
     "e4m3_decode",
     "decode_absorbed_fp8",
+    "prefill_expanded",
+    "prefill_chunked",
+    "crossover_tokens",
 ]
 
 
@@ -389,3 +397,93 @@ def decode_absorbed_fp8(q_lat, cache_codes, row_scales, block_table, seqlens, sc
     """
     rows = e4m3_decode(cache_codes) * _f64(row_scales)[..., None]
     return decode_absorbed(q_lat, rows, block_table, seqlens, scale, causal, dv=dv)
+
+
+def _prefill_rows(q_nope, q_rope, K_lat, W_uk, W_uv, scale, L, s_q, a, e, causal=True):
+    """Path-one attention of the s_q new tokens over cached tokens [a, e) of a
+    sequence of L tokens (rows K_lat[j] = [c_j ; k^R_j]). Returns o [s_q,H,dv]
+    and lse [s_q,H] (o = 0, lse = -inf where a row sees no key in [a, e))."""
+    dc = W_uk.shape[1]
+    c = K_lat[a:e, :dc]
+    k_r = K_lat[a:e, dc:]
+    k_n = np.einsum("tc,hcd->htd", c, W_uk)            # [H, n, nope]
+    v = np.einsum("tc,hcd->htd", c, W_uv)              # [H, n, dv]
+    H = W_uk.shape[0]
+    o = np.zeros((s_q, H, W_uv.shape[2]))
+    lse = np.full((s_q, H), -np.inf)
+    for i in range(s_q):
+        last = (L - s_q + i) if causal else (L - 1)   # the new tokens are the last s_q of L
+        n = min(e, last + 1) - a
+        if n <= 0:
+            continue
+        s = (np.einsum("hd,htd->ht", q_nope[i], k_n[:, :n]) + q_rope[i] @ k_r[:n].T) * scale  # [H, n]
+        M = s.max(axis=1, keepdims=True)
+        w = np.exp(s - M)
+        Z = w.sum(axis=1, keepdims=True)
+        o[i] = np.einsum("ht,htd->hd", w / Z, v[:, :n])
+        lse[i] = (M + np.log(Z))[:, 0]
+    return o, lse
+
+
+def prefill_expanded(q_nope, q_rope, cache, block_table, seqlens, W_uk, W_uv, scale: float, causal: bool = True):
+    """Path one ("展开") on a paged latent cache, for new tokens after a prefix.
+
+    [MLA-推理] §"两条等价的路径" (path one: expand the latent into per-head
+    keys k^N = c W_UK[h] and values v = c W_UV[h], attach the shared k^R, run
+    ordinary multi-head attention with scale 1/sqrt(nope + rope)) and
+    §"谁快：看新 token 和缓存 token 的数量" (prefill and extend: the s_q new
+    tokens are the last s_q of the L cached ones and see every earlier token).
+    q_nope [B,s_q,H,nope], q_rope [B,s_q,H,rope] (rotated), cache rows
+    [c ; k^R] [num_pages,page,dc+rope], W_uk [H,dc,nope], W_uv [H,dc,dv].
+    Returns per-head outputs o [B,s_q,H,dv] (before W_o) and lse [B,s_q,H].
+    """
+    q_nope, q_rope = _f64(q_nope), _f64(q_rope)
+    W_uk, W_uv = _f64(W_uk), _f64(W_uv)
+    B, s_q, H, _ = q_nope.shape
+    o = np.zeros((B, s_q, H, W_uv.shape[2]))
+    lse = np.zeros((B, s_q, H))
+    for b in range(B):
+        L = int(seqlens[b])
+        K_lat = gather_tokens(cache, block_table[b], L)
+        o[b], lse[b] = _prefill_rows(q_nope[b], q_rope[b], K_lat, W_uk, W_uv, scale, L, s_q, 0, L, causal)
+    return o, lse
+
+
+def prefill_chunked(q_nope, q_rope, cache, block_table, seqlens, W_uk, W_uv, scale: float, chunk: int,
+                    causal: bool = True):
+    """Path one with the cached tokens expanded ``chunk`` at a time.
+
+    [MLA-推理] §"谁快" (SGLang's MHA_CHUNKED_KV: the prefix is expanded chunk by
+    chunk, attention runs per chunk, and the chunk results are merged by
+    their LSE, as in context parallelism). Partials per chunk, then lse_merge.
+    """
+    q_nope, q_rope = _f64(q_nope), _f64(q_rope)
+    W_uk, W_uv = _f64(W_uk), _f64(W_uv)
+    B, s_q, H, _ = q_nope.shape
+    o = np.zeros((B, s_q, H, W_uv.shape[2]))
+    lse = np.zeros((B, s_q, H))
+    for b in range(B):
+        L = int(seqlens[b])
+        K_lat = gather_tokens(cache, block_table[b], L)
+        parts = [_prefill_rows(q_nope[b], q_rope[b], K_lat, W_uk, W_uv, scale, L, s_q, a, min(a + chunk, L), causal)
+                 for a in range(0, L, chunk)]
+        o[b], lse[b] = lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    return o, lse
+
+
+def crossover_tokens(L: int, H: int = 128, nope: int = 128, rope: int = 64, dv: int = 128, dc: int = 512) -> float:
+    """New-token count above which path one (expanded) costs fewer FLOPs for
+    a sequence of L keys counting the new ones.
+
+    [MLA-推理] §"谁快": path one pays the expansion per cached token and the
+    cheap pair cost; path two pays the absorption per new token and the
+    dearer pair cost. With e = expansion per key, b = absorption per query,
+    p1, p2 the pair costs and pairs ≈ q L (q ≪ L), path one wins when
+    q (b + (p2 - p1) L) > e L, i.e. q > e L / (b + (p2 - p1) L); for L → ∞
+    this is e / (p2 - p1), the chapter's 171.
+    """
+    e = 2 * dc * H * (nope + dv)
+    b = 2 * H * nope * dc + 2 * H * dc * dv
+    p1 = 2 * H * (nope + rope) + 2 * H * dv
+    p2 = 2 * H * (dc + rope) + 2 * H * dc
+    return e * L / (b + (p2 - p1) * L)

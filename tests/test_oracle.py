@@ -518,3 +518,65 @@ def test_mutation_e4m3_wrong_bias_is_caught(monkeypatch):
     monkeypatch.setattr(orc, "e4m3_decode", lambda c: real(c) * 2.0)  # bias 6 instead of 7
     with pytest.raises(AssertionError):
         test_e4m3_hand_values()
+
+
+# ---------------------------------------------------------------------------
+# Path one on a paged cache (prefill / extend) and the path choice.
+# ---------------------------------------------------------------------------
+
+def _prefill_case(seed, lens, s_q, H=4, nope=8, rope=4, dv=6, dc=16):
+    rng = np.random.default_rng(seed)
+    case = make_decode_case(lens, s_q=s_q, H=H, seed=seed, dtype=torch.float32, d_qk=dc + rope, q_scale=1.0,
+                            scale=1.0 / math.sqrt(nope + rope))
+    q_n = rng.standard_normal((len(lens), s_q, H, nope))
+    q_r = rng.standard_normal((len(lens), s_q, H, rope))
+    W_uk = rng.standard_normal((H, dc, nope)) / 4
+    W_uv = rng.standard_normal((H, dc, dv)) / 4
+    return case, q_n, q_r, W_uk, W_uv
+
+
+@pytest.mark.parametrize("s_q,lens", [(1, [1, 40]), (3, [3, 70, 129]), (17, [17, 100])])
+def test_prefill_expanded_equals_absorbed_path(s_q, lens):
+    # Path one (expand, then MHA) and path two (absorb q, latent attention,
+    # W_UV after) are the same computation: outputs and LSEs agree to rounding.
+    case, q_n, q_r, W_uk, W_uv = _prefill_case(50 + s_q, lens, s_q)
+    _, cache, table, L = _case_arrays(case)
+    o1, l1 = orc.prefill_expanded(q_n, q_r, cache, table, L, W_uk, W_uv, case.scale)
+    q_lat = orc.absorb_q(q_n.reshape(-1, *q_n.shape[2:]), q_r.reshape(-1, *q_r.shape[2:]), W_uk)
+    q_lat = q_lat.reshape(len(lens), s_q, *q_lat.shape[1:])
+    ol, l2 = orc.decode_absorbed(q_lat, cache, table, L, case.scale, True, dv=W_uk.shape[1])
+    o2 = orc.out_uv(ol.reshape(-1, *ol.shape[2:]), W_uv).reshape(o1.shape)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12 and np.max(np.abs(l1 - l2)) <= 1e-12
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 64, 1000])
+def test_prefill_chunked_equals_unchunked(chunk):
+    case, q_n, q_r, W_uk, W_uv = _prefill_case(61, [130, 64, 7], 5)
+    _, cache, table, L = _case_arrays(case)
+    o1, l1 = orc.prefill_expanded(q_n, q_r, cache, table, L, W_uk, W_uv, case.scale)
+    o2, l2 = orc.prefill_chunked(q_n, q_r, cache, table, L, W_uk, W_uv, case.scale, chunk)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12 and np.max(np.abs(l1 - l2)) <= 1e-12
+
+
+def test_prefill_expanded_matches_worked_example():
+    # The page's tiny model (T = 6 prompt tokens, no prefix): path one on a
+    # one-page cache built from its c and k^R equals its expanded attention.
+    w = tiny_mla_weights()
+    q_n, q_r, c, k_r = orc.project(w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["H"], w["NOPE"], w["ROPE"])
+    T = c.shape[0]
+    cache = np.concatenate([c, k_r], axis=1)[None]  # [1 page, T rows, dc + rope]
+    o, _ = orc.prefill_expanded(q_n[None], q_r[None], cache, np.zeros((1, 1), dtype=np.int64), [T],
+                                w["W_uk"], w["W_uv"], 1.0 / math.sqrt(w["NOPE"] + w["ROPE"]))
+    ref = orc.expanded_attention(q_n, q_r, c, k_r, w["W_uk"], w["W_uv"], causal=True)
+    assert np.max(np.abs(o[0] - ref)) <= 1e-12
+
+
+def test_crossover_matches_printed_171():
+    g = load_golden("flop_accounting.txt")
+    assert round(orc.crossover_tokens(10 ** 9)) == g["crossover_new_tokens"]
+    # The cost comparison it stands for: at L = 32768 + 64 the absorbed path
+    # wins for 64 new tokens, at 32768 + 512 the expanded one for 512.
+    assert 64 < orc.crossover_tokens(32768 + 64) < 512
+    g2 = load_golden("crossover.txt")
+    assert round(orc.crossover_tokens(512)) == g2["crossover_L512"]
+    assert round(orc.crossover_tokens(131072)) == g2["crossover_L131072"]
