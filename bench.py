@@ -48,8 +48,12 @@ DEFAULT_WORKLOAD_TEXT = ("batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=
 # --workload name -> seeded input recipe (mla_inputs.config_case index, mtp<s_q>, or the
 # top-k shape: B=64 histories of 16384 tokens, 2048 selected per new token)
 WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8", "topk": "topk",
-             "fp8": "fp8"}
+             "fp8": "fp8", "prefill": "prefill", "extend": "extend"}
 TOPK_SHAPE = dict(B=64, L=16384, topk=2048)
+# Expanded path (prefill / extend), B=1, H=128: a fresh 8K-token prefill, and
+# 512 new tokens after a 32K-token prefix expanded 8192 tokens at a time.
+PREFILL_SHAPES = {"prefill": dict(L=8192, s_q=8192, chunk=8192),
+                  "extend": dict(L=32768 + 512, s_q=512, chunk=8192)}
 
 
 def _log(msg):
@@ -144,6 +148,119 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
             "seconds": secs}
 
 
+def prefill_cpu_baseline(case, budget_s: float) -> dict:
+    """Time the fp64 oracle of the expanded path on a bounded sample: a few
+    heads and the last rows of the new tokens, over the whole sequence."""
+    import numpy as np
+
+    from mla_decode_fwd_amd import accounting as acc
+    from oracle import mla_oracle as orc
+
+    m = case.meta
+    L = int(case.seqlens[0])
+    heads, rows = 2, 32
+    q_n = m["q_nope"][:, -rows:, :heads].double().numpy()
+    q_r = m["q_rope"][:, -rows:, :heads].double().numpy()
+    w_uk = m["w_uk"][:heads].double().numpy()
+    w_uv = m["w_uv"][:heads].double().numpy()
+    table = case.block_table.numpy()
+    npg = (L + 63) // 64
+    cache = case.cache[table[0, :npg]].double().numpy()
+    t = np.arange(npg, dtype=np.int32)[None]
+    secs, n = 0.0, 0
+    while secs < budget_s or n == 0:
+        t0 = time.perf_counter()
+        orc.prefill_expanded(q_n, q_r, cache, t, np.array([L]), w_uk, w_uv, case.scale)
+        secs += time.perf_counter() - t0
+        n += 1
+    flops = n * acc.prefill_flops([L], rows, heads)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # threadpoolctl missing: count the cores we may run on
+        cores = len(os.sched_getaffinity(0))
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} x expanded-path prefill of {heads} of {case.H} heads, the last {rows} of the "
+                      f"{case.s_q} new tokens over all {L} tokens (expansion included), fp64 numpy, {secs:.1f} s",
+            "seconds": secs}
+
+
+def prefill_main(args):
+    """The expanded path (mla_prefill_fwd): expansion of the cached latent into
+    per-head keys and values, causal attention of the new tokens, and the LSE
+    merge when the prefix is expanded in more than one chunk."""
+    import torch
+
+    import mla_decode_fwd_amd as mla
+    from mla_decode_fwd_amd import accounting as acc
+    from mla_inputs import prefill_case
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mla.load_library()
+    shp = PREFILL_SHAPES[args.workload]
+    L, s_q, chunk, H = shp["L"], shp["s_q"], shp["chunk"], 128
+    case = prefill_case([L], s_q, H=H, seed=160)
+    m = case.meta
+    args_dev = [m["q_nope"].to(dev), m["q_rope"].to(dev), case.cache.to(dev), case.block_table.to(dev), [L],
+                m["w_uk"].to(dev), m["w_uv"].to(dev), case.scale]
+    n_chunks = (L + chunk - 1) // chunk
+    ws = torch.empty(mla.prefill_workspace_size(s_q, H, chunk, n_chunks), dtype=torch.uint8, device=dev)
+    o = torch.empty((1, s_q, H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, s_q, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mla.mla_prefill_fwd(*args_dev, chunk_tokens=chunk, workspace=ws, o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = e0.elapsed_time(e1) / args.steps
+    flops = acc.prefill_flops([L], s_q, H)
+    nbytes = acc.prefill_bytes([L], s_q, H)
+    rf = acc.roofline(flops, nbytes, gpu_ms / 1e3)
+    step_rf = acc.roofline(flops, nbytes, ms_per_step / 1e3)
+    what = ("fresh prefill" if L == s_q else f"extend: {s_q} new tokens after a {L - s_q}-token prefix")
+    out = {
+        "metric": "MLA expanded-path prefill TFLOP/s (% bf16 MFMA roofline)",
+        "value": round(step_rf["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"expanded-path MLA {what}, B=1, L={L}, s_q={s_q}, H={H}, k = [c W_UK ; k^R] "
+                               f"(128+64), v = c W_UV (128), latent 512, causal, prefix expanded {chunk} tokens "
+                               "at a time, bf16, 64-token pages in a shuffled pool",
+                   "B": 1, "ctx": L, "s_q": s_q, "H": H, "chunk_tokens": chunk, "chunks": n_chunks,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": rf["bound"], "achieved": round(rf["achieved"], 1), "peak": rf["peak"],
+                     "unit": rf["unit"], "frac": round(rf["frac"], 4), "traffic": None,
+                     "kernel": "mla_prefill_fwd (expand_kernel + attn_kernel" +
+                               (" + merge_kernel, per chunk)" if n_chunks > 1 else ")"),
+                     "call_us": round(gpu_ms * 1e3, 2), "algorithmic_flops": flops, "algorithmic_bytes": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle ...")
+        out["cpu_baseline"] = prefill_cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +277,9 @@ def main():
         print("bench.py measures one GPU: the decode path runs on one MI355X and has no multi-GPU mode "
               "(a data-parallel deployment gives each GPU its own sequences and caches).", file=sys.stderr)
         sys.exit(2)
+    if args.workload in PREFILL_SHAPES:
+        prefill_main(args)
+        return
 
     import torch
 

@@ -73,7 +73,8 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 3 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8). */
+/* Library ABI version, currently 4 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
+   4 the expanded path: mla_select_path, mla_prefill_workspace_size, mla_prefill_fwd). */
 int mla_abi_version(void);
 
 /*
@@ -220,6 +221,54 @@ mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, co
                                 int total_splits, int B, int s_q, int H, int d_qk, int d_v, int page_size,
                                 int max_pages_per_seq, int num_pages, float softmax_scale, int causal,
                                 void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream);
+
+/*
+ * Path choice for s_q new tokens over L keys (L counting them)
+ * ([MLA-推理] section "谁快：看新 token 和缓存 token 的数量" and [AI-MTP] 5.6):
+ * 1 when the expanded path (mla_prefill_fwd) costs fewer FLOPs than the
+ * absorbed one (mla_absorb_q + mla_decode_fwd + mla_out_uv) at the
+ * DeepSeek-V3 shape (d_c 512, d_nope 128, d_rope 64, d_v 128), else 0;
+ * -1 for s_q <= 0 or L < s_q. For L >> s_q the switch is at s_q ≈ 171.
+ */
+int mla_select_path(int s_q, int L);
+
+/*
+ * Workspace bytes of mla_prefill_fwd for chunks of chunk_tokens cached tokens
+ * and at most max_chunks chunks per sequence: the expanded K and V of one
+ * chunk (H * chunk_tokens * (192 + 128) bf16, about 80 KB per token at H =
+ * 128) and the chunk partials (max_chunks * s_q * H * (128 bf16 + 1 fp32)).
+ * 0 for non-positive arguments.
+ */
+size_t mla_prefill_workspace_size(int s_q, int H, int chunk_tokens, int max_chunks);
+
+/*
+ * The expanded path (path one of [MLA-推理] "两条等价的路径") for prefill and
+ * extend: the s_q new tokens of each sequence (the last s_q of its L_b
+ * cached tokens, which the cache already holds) attend causally to all
+ * L_b tokens through per-head keys and values expanded from the latent:
+ *   k_j^h = [c_j W_UK[h] ; k^R_j],  v_j^h = c_j W_UV[h]
+ *   s     = softmax_scale * ([q^N ; q^R] . k_j^h),  o^h = softmax(s) V^h
+ * returning per-head outputs o [B, s_q, H, 128] (before W_o) and the
+ * natural-log LSE [B, s_q, H]. The cached tokens are expanded
+ * chunk_tokens at a time and the chunk results merged by their LSE
+ * ([MLA-推理] "谁快": SGLang's MHA_CHUNKED_KV, threshold 8192 by default).
+ *
+ *   q_nope [B, s_q, H, 128], q_rope [B, s_q, H, 64] (rotated), bf16.
+ *   kv_cache [num_pages, 64, 576] bf16 rows [c (512) ; k^R (64)];
+ *   block_table [B, max_pages_per_seq] int32 (device);
+ *   seqlens_host [B] (HOST) L_b in [s_q, 64 * max_pages_per_seq].
+ *   w_uk, w_uv [H, 512, 128] bf16 (latent rows), as for mla_absorb_q/out_uv.
+ *   chunk_tokens >= 1; at most 64 chunks per sequence (else UNSUPPORTED).
+ *   H 1..128. softmax_scale finite and > 0 (1/sqrt(192) for DeepSeek-V3).
+ *   workspace of at least mla_prefill_workspace_size(s_q, H, chunk_tokens,
+ *   max over b of ceil(L_b / chunk_tokens)) bytes, contents ignored.
+ * Launches two kernels per chunk and one merge per sequence on stream; the
+ * host loop reads seqlens_host only.
+ */
+mla_status_t mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* kv_cache, const int32_t* block_table,
+                             const int32_t* seqlens_host, int B, int s_q, int H, int max_pages_per_seq, int num_pages,
+                             const void* w_uk, const void* w_uv, int chunk_tokens, float softmax_scale,
+                             void* workspace, size_t workspace_bytes, void* o, float* lse, void* stream);
 
 /*
  * LSE merge of split-KV partial results ([MLA-推理] sections

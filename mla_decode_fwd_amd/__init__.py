@@ -29,6 +29,7 @@ __all__ = [
 D_QK = 576
 D_V = 512
 PAGE_SIZE = 64
+MAX_DECODE_SQ = 16  # query tokens per sequence the decode kernel takes
 MAX_SPLITS = 64
 
 MLA_BF16 = 0
@@ -72,6 +73,9 @@ def load_library():
         "mla_decode_fwd": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, Z, P, P, P], I),
         "mla_sparse_decode_fwd": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P, Z, P, P, P], I),
         "mla_decode_fwd_fp8": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, Z, P, P, P], I),
+        "mla_select_path": ([I, I], I),
+        "mla_prefill_workspace_size": ([I, I, I, I], Z),
+        "mla_prefill_fwd": ([P, P, P, P, P, I, I, I, I, I, P, P, I, F, P, Z, P, P, P], I),
         "mla_splitkv_combine": ([P, P, P, I, I, I, I, I, I, P, P, P], I),
         "mla_absorb_q": ([P, P, P, I, I, I, I, I, I, P, P], I),
         "mla_out_uv": ([P, P, I, I, I, I, I, P, P], I),
@@ -447,3 +451,91 @@ def mla_out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tens
     st = load_library().mla_out_uv(_ptr(o_lat), _ptr(w_uv), N, H, dc, dv, _DTYPES[dtype], _ptr(out), _stream())
     _check("mla_out_uv", st)
     return out
+
+
+# ---------------------------------------------------------------------------
+# The expanded path (prefill / extend) and the choice between the two paths.
+# ---------------------------------------------------------------------------
+
+PREFILL_CHUNK = 8192  # cached tokens expanded at a time: the prefix-length threshold [MLA-推理] "谁快" gives
+
+
+def select_path(s_q: int, L: int) -> str:
+    """"expanded" or "absorbed": the cheaper path in FLOPs (mla_select_path)."""
+    r = load_library().mla_select_path(int(s_q), int(L))
+    if r < 0:
+        raise ValueError("need 1 <= s_q <= L")
+    return "expanded" if r == 1 else "absorbed"
+
+
+def prefill_workspace_size(s_q: int, H: int, chunk_tokens: int, max_chunks: int) -> int:
+    return int(load_library().mla_prefill_workspace_size(int(s_q), int(H), int(chunk_tokens), int(max_chunks)))
+
+
+def mla_prefill_fwd(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                    seqlens_host: Sequence[int], w_uk: torch.Tensor, w_uv: torch.Tensor, softmax_scale: float,
+                    chunk_tokens: int = PREFILL_CHUNK, workspace: Optional[torch.Tensor] = None,
+                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Expanded path (mla_prefill_fwd): per-head outputs o [B,s_q,H,128] bf16 and lse [B,s_q,H] fp32 of
+    the s_q new tokens (the last s_q of each sequence's cached tokens), the cache expanded chunk_tokens
+    at a time with an LSE merge across chunks."""
+    dev = q_nope.device
+    if q_nope.dim() != 4 or q_rope.dim() != 4 or tuple(q_rope.shape[:3]) != tuple(q_nope.shape[:3]):
+        raise ValueError("expected q_nope [B,s_q,H,128] and q_rope [B,s_q,H,64]")
+    B, s_q, H, _ = q_nope.shape
+    for t, name in ((q_nope, "q_nope"), (q_rope, "q_rope"), (kv_cache, "kv_cache"), (w_uk, "w_uk"), (w_uv, "w_uv")):
+        _need(t, name, dtype=torch.bfloat16, device=dev)
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    if q_nope.shape[3] != 128 or q_rope.shape[3] != 64:
+        raise ValueError("expanded path needs d_nope = d_v = 128 and d_rope = 64")
+    for w, name in ((w_uk, "w_uk"), (w_uv, "w_uv")):
+        if tuple(w.shape) != (H, 512, 128):
+            raise ValueError(f"{name} must be [H,512,128], got {tuple(w.shape)}")
+    if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_SIZE, 576):
+        raise ValueError("kv_cache must be [num_pages, 64, 576]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    L = np.ascontiguousarray(np.asarray(seqlens_host, dtype=np.int32))
+    if L.shape != (B,):
+        raise ValueError("seqlens_host must have B entries")
+    max_chunks = int(max(1, ((L.astype(np.int64) + chunk_tokens - 1) // chunk_tokens).max()))
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(s_q, H, chunk_tokens, max_chunks), dtype=torch.uint8,
+                                device=dev)
+    o = torch.empty((B, s_q, H, 128), dtype=torch.bfloat16, device=dev) if o is None else o
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(o, "o", dtype=torch.bfloat16, device=dev)
+    _need(lse, "lse", dtype=torch.float32, device=dev)
+    if tuple(o.shape) != (B, s_q, H, 128) or tuple(lse.shape) != (B, s_q, H):
+        raise ValueError("o must be [B,s_q,H,128] and lse [B,s_q,H]")
+    st = load_library().mla_prefill_fwd(_ptr(q_nope), _ptr(q_rope), _ptr(kv_cache), _ptr(block_table),
+                                        L.ctypes.data_as(ctypes.c_void_p), B, s_q, H, int(block_table.shape[1]),
+                                        int(kv_cache.shape[0]), _ptr(w_uk), _ptr(w_uv), int(chunk_tokens),
+                                        float(softmax_scale), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse), _stream())
+    _check("mla_prefill_fwd", st)
+    return o, lse
+
+
+def mla_attention_fwd(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                      seqlens: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, softmax_scale: float,
+                      path: str = "auto", chunk_tokens: int = PREFILL_CHUNK):
+    """Attention of the s_q new tokens of each sequence by either path, per-head outputs
+    o [B,s_q,H,128] and lse [B,s_q,H]. path "auto" asks mla_select_path with the longest sequence;
+    "absorbed" runs mla_absorb_q, mla_decode_fwd (causal, split by mla_decode_plan) and mla_out_uv
+    (s_q <= 16); "expanded" runs mla_prefill_fwd. Both compute the same attention ([MLA-推理]
+    "两条等价的路径"); "auto" takes the expanded one also when s_q exceeds the decode kernel's 16."""
+    B, s_q, H, _ = q_nope.shape
+    L = [int(x) for x in seqlens.cpu().tolist()]
+    if path == "auto":
+        path = select_path(s_q, max(L)) if s_q <= MAX_DECODE_SQ else "expanded"
+    if path == "expanded":
+        return mla_prefill_fwd(q_nope, q_rope, kv_cache, block_table, L, w_uk, w_uv, softmax_scale, chunk_tokens)
+    if path != "absorbed":
+        raise ValueError(f"unknown path {path}")
+    q_lat = mla_absorb_q(q_nope.reshape(B * s_q, H, -1), q_rope.reshape(B * s_q, H, -1), w_uk)
+    p = decode_plan(L, s_q, H)
+    kw = dict(split_offsets=p.device_offsets(q_nope.device), total_splits=p.total_splits) if p.any_split else {}
+    o_lat, lse = mla_decode_fwd(q_lat.view(B, s_q, H, -1), kv_cache, block_table, seqlens, softmax_scale, True, **kw)
+    o = mla_out_uv(o_lat.view(B * s_q, H, -1), w_uv)
+    return o.view(B, s_q, H, -1), lse

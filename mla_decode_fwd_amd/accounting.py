@@ -152,3 +152,23 @@ def roofline(flops: float, nbytes: float, seconds: float,
     return dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
                 ai=ai, tflops=tflops, gbs=gbs,
                 frac_mfma=tflops / (peak_flops / 1e12), frac_hbm=gbs / (peak_bw / 1e9))
+
+
+def prefill_flops(seqlens: Iterable[int], s_q: int, H: int, nope=128, rope=64, dv=128, dc=512) -> float:
+    """Expanded path over a batch: expansion of every cached token plus the
+    causal (query, key) pairs of the s_q new tokens of each sequence."""
+    return float(sum(path_flops(s_q, int(L), H, nope, rope, dv, dc)[0] for L in seqlens))
+
+
+def prefill_bytes(seqlens: Iterable[int], s_q: int, H: int, nope=128, rope=64, dv=128, dc=512,
+                  elem_bytes: int = 2) -> float:
+    """Compulsory HBM bytes of the expanded path: the latent rows, both weight
+    stacks and the queries read once, o and the LSE written once."""
+    B = 0
+    total = 0.0
+    for L in seqlens:
+        B += 1
+        total += int(L) * (dc + rope) * elem_bytes
+    total += 2 * H * dc * nope * elem_bytes if nope == dv else H * dc * (nope + dv) * elem_bytes
+    total += B * s_q * H * ((nope + rope) * elem_bytes + dv * elem_bytes + 4)
+    return total

@@ -45,7 +45,7 @@ const char* mla_status_string(mla_status_t status) {
   return "unknown status";
 }
 
-int mla_abi_version(void) { return 3; }
+int mla_abi_version(void) { return 4; }
 
 size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
   return workspace_size(total_splits, s_q, H);
@@ -194,6 +194,85 @@ mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, co
   return run_decode(q_lat, kv_cache_e4m3, row_scales, block_table, seqlens, nullptr, 0, split_offsets, total_splits,
                     B, s_q, H, d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, MLA_BF16,
                     workspace, workspace_bytes, o_lat, lse, stream);
+}
+
+// ---- expanded path (prefill / extend) ----
+
+namespace {
+constexpr int kPrefillMaxChunks = 64;
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t prefill_kv_bytes(int H, int chunk) { return align256((size_t)H * chunk * (192 + 128) * 2); }
+}  // namespace
+
+size_t mla_prefill_workspace_size(int s_q, int H, int chunk_tokens, int max_chunks) {
+  if (s_q <= 0 || H <= 0 || chunk_tokens <= 0 || max_chunks <= 0) return 0;
+  const size_t parts = (size_t)max_chunks * s_q * H;
+  return prefill_kv_bytes(H, chunk_tokens) + align256(parts * 128 * 2) + align256(parts * 4);
+}
+
+int mla_select_path(int s_q, int L) {
+  if (s_q <= 0 || L < s_q) return -1;
+  // FLOPs of the two paths for s_q new tokens over L keys at the DeepSeek-V3
+  // shape (H cancels): expansion per key e and absorption per query b are
+  // both d_c (d_nope + d_v) multiply-adds; per (query, key) pair the
+  // absorbed path costs 2 d_c + d_rope and the expanded d_nope + d_rope + d_v.
+  const double e = 512.0 * 256.0, b = e, p_abs = 1088.0, p_exp = 320.0;
+  const double pairs = (double)s_q * L - (double)s_q * (s_q - 1) / 2.0;
+  const double absorbed = s_q * b + pairs * p_abs, expanded = L * e + pairs * p_exp;
+  return expanded < absorbed ? 1 : 0;
+}
+
+mla_status_t mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* kv_cache, const int32_t* block_table,
+                             const int32_t* seqlens_host, int B, int s_q, int H, int max_pages_per_seq, int num_pages,
+                             const void* w_uk, const void* w_uv, int chunk_tokens, float softmax_scale,
+                             void* workspace, size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (!q_nope || !q_rope || !kv_cache || !block_table || !seqlens_host || !w_uk || !w_uv || !o || !lse)
+    return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0 || H > kMaxHeads || max_pages_per_seq <= 0 || num_pages <= 0 || chunk_tokens <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  int max_chunks = 1;
+  for (int b = 0; b < B; ++b) {
+    const long long L = seqlens_host[b];
+    if (L < s_q || L > (long long)max_pages_per_seq * MLA_PAGE_SIZE) return MLA_ERR_INVALID_ARG;
+    const long long n = (L + chunk_tokens - 1) / chunk_tokens;
+    if (n > kPrefillMaxChunks) return MLA_ERR_UNSUPPORTED;
+    if (n > max_chunks) max_chunks = (int)n;
+  }
+  const size_t need = mla_prefill_workspace_size(s_q, H, chunk_tokens, max_chunks);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* K = ws;
+  void* V = ws + (size_t)H * chunk_tokens * 192 * 2;
+  const size_t parts = (size_t)max_chunks * s_q * H;
+  char* o_part = ws + prefill_kv_bytes(H, chunk_tokens);
+  float* lse_part = reinterpret_cast<float*>(o_part + align256(parts * 128 * 2));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t q_rows = (size_t)s_q * H;
+  for (int b = 0; b < B; ++b) {
+    const int L = seqlens_host[b];
+    const int n_chunks = (L + chunk_tokens - 1) / chunk_tokens;
+    const char* qn = static_cast<const char*>(q_nope) + (size_t)b * q_rows * 128 * 2;
+    const char* qr = static_cast<const char*>(q_rope) + (size_t)b * q_rows * 64 * 2;
+    char* ob = static_cast<char*>(o) + (size_t)b * q_rows * 128 * 2;
+    float* lb = lse + (size_t)b * q_rows;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int t0 = c * chunk_tokens;
+      const int n = L - t0 < chunk_tokens ? L - t0 : chunk_tokens;
+      hipError_t e = mla::launch_expand(kv_cache, block_table + (size_t)b * max_pages_per_seq, t0, n, num_pages, w_uk,
+                                        w_uv, H, K, V, chunk_tokens, st);
+      if (e != hipSuccess) return MLA_ERR_HIP;
+      void* od = n_chunks == 1 ? static_cast<void*>(ob) : static_cast<void*>(o_part + (size_t)c * q_rows * 128 * 2);
+      float* ld = n_chunks == 1 ? lb : lse_part + (size_t)c * q_rows;
+      e = mla::launch_prefill_attn(qn, qr, s_q, H, K, V, n, chunk_tokens, t0, L - s_q, 1, softmax_scale, od, ld, st);
+      if (e != hipSuccess) return MLA_ERR_HIP;
+    }
+    if (n_chunks > 1) {
+      if (mla::launch_prefill_merge(o_part, lse_part, n_chunks, (int)q_rows, ob, lb, st) != hipSuccess)
+        return MLA_ERR_HIP;
+    }
+  }
+  return MLA_OK;
 }
 
 mla_status_t mla_splitkv_combine(const void* o_part, const float* lse_part,

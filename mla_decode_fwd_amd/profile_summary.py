@@ -1,19 +1,20 @@
 """Summarise rocprofv3 CSV output of bench.py into a short markdown file.
 
-Inputs are three rocprofv3 output folders made from bench.py:
+Inputs are rocprofv3 output folders made from bench.py:
   --trace  a `--kernel-trace --stats --output-format csv` run (kernel durations),
   --fetch  a `--pmc FETCH_SIZE --output-format csv` run with `--copy-mb N`,
   --write  a `--pmc WRITE_SIZE --output-format csv` run with `--copy-mb N`.
+The two counter runs are optional (both or neither).
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch. They are scaled
 by what the same counter reads for the plain device copy of N MiB that
 `bench.py --copy-mb N` launches (`__amd_rocclr_copyBuffer`, N MiB read and N
 MiB written): factor = N MiB / counter reading. The summary records the
-SHA-256 of the decode kernel's source, so a reader (bench.py) can tell when
+SHA-256 of the dominant kernel's sources, so a reader (bench.py) can tell when
 the kernel has changed since the counters were taken.
 
-usage: python -m mla_decode_fwd_amd.profile_summary --trace D1 --fetch D2 --write D3
-           --copy-mb N --command "..." --out profiles/<kernel>_<workload>.md
+usage: python -m mla_decode_fwd_amd.profile_summary --trace D1 [--fetch D2 --write D3 --copy-mb N]
+           --command "..." [--kernel NAME --sources a.hip,b.h] --out profiles/<kernel>_<workload>.md
 """
 from __future__ import annotations
 
@@ -30,9 +31,9 @@ DECODE_KERNEL = "mla_decode_bf16_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def decode_source_sha256() -> str:
+def decode_source_sha256(sources=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -45,9 +46,30 @@ def _one(folder: str, pattern: str) -> str:
     return hits[0]
 
 
+def _demangle_nested(name: str) -> str:
+    """'mla::(anonymous namespace)::f' from an Itanium nested name '_ZN3mla12_GLOBAL__N_11fE...'
+    (the trace leaves some kernel names mangled)."""
+    if not name.startswith("_ZN"):
+        return name
+    parts, i = [], 3
+    while i < len(name) and name[i].isdigit():
+        j = i
+        while name[j].isdigit():
+            j += 1
+        n = int(name[i:j])
+        part = name[j:j + n]
+        parts.append("(anonymous namespace)" if part.startswith("_GLOBAL__N") else part)
+        i = j + n
+    return "::".join(parts) + "(...)" if parts else name
+
+
 def _short(name: str) -> str:
-    base = name.replace("(anonymous namespace)", "").split("(")[0]
+    base = _demangle_nested(name).replace("(anonymous namespace)", "").split("(")[0]
     return base.split("::")[-1].replace("void ", "")
+
+
+def _ours(name: str) -> bool:
+    return _demangle_nested(name).lstrip("void ").startswith("mla::")
 
 
 def kernel_stats(folder: str):
@@ -76,35 +98,41 @@ def counter_medians(folder: str, counter: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-mb", type=int, required=True)
+    ap.add_argument("--fetch", default=None)
+    ap.add_argument("--write", default=None)
+    ap.add_argument("--copy-mb", type=int, default=0)
     ap.add_argument("--command", required=True, help="the bench command line of the kernel-trace run")
     ap.add_argument("--pmc-command", default=None,
                     help="the bench command line of the counter runs, without --copy-mb (default: --command)")
     ap.add_argument("--workload", default="batched decode B=64 x ctx 4096, s_q=1, H=128, bf16")
+    ap.add_argument("--kernel", default=DECODE_KERNEL, help="the dominant kernel (a substring of its name)")
+    ap.add_argument("--sources", default=",".join(DECODE_SOURCES),
+                    help="its sources, relative to the package, for the hash")
     ap.add_argument("--algorithmic-bytes", type=float, default=None)
     ap.add_argument("--bench-output", default=None,
                     help="stdout of the kernel-trace run (bench.py's JSON line), for the event-vs-trace check")
     ap.add_argument("--out", required=True)
     args = ap.parse_args()
+    if (args.fetch is None) != (args.write is None) or (args.fetch and args.copy_mb <= 0):
+        raise SystemExit("--fetch and --write go together, with --copy-mb")
+    sources = tuple(x for x in args.sources.split(",") if x)
 
     stats = kernel_stats(args.trace)
-    fetch, copy_fetch = counter_medians(args.fetch, "FETCH_SIZE")
-    write, copy_write = counter_medians(args.write, "WRITE_SIZE")
     pmc_cmd = args.pmc_command or args.command
-    copy_kib = args.copy_mb * 1024.0
-    f_fetch = copy_kib / copy_fetch
-    f_write = copy_kib / copy_write
 
-    lines = [f"# rocprofv3 summary: {DECODE_KERNEL}, {args.workload}", ""]
+    lines = [f"# rocprofv3 summary: {args.kernel}, {args.workload}", ""]
     lines += ["Commands (from the repository root, on one MI355X):", "", "```"]
-    lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d <trace> -o run -- {args.command}",
-              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}",
-              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}",
-              "python -m mla_decode_fwd_amd.profile_summary --trace <trace> --fetch <fetch> --write <write> "
-              f"--copy-mb {args.copy_mb} --command '{args.command}' --pmc-command '{pmc_cmd}' --out <this file>",
-              "```", ""]
+    redirect = " > <stdout>" if args.bench_output else ""
+    lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d <trace> -o run -- {args.command}{redirect}"]
+    summary = (f"python -m mla_decode_fwd_amd.profile_summary --trace <trace> --command '{args.command}' "
+               f"--kernel {args.kernel} --sources {args.sources} --workload '{args.workload}'")
+    if args.bench_output:
+        summary += " --bench-output <stdout>"
+    if args.fetch:
+        lines += [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}",
+                  f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}"]
+        summary += f" --fetch <fetch> --write <write> --copy-mb {args.copy_mb} --pmc-command '{pmc_cmd}'"
+    lines += [summary + " --out <this file>", "```", ""]
     lines += ["## Kernel durations (kernel trace)", "",
               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
@@ -115,30 +143,47 @@ def main():
         for line in open(args.bench_output, encoding="utf-8", errors="replace"):
             if line.startswith("{") and '"roofline"' in line:
                 rec = json.loads(line)
-        if rec:
+        if rec and "kernel_us" in rec["roofline"]:
             ev_us = rec["roofline"]["kernel_us"]
-            tr_us = next(avg for name, _, avg, _, _, _ in stats if DECODE_KERNEL in name) / 1e3
-            lines += ["", f"Cross-check in the same run: bench.py's HIP events give the decode kernel {ev_us:.2f} us "
+            tr_us = next(avg for name, _, avg, _, _, _ in stats if args.kernel in _demangle_nested(name)) / 1e3
+            lines += ["", f"Cross-check in the same run: bench.py's HIP events give {args.kernel} {ev_us:.2f} us "
                           f"per launch, the kernel trace {tr_us:.2f} us ({100 * (ev_us / tr_us - 1):+.1f}%)."]
-    lines += ["", "## HBM traffic per dispatch (memory counters)", "",
-              f"Copy calibration: a device copy of {args.copy_mb} MiB reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
-              f"WRITE_SIZE = {copy_write:.0f} KiB, so the counters are scaled by {f_fetch:.3f} (fetch) and "
-              f"{f_write:.3f} (write).", "",
-              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | total MB |",
-              "|---|---|---|---|---|---|"]
-    decode_total = None
-    for name in sorted(n for n in set(fetch) | set(write) if n.lstrip("void ").startswith("mla::")):
-        fk, wk = fetch.get(name, 0.0), write.get(name, 0.0)
-        rb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-        lines.append(f"| {_short(name)} | {fk:.0f} | {wk:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
-        if DECODE_KERNEL in name:
-            decode_total = rb + wb
+        elif rec and "call_us" in rec["roofline"]:
+            # One library call launches several kernels: compare the events'
+            # time per call with the traced kernel time per call.
+            n_calls = rec["steps"] + rec["warmup"]
+            tr_us = sum(avg * calls for name, calls, avg, _, _, _ in stats if _ours(name)) / n_calls / 1e3
+            ev_us = rec["roofline"]["call_us"]
+            lines += ["", f"Cross-check in the same run: bench.py's HIP events give {ev_us:.2f} us per library call "
+                          f"(back to back), the kernel trace {tr_us:.2f} us of kernel time per call over "
+                          f"{n_calls} calls ({100 * (ev_us / tr_us - 1):+.1f}%)."]
+    total = None
+    if args.fetch:
+        fetch, copy_fetch = counter_medians(args.fetch, "FETCH_SIZE")
+        write, copy_write = counter_medians(args.write, "WRITE_SIZE")
+        copy_kib = args.copy_mb * 1024.0
+        f_fetch = copy_kib / copy_fetch
+        f_write = copy_kib / copy_write
+        lines += ["", "## HBM traffic per dispatch (memory counters)", "",
+                  f"Copy calibration: a device copy of {args.copy_mb} MiB reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
+                  f"WRITE_SIZE = {copy_write:.0f} KiB, so the counters are scaled by {f_fetch:.3f} (fetch) and "
+                  f"{f_write:.3f} (write).", "",
+                  "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | total MB |",
+                  "|---|---|---|---|---|---|"]
+        for name in sorted(n for n in set(fetch) | set(write) if _ours(n)):
+            fk, wk = fetch.get(name, 0.0), write.get(name, 0.0)
+            rb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
+            lines.append(f"| {_short(name)} | {fk:.0f} | {wk:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                         f"{(rb + wb) / 1e6:.1f} |")
+            if args.kernel in _demangle_nested(name):
+                total = rb + wb
     lines += [""]
     if args.algorithmic_bytes:
-        lines += [f"Algorithmic bytes per decode launch: {args.algorithmic_bytes / 1e6:.1f} MB.", ""]
-    lines += ["Machine-readable (read by bench.py; valid only while the source hash matches):", "",
-              f"traffic_bytes_per_launch: {decode_total:.0f}",
-              f"kernel_source_sha256: {decode_source_sha256()}", ""]
+        lines += [f"Algorithmic bytes per launch of {args.kernel}: {args.algorithmic_bytes / 1e6:.1f} MB.", ""]
+    lines += ["Machine-readable (read by bench.py; valid only while the source hash matches):", ""]
+    if total is not None:
+        lines += [f"traffic_bytes_per_launch: {total:.0f}"]
+    lines += [f"kernel_source_sha256: {decode_source_sha256(sources)}", ""]
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         f.write("\n".join(lines))

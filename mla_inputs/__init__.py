@@ -84,12 +84,14 @@ def make_decode_case(
     extra_table_cols: int = 1,
     d_qk: int = D_QK,
     name: str = "",
+    draw_q: bool = True,
 ) -> DecodeCase:
     """Draw one paged decode problem.
 
     Draw order from ``default_rng(seed)``: page permutation, cache normals,
     query normals, then (if ``outlier_frac``) the outlier rows per sequence.
-    ``causal`` defaults to ``s_q > 1``.
+    ``causal`` defaults to ``s_q > 1``. ``draw_q=False`` skips the query
+    draw (q_lat is then empty), for callers that draw their own queries.
     """
     seqlens = [int(x) for x in seqlens]
     B = len(seqlens)
@@ -111,7 +113,8 @@ def make_decode_case(
         table[b, pages[b] :] = spare_ids[b % len(spare_ids)]
         pos += pages[b]
     cache32 = rng.standard_normal((num_pages, PAGE, d_qk), dtype=np.float32)
-    q32 = rng.standard_normal((B, s_q, H, d_qk), dtype=np.float32) * np.float32(q_scale)
+    q32 = (rng.standard_normal((B, s_q, H, d_qk), dtype=np.float32) * np.float32(q_scale) if draw_q
+           else np.zeros((B, s_q, H, 0), dtype=np.float32))
     cache = _round_to(cache32, dtype)
     del cache32
     if outlier_frac > 0:
@@ -258,6 +261,26 @@ def fp8_case(seqlens: Sequence[int], s_q: int = 1, seed: int = 100, H: int = 128
     scales[~owned] = float("nan")
     case.meta["cache_fp8"] = codes.contiguous()
     case.meta["row_scales"] = scales.contiguous()
+    return case
+
+
+def prefill_case(seqlens: Sequence[int], s_q: int, H: int = 128, seed: int = 130, nope: int = 128,
+                 rope: int = 64, dv: int = 128) -> DecodeCase:
+    """Inputs of the expanded (prefill / extend) path: the paged latent cache of
+    ``make_decode_case`` (rows [c ; k^R] ~ N(0,1), bf16), per-head queries
+    q^N [B,s_q,H,nope] and rotated q^R [B,s_q,H,rope] ~ N(0,1), and W_UK
+    [H,512,nope], W_UV [H,512,dv] ~ N(0, 1/512), all bf16 (meta["q_nope"],
+    meta["q_rope"], meta["w_uk"], meta["w_uv"]). Expanded keys and values
+    are then ~ N(0,1) and the scores, at scale 1/sqrt(nope+rope), ~ N(0,1)."""
+    case = make_decode_case(seqlens, s_q=s_q, H=H, seed=seed, scale=1.0 / math.sqrt(nope + rope),
+                            name=f"prefill B={len(seqlens)} s_q={s_q} H={H}", draw_q=False)
+    rng = np.random.default_rng(seed + 11)
+    B = len(seqlens)
+    case.meta["q_nope"] = _round_to(rng.standard_normal((B, s_q, H, nope), dtype=np.float32), torch.bfloat16)
+    case.meta["q_rope"] = _round_to(rng.standard_normal((B, s_q, H, rope), dtype=np.float32), torch.bfloat16)
+    w = np.float32(1.0 / math.sqrt(512))
+    case.meta["w_uk"] = _round_to(rng.standard_normal((H, 512, nope), dtype=np.float32) * w, torch.bfloat16)
+    case.meta["w_uv"] = _round_to(rng.standard_normal((H, 512, dv), dtype=np.float32) * w, torch.bfloat16)
     return case
 
 

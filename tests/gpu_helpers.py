@@ -152,3 +152,13 @@ def run_fp8(case, plan="auto", num_cus=256, dev="cuda"):
                                     d["block_table"], d["seqlens"], case.scale, case.causal, **kw)
     torch.cuda.synchronize()
     return o, lse
+
+
+def oracle_prefill(case, chunk=None):
+    """Oracle of the expanded path (prefill_expanded, or prefill_chunked when chunk is given)."""
+    m = case.meta
+    args = (to_np(m["q_nope"]), to_np(m["q_rope"]), to_np(case.cache), case.block_table.numpy(),
+            case.seqlens.numpy(), to_np(m["w_uk"]), to_np(m["w_uv"]), case.scale)
+    if chunk is None:
+        return orc.prefill_expanded(*args)
+    return orc.prefill_chunked(*args, chunk)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 3
+    assert mla.abi_version() == 4
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -188,3 +188,38 @@ def test_fp8_decode_validation(lib):
     assert call(scale=-1.0) == INVALID
     assert call(so=FAKE, total=4, ws=None, wsb=0) == WORKSPACE
     assert call(o=None) == INVALID
+
+
+def test_select_path_matches_the_printed_choices(lib):
+    # [MLA-推理] "谁快": decode over 8K -> absorbed, prefill 8K -> expanded,
+    # 64 new tokens after 32K -> absorbed, 512 after 32K -> expanded.
+    assert mla.select_path(1, 8192) == "absorbed"
+    assert mla.select_path(8192, 8192) == "expanded"
+    assert mla.select_path(64, 32768 + 64) == "absorbed"
+    assert mla.select_path(512, 32768 + 512) == "expanded"
+    assert lib.mla_select_path(0, 10) == -1 and lib.mla_select_path(5, 4) == -1
+
+
+def test_prefill_validation(lib):
+    L = np.array([100, 200], dtype=np.int32)
+    c = L.ctypes.data_as(ctypes.c_void_p)
+
+    def call(**kw):
+        a = dict(qn=FAKE, qr=FAKE, kv=FAKE, bt=FAKE, L=c, B=2, s_q=4, H=16, maxp=4, npages=8, wuk=FAKE, wuv=FAKE,
+                 chunk=64, scale=0.07, ws=FAKE, wsb=1 << 40, o=FAKE, lse=FAKE)
+        a.update(kw)
+        return lib.mla_prefill_fwd(a["qn"], a["qr"], a["kv"], a["bt"], a["L"], a["B"], a["s_q"], a["H"], a["maxp"],
+                                   a["npages"], a["wuk"], a["wuv"], a["chunk"], a["scale"], a["ws"], a["wsb"],
+                                   a["o"], a["lse"], None)
+    assert call(qn=None) == INVALID
+    assert call(L=None) == INVALID
+    assert call(chunk=0) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(H=129) == INVALID
+    assert call(s_q=101) == INVALID          # L_0 = 100 < s_q
+    assert call(maxp=1) == INVALID           # 200 tokens > 64 * 1
+    assert call(chunk=3) == UNSUPPORTED      # 67 chunks > 64
+    assert call(ws=None) == WORKSPACE
+    need = mla.prefill_workspace_size(4, 16, 64, 4)
+    assert call(wsb=need - 1) == WORKSPACE
+    assert mla.prefill_workspace_size(0, 16, 64, 4) == 0

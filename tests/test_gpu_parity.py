@@ -459,3 +459,64 @@ def test_fp8_partials_then_combine_matches_one_call():
     torch.cuda.synchronize()
     multi = torch.from_numpy(p.num_splits > 1)
     assert torch.equal(o1[multi], o2[multi]) and torch.equal(l1[multi], l2[multi])
+
+
+# ---------------------------------------------------------------------------
+# Expanded path (prefill / extend), chunked prefix, and the path choice
+# ---------------------------------------------------------------------------
+
+# The expanded path materialises K and V in bf16 (as any implementation of
+# that path does), so each score carries the rounding of its 128 expanded key
+# elements (relative 2^-9, uniform): with unit-variance q and k and scale
+# 1/sqrt(192) the score error has standard deviation ~2^-9/sqrt(3) * sqrt(128/192)
+# ~ 9e-4, and an LSE inherits at most the largest of its scores' errors. The
+# bound 1e-2 is ~10 of those deviations, far below a wrong key or scale (an
+# error of order 1). Outputs keep rel-L2 5e-3 and max-abs 2e-2 relative to
+# their scale.
+PREFILL_LSE_TOL = 1e-2
+
+
+def _prefill_compare(o, lse, o_ref, l_ref, label):
+    og, lg = to_np(o), to_np(lse)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), label
+    rel = np.linalg.norm(og - o_ref) / np.linalg.norm(o_ref)
+    mabs = np.max(np.abs(og - o_ref))
+    lerr = np.max(np.abs(lg - l_ref))
+    print(f"[parity] {label} rel_l2={rel:.3e} max_abs={mabs:.3e} lse={lerr:.3e}", flush=True)
+    assert rel <= 5e-3 and mabs <= 2e-2 * max(1.0, np.max(np.abs(o_ref))) and lerr <= PREFILL_LSE_TOL, \
+        (label, rel, mabs, lerr)
+
+
+@pytest.mark.parametrize("lens,s_q,H,chunk", [([300, 1000], 1, 16, 8192), ([300, 1000], 5, 16, 128),
+                                              ([1000, 77], 77, 16, 100), ([2000], 300, 32, 512),
+                                              ([640, 129], 129, 128, 256)])
+def test_prefill_expanded(lens, s_q, H, chunk):
+    from gpu_helpers import oracle_prefill
+    from mla_inputs import prefill_case
+    case = prefill_case(lens, s_q, H=H, seed=140 + s_q)
+    m = case.meta
+    d = to_device(case)
+    o, lse = mla.mla_prefill_fwd(m["q_nope"].cuda(), m["q_rope"].cuda(), d["kv_cache"], d["block_table"], lens,
+                                 m["w_uk"].cuda(), m["w_uv"].cuda(), case.scale, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_prefill(case)
+    _prefill_compare(o, lse, o_ref, l_ref, f"{case.name} lens={lens} chunk={chunk}")
+
+
+def test_two_paths_agree_and_auto_choice():
+    # Both paths on one extend batch (s_q = 8 new tokens): each against the
+    # oracle of the expanded path, and "auto" picks the absorbed one here and
+    # the expanded one for 300 new tokens (the crossover is ~171).
+    from gpu_helpers import oracle_prefill
+    from mla_inputs import prefill_case
+    case = prefill_case([1000, 300], 8, H=128, seed=150)
+    m = case.meta
+    d = to_device(case)
+    args = (m["q_nope"].cuda(), m["q_rope"].cuda(), d["kv_cache"], d["block_table"], d["seqlens"],
+            m["w_uk"].cuda(), m["w_uv"].cuda(), case.scale)
+    o_ref, l_ref = oracle_prefill(case)
+    for path in ("absorbed", "expanded"):
+        o, lse = mla.mla_attention_fwd(*args, path=path, chunk_tokens=512)
+        torch.cuda.synchronize()
+        _prefill_compare(o, lse, o_ref, l_ref, f"extend s_q=8 via {path}")
+    assert mla.select_path(8, 1000) == "absorbed" and mla.select_path(300, 2000) == "expanded"
