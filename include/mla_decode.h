@@ -234,9 +234,11 @@ int mla_select_path(int s_q, int L);
 
 /*
  * Workspace bytes of mla_prefill_fwd for chunks of chunk_tokens cached tokens
- * and at most max_chunks chunks per sequence: the expanded K and V of one
- * chunk (H * chunk_tokens * (192 + 128) bf16, about 80 KB per token at H =
- * 128) and the chunk partials (max_chunks * s_q * H * (128 bf16 + 1 fp32)).
+ * and at most max_chunks chunks per sequence: the expanded keys and values
+ * of one chunk (H * chunk_tokens * (128 + 128) bf16, 64 KB per token at
+ * H = 128), the chunk's RoPE keys, which every head shares
+ * (chunk_tokens * 64 bf16), and the chunk partials
+ * (max_chunks * s_q * H * (128 bf16 + 1 fp32)).
  * 0 for non-positive arguments.
  */
 size_t mla_prefill_workspace_size(int s_q, int H, int chunk_tokens, int max_chunks);
@@ -258,7 +260,8 @@ size_t mla_prefill_workspace_size(int s_q, int H, int chunk_tokens, int max_chun
  *   block_table [B, max_pages_per_seq] int32 (device);
  *   seqlens_host [B] (HOST) L_b in [s_q, 64 * max_pages_per_seq].
  *   w_uk, w_uv [H, 512, 128] bf16 (latent rows), as for mla_absorb_q/out_uv.
- *   chunk_tokens >= 1; at most 64 chunks per sequence (else UNSUPPORTED).
+ *   1 <= chunk_tokens <= 65536 and at most 64 chunks per sequence (else
+ *   UNSUPPORTED).
  *   H 1..128. softmax_scale finite and > 0 (1/sqrt(192) for DeepSeek-V3).
  *   workspace of at least mla_prefill_workspace_size(s_q, H, chunk_tokens,
  *   max over b of ceil(L_b / chunk_tokens)) bytes, contents ignored.

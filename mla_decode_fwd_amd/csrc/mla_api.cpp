@@ -200,8 +200,11 @@ mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, co
 
 namespace {
 constexpr int kPrefillMaxChunks = 64;
+constexpr int kPrefillMaxChunkTokens = 65536;  // the expansion keeps one range's page ids in LDS
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-size_t prefill_kv_bytes(int H, int chunk) { return align256((size_t)H * chunk * (192 + 128) * 2); }
+// Expanded keys K [H, chunk, 128] and values V [H, chunk, 128], and the
+// chunk's RoPE keys R [chunk, 64] that every head shares.
+size_t prefill_kv_bytes(int H, int chunk) { return align256((size_t)H * chunk * (128 + 128) * 2 + (size_t)chunk * 64 * 2); }
 }  // namespace
 
 size_t mla_prefill_workspace_size(int s_q, int H, int chunk_tokens, int max_chunks) {
@@ -231,6 +234,7 @@ mla_status_t mla_prefill_fwd(const void* q_nope, const void* q_rope, const void*
   if (B <= 0 || s_q <= 0 || H <= 0 || H > kMaxHeads || max_pages_per_seq <= 0 || num_pages <= 0 || chunk_tokens <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (chunk_tokens > kPrefillMaxChunkTokens) return MLA_ERR_UNSUPPORTED;
   int max_chunks = 1;
   for (int b = 0; b < B; ++b) {
     const long long L = seqlens_host[b];
@@ -243,7 +247,8 @@ mla_status_t mla_prefill_fwd(const void* q_nope, const void* q_rope, const void*
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   void* K = ws;
-  void* V = ws + (size_t)H * chunk_tokens * 192 * 2;
+  void* V = ws + (size_t)H * chunk_tokens * 128 * 2;
+  void* R = ws + (size_t)H * chunk_tokens * 256 * 2;
   const size_t parts = (size_t)max_chunks * s_q * H;
   char* o_part = ws + prefill_kv_bytes(H, chunk_tokens);
   float* lse_part = reinterpret_cast<float*>(o_part + align256(parts * 128 * 2));
@@ -260,11 +265,12 @@ mla_status_t mla_prefill_fwd(const void* q_nope, const void* q_rope, const void*
       const int t0 = c * chunk_tokens;
       const int n = L - t0 < chunk_tokens ? L - t0 : chunk_tokens;
       hipError_t e = mla::launch_expand(kv_cache, block_table + (size_t)b * max_pages_per_seq, t0, n, num_pages, w_uk,
-                                        w_uv, H, K, V, chunk_tokens, st);
+                                        w_uv, H, K, V, R, chunk_tokens, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
       void* od = n_chunks == 1 ? static_cast<void*>(ob) : static_cast<void*>(o_part + (size_t)c * q_rows * 128 * 2);
       float* ld = n_chunks == 1 ? lb : lse_part + (size_t)c * q_rows;
-      e = mla::launch_prefill_attn(qn, qr, s_q, H, K, V, n, chunk_tokens, t0, L - s_q, 1, softmax_scale, od, ld, st);
+      e = mla::launch_prefill_attn(qn, qr, s_q, H, K, V, R, n, chunk_tokens, t0, L - s_q, 1, softmax_scale, od, ld,
+                                   st);
       if (e != hipSuccess) return MLA_ERR_HIP;
     }
     if (n_chunks > 1) {

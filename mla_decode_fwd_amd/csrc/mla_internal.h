@@ -49,10 +49,11 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 // for cached tokens t0 .. t0+n-1 of one sequence; causal attention of s_q new
 // tokens over them; LSE merge of n_parts chunk partials of width 128.
 hipError_t launch_expand(const void* cache, const int32_t* btab_row, int t0, int n, int num_pages, const void* w_uk,
-                         const void* w_uv, int H, void* k_out, void* v_out, int n_stride, hipStream_t stream);
+                         const void* w_uv, int H, void* k_out, void* v_out, void* r_out, int n_stride,
+                         hipStream_t stream);
 hipError_t launch_prefill_attn(const void* q_nope, const void* q_rope, int s_q, int H, const void* K, const void* V,
-                               int n, int n_stride, int k_pos0, int q_pos0, int causal, float scale, void* o,
-                               float* lse, hipStream_t stream);
+                               const void* R, int n, int n_stride, int k_pos0, int q_pos0, int causal, float scale,
+                               void* o, float* lse, hipStream_t stream);
 hipError_t launch_prefill_merge(const void* o_part, const float* lse_part, int n_parts, int rows, void* o, float* lse,
                                 hipStream_t stream);
 
