@@ -301,8 +301,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, hi32 = lane >> 5;
-  const int h = blockIdx.y;
-  const int qb = blockIdx.x * kRowsPerGroup;
+  // Head-major, XCD-aware order: workgroup x runs on XCD x & 7, which takes
+  // heads x & 7, 8 + (x & 7), ... one at a time, heaviest query block first.
+  // So the query blocks of one head run together on one XCD and re-read
+  // that head's keys and values from its L2 and the last-level cache rather
+  // than from HBM.
+  const int n_qb = (s_q + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int xk = blockIdx.x >> 3;
+  const int h = (xk / n_qb) * 8 + (blockIdx.x & 7);
+  if (h >= H) return;  // uniform over the workgroup, before any barrier
+  const int qb = (n_qb - 1 - xk % n_qb) * kRowsPerGroup;
   const int qrow = qb + wave * kWaveRows + r32;
   const int qc = min(qrow, s_q - 1);
   const int qpos = q_pos0 + qc;
@@ -518,7 +526,8 @@ hipError_t launch_expand(const void* cache, const int32_t* btab_row, int t0, int
 hipError_t launch_prefill_attn(const void* q_nope, const void* q_rope, int s_q, int H, const void* K, const void* V,
                                const void* R, int n, int n_stride, int k_pos0, int q_pos0, int causal, float scale,
                                void* o, float* lse, hipStream_t stream) {
-  const dim3 grid((unsigned)((s_q + kRowsPerGroup - 1) / kRowsPerGroup), (unsigned)H);
+  const int n_qb = (s_q + kRowsPerGroup - 1) / kRowsPerGroup;
+  const dim3 grid((unsigned)(n_qb * ((H + 7) / 8) * 8));
   hipLaunchKernelGGL(attn_kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q_nope),
                      static_cast<const __bf16*>(q_rope), s_q, H, static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), static_cast<const __bf16*>(R), n, n_stride, k_pos0, q_pos0,

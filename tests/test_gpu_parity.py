@@ -520,3 +520,37 @@ def test_two_paths_agree_and_auto_choice():
         torch.cuda.synchronize()
         _prefill_compare(o, lse, o_ref, l_ref, f"extend s_q=8 via {path}")
     assert mla.select_path(8, 1000) == "absorbed" and mla.select_path(300, 2000) == "expanded"
+
+
+def _prefill_sampled(L, s_q, chunk, heads, seed):
+    """The expanded path at a full workload size, checked on two blocks of 16
+    query rows (the first and the last new tokens) for a few heads: each
+    block is the last 16 tokens of a prefix of the sequence, which is how
+    the oracle states it."""
+    from mla_inputs import prefill_case
+    case = prefill_case([L], s_q, H=128, seed=seed)
+    m = case.meta
+    d = to_device(case)
+    o, lse = mla.mla_prefill_fwd(m["q_nope"].cuda(), m["q_rope"].cuda(), d["kv_cache"], d["block_table"], [L],
+                                 m["w_uk"].cuda(), m["w_uv"].cuda(), case.scale, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    og, lg = to_np(o), to_np(lse)
+    hs = list(heads)
+    for first in (0, s_q - 16):
+        rows = slice(first, first + 16)
+        Lp = L - s_q + first + 16  # the block's last query sits at position Lp - 1
+        o_ref, l_ref = orc.prefill_expanded(to_np(m["q_nope"][:, rows][:, :, hs]), to_np(m["q_rope"][:, rows][:, :, hs]),
+                                            to_np(case.cache), case.block_table.numpy(), np.array([Lp]),
+                                            to_np(m["w_uk"][hs]), to_np(m["w_uv"][hs]), case.scale)
+        _prefill_compare(torch.from_numpy(og[:, rows][:, :, hs].copy()), torch.from_numpy(lg[:, rows][:, :, hs].copy()),
+                         o_ref, l_ref, f"L={L} s_q={s_q} chunk={chunk} rows {first}..{first + 15} heads {hs}")
+
+
+def test_prefill_8k_sampled():
+    # The prefill bench workload: a fresh 8K-token prefill, one 8192-token chunk.
+    _prefill_sampled(8192, 8192, 8192, (0, 77, 127), seed=160)
+
+
+def test_extend_32k_sampled():
+    # The extend bench workload: 512 new tokens after 32K, five chunks merged by LSE.
+    _prefill_sampled(32768 + 512, 512, 8192, (0, 127), seed=161)
