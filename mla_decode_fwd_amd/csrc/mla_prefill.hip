@@ -278,39 +278,50 @@ __global__ __launch_bounds__(kExpThreads, 1) void expand_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// attn_kernel: one workgroup per (128 new tokens, head); wave w takes 32 query
-// rows. Q^T (12 k-steps over 192) stays in VGPRs, O^T (128 columns) in four
-// 32x32 accumulators. Keys come in tiles of 32: S^T = K Q^T, base-2 online
-// softmax with a lazily moved reference (as the decode kernel), O^T += V^T P^T
-// with P^T taken from the score registers and V^T read transposed.
+// attn_kernel: one workgroup per (256 new tokens, head), eight waves of 32
+// query rows (two per SIMD). Q^T (12 k-steps over 192) stays in VGPRs, O^T
+// (128 columns) in four 32x32 accumulators. Keys come in tiles of 64,
+// double-buffered in LDS (global loads into registers during the previous
+// tile's products, one barrier per tile), so every K and V byte in LDS
+// feeds the eight waves: S^T = K Q^T per 32-key half, base-2 online softmax
+// over the 64 keys with a lazily moved reference (as the decode kernel),
+// O^T += V^T P^T with P^T taken from the score registers and V^T read
+// transposed. A wave skips the products of tiles that lie wholly past its
+// last row's position.
 // ---------------------------------------------------------------------------
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kQRows = kAttnWaves * kWaveRows;  // 256 query rows per workgroup
 constexpr int kKStride = kHeadK * 2 + 16;   // 400: 16 consecutive keys on 16 bank groups
 constexpr int kVStride = kHeadV * 2 + 64;   // 320
-constexpr int kKTile = 32;
-constexpr int kKBuf = kKTile * kKStride;    // 12,800
-constexpr int kVBuf = kKTile * kVStride;    // 10,240
+constexpr int kKTile = 64;
+constexpr int kKBuf = kKTile * kKStride;    // 25,600
+constexpr int kVBuf = kKTile * kVStride;    // 20,480
 constexpr int kStage = kKBuf + kVBuf;
+static_assert(kKTile * 24 == 3 * kAttnThreads && kKTile * 16 == 2 * kAttnThreads, "tile loads: 3 + 2 pieces per thread");
 
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restrict__ q_nope,
-                                                          const __bf16* __restrict__ q_rope, int s_q, int H,
-                                                          const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                                                          const __bf16* __restrict__ R, int n, int n_stride,
-                                                          int k_pos0, int q_pos0, int causal,
-                                                          float scale, __bf16* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(const __bf16* __restrict__ q_nope,
+                                                              const __bf16* __restrict__ q_rope, int s_q, int H,
+                                                              const __bf16* __restrict__ K,
+                                                              const __bf16* __restrict__ V,
+                                                              const __bf16* __restrict__ R, int n, int n_stride,
+                                                              int k_pos0, int q_pos0, int causal, float scale,
+                                                              __bf16* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r32 = lane & 31, hi32 = lane >> 5;
   // Head-major, XCD-aware order: workgroup x runs on XCD x & 7, which takes
   // heads x & 7, 8 + (x & 7), ... one at a time, heaviest query block first.
   // So the query blocks of one head run together on one XCD and re-read
   // that head's keys and values from its L2 and the last-level cache rather
   // than from HBM.
-  const int n_qb = (s_q + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int n_qb = (s_q + kQRows - 1) / kQRows;
   const int xk = blockIdx.x >> 3;
   const int h = (xk / n_qb) * 8 + (blockIdx.x & 7);
   if (h >= H) return;  // uniform over the workgroup, before any barrier
-  const int qb = (n_qb - 1 - xk % n_qb) * kRowsPerGroup;
+  const int qb = (n_qb - 1 - xk % n_qb) * kQRows;
   const int qrow = qb + wave * kWaveRows + r32;
   const int qc = min(qrow, s_q - 1);
   const int qpos = q_pos0 + qc;
@@ -327,20 +338,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
   }
 
   // Keys this workgroup may need: up to the last query's position.
-  const int q_last = q_pos0 + min(s_q, qb + kRowsPerGroup) - 1;
+  const int q_last = q_pos0 + min(s_q, qb + kQRows) - 1;
   const int n_vis = causal ? max(0, min(n, q_last - k_pos0 + 1)) : n;
   const int tiles = (n_vis + kKTile - 1) / kKTile;
-  const int q_first_wave = q_pos0 + min(qb + wave * kWaveRows, s_q - 1);  // smallest position in this wave
+  const int w_first = q_pos0 + min(qb + wave * kWaveRows, s_q - 1);                   // this wave's first row
+  const int w_last = q_pos0 + min(qb + wave * kWaveRows + kWaveRows, s_q) - 1;         // and its last row
 
   const __bf16* Kh = K + (size_t)h * n_stride * kNope;
   const __bf16* Vh = V + (size_t)h * n_stride * kHeadV;
-  // Tile loads: K 32 rows x 24 chunks (3 per thread; chunks 0-15 from the
-  // head's expanded keys, 16-23 the shared RoPE key), V 32 rows x 16 chunks
+  // Tile loads: K 64 rows x 24 chunks (3 per thread; chunks 0-15 from the
+  // head's expanded keys, 16-23 the shared RoPE key), V 64 rows x 16 chunks
   // (2 per thread).
   auto load_tile = [&](int kt, u32x4_t (&kr)[3], u32x4_t (&vr)[2]) {
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-      const int idx = u * kThreads + (int)threadIdx.x;
+      const int idx = u * kAttnThreads + t;
       const int row = idx / 24, c16 = idx % 24;
       const int key = min(kt * kKTile + row, n - 1);
       kr[u] = *reinterpret_cast<const u32x4_t*>(c16 < 16 ? Kh + (size_t)key * kNope + 8 * c16
@@ -348,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = u * kThreads + (int)threadIdx.x;
+      const int idx = u * kAttnThreads + t;
       const int row = idx >> 4, c16 = idx & 15;
       const int key = min(kt * kKTile + row, n - 1);
       vr[u] = *reinterpret_cast<const u32x4_t*>(Vh + (size_t)key * kHeadV + 8 * c16);
@@ -357,12 +369,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
   auto store_tile = [&](char* buf, const u32x4_t (&kr)[3], const u32x4_t (&vr)[2]) {
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-      const int idx = u * kThreads + (int)threadIdx.x;
+      const int idx = u * kAttnThreads + t;
       *reinterpret_cast<u32x4_t*>(buf + (idx / 24) * kKStride + 16 * (idx % 24)) = kr[u];
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = u * kThreads + (int)threadIdx.x;
+      const int idx = u * kAttnThreads + t;
       *reinterpret_cast<u32x4_t*>(buf + kKBuf + (idx >> 4) * kVStride + 16 * (idx & 15)) = vr[u];
     }
   };
@@ -386,30 +398,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
   for (int kt = 0; kt < tiles; ++kt) {
     char* buf = smem + (kt & 1) * kStage;
     store_tile(buf, kr, vr);
-    __syncthreads();
+    __syncthreads();  // tile kt visible; every wave is done with tile kt-2, whose buffer the next store refills
     if (kt + 1 < tiles) load_tile(kt + 1, kr, vr);
     const int key0 = k_pos0 + kt * kKTile;  // position of the tile's first key
-    if (!causal || key0 <= q_pos0 + min(qb + wave * kWaveRows + kWaveRows, s_q) - 1) {
-      f32x16_t st;
+    if (!causal || key0 <= w_last) {
+      f32x16_t st[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      for (int T = 0; T < 2; ++T) {
 #pragma unroll
-      for (int s = 0; s < kHeadK / 16; ++s) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(buf + qk_off + 32 * s);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st, 0, 0, 0);
-      }
-      // Mask keys past the chunk or past the query's position.
-      const bool full = kt * kKTile + kKTile <= n_vis && (!causal || key0 + kKTile - 1 <= q_first_wave);
-      if (!full) {
+        for (int r = 0; r < 16; ++r) st[T][r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = kt * kKTile + 8 * (r >> 2) + 4 * hi32 + (r & 3);
-          if (kl >= n_vis || (causal && k_pos0 + kl > qpos)) st[r] = -INFINITY;
+        for (int s = 0; s < kHeadK / 16; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(buf + T * 32 * kKStride + qk_off + 32 * s);
+          st[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[T], 0, 0, 0);
         }
       }
-      float mx = st[0];
+      // Mask keys past the chunk or past the query's position.
+      const bool full = kt * kKTile + kKTile <= n_vis && (!causal || key0 + kKTile - 1 <= w_first);
+      if (!full) {
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kl = kt * kKTile + 32 * T + 8 * (r >> 2) + 4 * hi32 + (r & 3);
+            if (kl >= n_vis || (causal && k_pos0 + kl > qpos)) st[T][r] = -INFINITY;
+          }
+      }
+      float mx = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(mx, __uint_as_float(hi32 ? sw[0] : sw[1])) * sl2;
       const float m_new = (mx > m_ref + 8.0f || m_ref == -INFINITY) ? mx : m_ref;
@@ -423,15 +440,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
       }
       m_ref = m_new;
       const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      bf16x8_t pf[2];
+      // k-step u of the tile: keys 16u .. 16u+15 = half T = u >> 1, scores 8(u&1) .. +8.
+      bf16x8_t pf[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, neg));
-        l_loc += p;
-        pf[r >> 3][r & 7] = (__bf16)p;
-      }
+      for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][r], sl2, neg));
+          l_loc += p;
+          pf[2 * T + (r >> 3)][r & 7] = (__bf16)p;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           bf16x8_t vf;
@@ -445,7 +465,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const __bf16* __restr
           acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], acc[ct], 0, 0, 0);
         }
     }
-    __syncthreads();
   }
 
   const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_loc), __float_as_uint(l_loc), false, false);
@@ -526,9 +545,9 @@ hipError_t launch_expand(const void* cache, const int32_t* btab_row, int t0, int
 hipError_t launch_prefill_attn(const void* q_nope, const void* q_rope, int s_q, int H, const void* K, const void* V,
                                const void* R, int n, int n_stride, int k_pos0, int q_pos0, int causal, float scale,
                                void* o, float* lse, hipStream_t stream) {
-  const int n_qb = (s_q + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int n_qb = (s_q + kQRows - 1) / kQRows;
   const dim3 grid((unsigned)(n_qb * ((H + 7) / 8) * 8));
-  hipLaunchKernelGGL(attn_kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q_nope),
+  hipLaunchKernelGGL(attn_kernel, grid, dim3(kAttnThreads), 0, stream, static_cast<const __bf16*>(q_nope),
                      static_cast<const __bf16*>(q_rope), s_q, H, static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), static_cast<const __bf16*>(R), n, n_stride, k_pos0, q_pos0,
                      causal, scale, static_cast<__bf16*>(o), lse);
