@@ -38,6 +38,15 @@ Function list and pins:
   prefill_chunked    the same over prefix chunks + LSE merge pinned (== unchunked)
   crossover_tokens   new-token count where the paths' FLOPs  pinned (the chapter's printed 171)
                      cross, for a given key count
+  e4m3_encode        value -> FP8 e4m3 code, nearest, ties   pinned (torch's float8_e4m3fn
+                     to even, saturating at 448              conversion on every tie and a dense
+                                                            sweep; round trip of all codes)
+  quantize_e4m3      per-tensor dynamic quantisation: scale  pinned (max element -> 448, zero
+                     = max|x| / 448, codes of x / scale      tensor, exact inputs round-trip)
+  absorb_q_fp8       absorb_q with an e4m3 query and e4m3    pinned (== absorb_q on exactly
+                     weights, both scaled                    representable inputs)
+  out_uv_fp8         out_uv with an e4m3 latent output and   pinned (== out_uv on exactly
+                     e4m3 weights stored transposed          representable inputs)
 No function is left without a pin.
 """
 from __future__ import annotations
@@ -64,6 +73,10 @@ __all__ = [
     "prefill_expanded",
     "prefill_chunked",
     "crossover_tokens",
+    "e4m3_encode",
+    "quantize_e4m3",
+    "absorb_q_fp8",
+    "out_uv_fp8",
 ]
 
 
@@ -487,3 +500,72 @@ def crossover_tokens(L: int, H: int = 128, nope: int = 128, rope: int = 64, dv: 
     p1 = 2 * H * (nope + rope) + 2 * H * dv
     p2 = 2 * H * (dc + rope) + 2 * H * dc
     return e * L / (b + (p2 - p1) * L)
+
+
+# ---------------------------------------------------------------------------
+# FP8 batched products for the absorption ([DSV2-MLA], the SGLang history
+# section: with FP8 weights w_kc and w_vc the absorbed query and the output
+# projection run as bmm_fp8 of an activation quantised to e4m3 on the fly,
+# one scale per tensor, against the e4m3 weights and their scale, with a
+# bf16 result).
+# ---------------------------------------------------------------------------
+
+_E4M3_CODES = np.arange(0x00, 0x7F)            # the 127 non-negative finite codes, increasing values
+_E4M3_VALUES = None
+
+
+def _e4m3_table():
+    global _E4M3_VALUES
+    if _E4M3_VALUES is None:
+        _E4M3_VALUES = e4m3_decode(_E4M3_CODES)
+    return _E4M3_VALUES
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest e4m3 ("fn") code of each value, ties to the even code, magnitudes
+    beyond the largest finite value 448 clamped to it; the sign is kept (so -0
+    gives 0x80). This is round-to-nearest-even onto the value set e4m3_decode
+    defines, taken over the exact float64 values of x."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = _e4m3_table()
+    mag = np.minimum(np.abs(x), vals[-1])
+    hi = np.searchsorted(vals, mag, side="left")          # vals[hi-1] < mag <= vals[hi]
+    hi = np.clip(hi, 1, len(vals) - 1)
+    lo = hi - 1
+    d_lo, d_hi = mag - vals[lo], vals[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_E4M3_CODES[hi] % 2 == 0))
+    code = np.where(pick_hi, _E4M3_CODES[hi], _E4M3_CODES[lo])
+    code = np.where(mag == 0.0, 0, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3(x):
+    """Per-tensor dynamic quantisation to e4m3, the activation side of the
+    pages' bmm_fp8: one fp32 scale s = max|x| / 448 (1 for an all-zero tensor)
+    and codes e4m3_encode(x / s), the quotient taken in fp32 (the precision
+    the kernel decides the codes in). Returns (codes uint8, s float32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    return e4m3_encode((x32 / s).astype(np.float32)), s
+
+
+def absorb_q_fp8(q_n, q_r, w_uk_codes, w_scale: float) -> np.ndarray:
+    """absorb_q with e4m3 operands: q^N quantised per tensor (quantize_e4m3),
+    W_UK given as e4m3 codes [H, DC, nope] with one scale, the product scaled
+    by both scales, q^R copied. Returns float64 [N, H, DC + rope]."""
+    codes, s = quantize_e4m3(q_n)
+    q = e4m3_decode(codes) * np.float64(s)
+    w = e4m3_decode(w_uk_codes) * float(w_scale)
+    return absorb_q(q, q_r, w)
+
+
+def out_uv_fp8(o_lat, w_uv_t_codes, w_scale: float) -> np.ndarray:
+    """out_uv with e4m3 operands: the latent output quantised per tensor, W_UV
+    given transposed as e4m3 codes [H, DV, DC] (the weight prepared once, as
+    the pages' history transposes the MLA weights offline) with one scale.
+    Returns float64 [N, H, DV]."""
+    codes, s = quantize_e4m3(o_lat)
+    o = e4m3_decode(codes) * np.float64(s)
+    w = e4m3_decode(w_uv_t_codes) * float(w_scale)
+    return out_uv(o, np.swapaxes(w, 1, 2))

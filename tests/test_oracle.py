@@ -582,3 +582,89 @@ def test_crossover_matches_printed_171():
     # At L = 128K the formula gives 170.4; the text rounds the range's upper
     # end to the large-L limit 171 (170.7), so allow one unit there.
     assert abs(orc.crossover_tokens(131072) - g2["crossover_L131072"]) < 1.0
+
+
+# ---------------------------------------------------------------------------
+# FP8 bmm for the absorption: encoder, per-tensor quantiser, fp8 absorb/out_uv
+# ---------------------------------------------------------------------------
+
+def _e4m3_finite_values():
+    v = orc.e4m3_decode(np.arange(256))
+    return v[np.isfinite(v)]
+
+
+def test_e4m3_encoder_matches_torch_on_every_tie_and_a_sweep():
+    # torch's float8_e4m3fn conversion rounds to nearest, ties to even; every
+    # midpoint between neighbouring values is a tie, exact in fp32.
+    v = np.unique(np.abs(_e4m3_finite_values()))
+    mids = (v[1:] + v[:-1]) / 2
+    x = np.concatenate([np.linspace(-448.0, 448.0, 100001), mids, -mids, v, -v,
+                        np.nextafter(mids, 0), np.nextafter(mids, 1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.e4m3_encode(x), ref)
+
+
+def test_e4m3_encoder_round_trip_saturation_and_signed_zero():
+    codes = np.arange(256)
+    vals = orc.e4m3_decode(codes)
+    fin = np.isfinite(vals)
+    assert np.array_equal(orc.e4m3_encode(vals[fin]), codes[fin].astype(np.uint8))
+    # 2^-10 is half way from 0 to the smallest step 2^-9 (ties to code 0);
+    # 3 * 2^-10 half way from 2^-9 to 2^-8 (ties to code 2).
+    assert list(orc.e4m3_encode([448.0, 463.9, 1e9, -1e9, -0.0, 0.0, 2.0 ** -10, 3 * 2.0 ** -10])) == \
+        [0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x00, 0x02]
+
+
+def test_quantize_e4m3_scale_and_extremes():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 3, 64)).astype(np.float32)
+    x[2, 1, 7] = -9.5  # the largest magnitude
+    codes, s = orc.quantize_e4m3(x)
+    assert s == np.float32(np.float32(9.5) / np.float32(448.0))
+    assert codes[2, 1, 7] == 0xFE and np.max(np.abs(orc.e4m3_decode(codes))) == 448.0
+    deq = orc.e4m3_decode(codes) * np.float64(s)
+    assert np.max(np.abs(deq - x) / np.maximum(np.abs(x), 2.0 ** -6 * s)) <= 2.0 ** -4  # half an ulp of 3 bits
+    zc, zs = orc.quantize_e4m3(np.zeros((4, 4), np.float32))
+    assert zs == 1.0 and not zc.any()
+
+
+def _representable_operands(rng, shape, step):
+    # Values on the e4m3 grid times a power of two, with the grid maximum 448
+    # present, so that the per-tensor scale is the power of two itself and
+    # quantisation is exact.
+    vals = _e4m3_finite_values()
+    x = rng.choice(vals, size=shape) * step
+    x.reshape(-1)[0] = 448.0 * step
+    return x.astype(np.float32)
+
+
+def test_absorb_q_fp8_equals_absorb_q_on_representable_inputs():
+    rng = np.random.default_rng(11)
+    q_n = _representable_operands(rng, (6, 4, 16), 2.0 ** -9)
+    q_r = rng.standard_normal((6, 4, 8))
+    w_codes = rng.integers(0, 256, size=(4, 32, 16)).astype(np.uint8)
+    w_codes[(w_codes & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    got = orc.absorb_q_fp8(q_n, q_r, w_codes, 0.125)
+    want = orc.absorb_q(q_n.astype(np.float64), q_r, orc.e4m3_decode(w_codes) * 0.125)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    assert np.array_equal(got[..., 32:], q_r)
+
+
+def test_out_uv_fp8_equals_out_uv_on_representable_inputs():
+    rng = np.random.default_rng(12)
+    o = _representable_operands(rng, (5, 3, 32), 2.0 ** -8)
+    w_t = rng.integers(0, 256, size=(3, 24, 32)).astype(np.uint8)  # [H, DV, DC]
+    w_t[(w_t & 0x7F) == 0x7F] = 0x44
+    got = orc.out_uv_fp8(o, w_t, 0.5)
+    want = orc.out_uv(o.astype(np.float64), np.swapaxes(orc.e4m3_decode(w_t) * 0.5, 1, 2))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_mutation_e4m3_ties_away_from_zero_is_caught(monkeypatch):
+    # A plausible encoder mistake, ties rounded away from zero, fails the torch pin.
+    v = np.unique(np.abs(_e4m3_finite_values()))
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)
+    real = orc.e4m3_encode
+    monkeypatch.setattr(orc, "e4m3_encode", lambda x: real(np.nextafter(np.asarray(x, np.float64), np.inf)))
+    ref = torch.from_numpy(mids).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert not np.array_equal(orc.e4m3_encode(mids), ref)
