@@ -27,6 +27,11 @@ recorded there, i.e. when the kernel changed after the counters were taken.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload on this host's cores.
 
+After the three timed regions, two more (not used for `value`): the K steps
+with one event pair each (`step_us_percentiles`: p10, median, p90), and the K
+steps on one copy of the cache only (`warm_step_us`). `cpu_baseline.cpu` names
+the host CPU.
+
 --copy-mb N adds, after the timed steps, three plain device-to-device copies
 of N MiB: a kernel of known traffic, for scaling the memory counters.
 """
@@ -81,6 +86,18 @@ def measured_traffic():
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8", errors="replace") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(case, budget_s: float = 15.0) -> dict:
@@ -143,6 +160,7 @@ def cpu_baseline(case, budget_s: float = 15.0) -> dict:
     except Exception:  # threadpoolctl missing: count the cores we may run on
         cores = len(os.sched_getaffinity(0))
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{n} sequence {'top-k ' if idx is not None else ''}decodes ({n / case.B:.2f} passes over "
                       f"the B={case.B} batch, ctx {int(L[0])}, H={case.H}), fp64 numpy, {secs:.1f} s",
             "seconds": secs}
@@ -181,6 +199,7 @@ def prefill_cpu_baseline(case, budget_s: float) -> dict:
     except Exception:  # threadpoolctl missing: count the cores we may run on
         cores = len(os.sched_getaffinity(0))
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{n} x expanded-path prefill of {heads} of {case.H} heads, the last {rows} of the "
                       f"{case.s_q} new tokens over all {L} tokens (expansion included), fp64 numpy, {secs:.1f} s",
             "seconds": secs}
@@ -362,6 +381,21 @@ def main():
     step_gpu_ms, ms_per_step = timed(step)
     decode_ms, _ = timed(lambda i: dec_calls[i % 2]())
     combine_ms, _ = timed(lambda i: comb_call())
+    # Distribution and warm-cache figures, from separate regions after the
+    # timed ones: one event pair per step (each event costs the GPU a few
+    # microseconds, so these steps read a little slower than ms_per_step),
+    # and the K steps again on one copy of the cache only (part of its 302 MB
+    # then stays in the 256 MB last-level cache between steps).
+    per_step = []
+    for i in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        per_step.append((e0, e1))
+    torch.cuda.synchronize()
+    per_step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in per_step)
+    warm_ms, _ = timed(lambda i: step(0))
 
     if args.copy_mb > 0:
         n = args.copy_mb << 20
@@ -428,6 +462,11 @@ def main():
                      "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},
         "plan_host_us": round(plan_us, 1),
         "step_gpu_ms": round(step_gpu_ms, 5),
+        "step_us_percentiles": {"p10": round(per_step_us[len(per_step_us) // 10], 2),
+                                "median": round(per_step_us[len(per_step_us) // 2], 2),
+                                "p90": round(per_step_us[(9 * len(per_step_us)) // 10], 2),
+                                "note": "one event pair per step, separate region"},
+        "warm_step_us": round(warm_ms * 1e3, 2),
     }
     if not args.no_cpu_baseline:
         _log("timing the CPU oracle ...")

@@ -73,8 +73,10 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 4 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
-   4 the expanded path: mla_select_path, mla_prefill_workspace_size, mla_prefill_fwd). */
+/* Library ABI version, currently 5 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
+   4 the expanded path: mla_select_path, mla_prefill_workspace_size, mla_prefill_fwd,
+   5 the FP8 products: mla_fp8_workspace_size, mla_quantize_e4m3, mla_absorb_q_fp8,
+   mla_out_uv_fp8). */
 int mla_abi_version(void);
 
 /*
@@ -321,6 +323,59 @@ mla_status_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_
  */
 mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d_c, int d_v,
                         mla_dtype_t dtype, void* out, void* stream);
+
+/*
+ * FP8 (e4m3) products for the absorption ([DSV2-MLA], the SGLang history
+ * section: with FP8 weights w_kc and w_vc, both bmm's run as bmm_fp8 of an
+ * activation quantised to e4m3 on the fly, one scale per tensor, against the
+ * e4m3 weights and their scale, with a bf16 result).
+ *
+ * Codes are e4m3 "fn" (bias 7, no infinities, NaN 0x7F/0xFF, largest finite
+ * 448). Per-tensor dynamic quantisation of a bf16 tensor x:
+ *   s = max|x| / 448 (fp32; 1 when x is all zero),
+ *   code = nearest e4m3 value of the fp32 quotient x / s, ties to even,
+ *          magnitudes clamped to 448.
+ */
+
+/* Workspace bytes for quantising n_elems elements inside mla_absorb_q_fp8 /
+   mla_out_uv_fp8 (partial maxima, the scale and the codes); 0 for 0. */
+size_t mla_fp8_workspace_size(size_t n_elems);
+
+/*
+ * Per-tensor quantisation on its own: x [n] bf16 (16-byte aligned) ->
+ * codes [n] uint8 (8-byte aligned) and *scale (one fp32, device). workspace:
+ * at least 1 KB of device scratch (contents ignored). Two kernels on stream.
+ */
+mla_status_t mla_quantize_e4m3(const void* x, size_t n, void* workspace, size_t workspace_bytes, uint8_t* codes,
+                               float* scale, void* stream);
+
+/*
+ * mla_absorb_q with FP8 operands:
+ *   q_lat[n,h,0:d_c] = bf16( s_q * w_scale * sum_d e4m3(q_nope)[n,h,d] * w_uk[h,c,d] )
+ *   q_lat[n,h,d_c:]  = q_rope[n,h,:]  (copied)
+ * where q_nope is quantised per tensor as above.
+ *   q_nope [N, H, d_nope] bf16 (16-byte aligned), q_rope [N, H, d_rope] bf16;
+ *   w_uk [H, d_c, d_nope] e4m3 codes (8-byte aligned) with scale w_scale
+ *   (host float, finite, > 0); q_lat out [N, H, d_c + d_rope] bf16 (8-byte aligned).
+ *   d_nope a multiple of 16, d_c and d_rope multiples of 4; H <= 1024; dims <= 4096.
+ *   workspace of at least mla_fp8_workspace_size(N * H * d_nope) bytes.
+ */
+mla_status_t mla_absorb_q_fp8(const void* q_nope, const void* q_rope, const uint8_t* w_uk, float w_scale, int N,
+                              int H, int d_nope, int d_rope, int d_c, void* workspace, size_t workspace_bytes,
+                              void* q_lat, void* stream);
+
+/*
+ * mla_out_uv with FP8 operands:
+ *   out[n,h,e] = bf16( s_o * w_scale * sum_c e4m3(o_lat)[n,h,c] * w_uv_t[h,e,c] )
+ * where o_lat is quantised per tensor as above and the weight is W_UV stored
+ * transposed, [H, d_v, d_c] e4m3 codes (prepared once, as the pages' history
+ * transposes the MLA weights offline), so that both operands run along d_c.
+ *   o_lat [N, H, d_c] bf16 (16-byte aligned); out [N, H, d_v] bf16 (8-byte
+ *   aligned). d_c a multiple of 16, d_v a multiple of 4; H <= 1024; dims <= 4096.
+ *   workspace of at least mla_fp8_workspace_size(N * H * d_c) bytes.
+ */
+mla_status_t mla_out_uv_fp8(const void* o_lat, const uint8_t* w_uv_t, float w_scale, int N, int H, int d_c, int d_v,
+                            void* workspace, size_t workspace_bytes, void* out, void* stream);
 
 #ifdef __cplusplus
 }

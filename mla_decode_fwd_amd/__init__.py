@@ -23,7 +23,11 @@ __all__ = [
     "decode_plan", "decode_workspace_size", "mla_decode_fwd", "mla_splitkv_combine",
     "mla_absorb_q", "mla_out_uv", "DecodePlan", "workspace_partials",
     "PreparedCall", "prepare_decode", "prepare_combine",
-    "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS",
+    "mla_sparse_decode_fwd", "sparse_decode_plan", "prepare_sparse_decode",
+    "mla_decode_fwd_fp8", "prepare_decode_fp8",
+    "select_path", "prefill_workspace_size", "mla_prefill_fwd", "mla_attention_fwd",
+    "fp8_workspace_size", "quantize_e4m3", "mla_absorb_q_fp8", "mla_out_uv_fp8",
+    "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS", "MAX_DECODE_SQ",
 ]
 
 D_QK = 576
@@ -79,6 +83,10 @@ def load_library():
         "mla_splitkv_combine": ([P, P, P, I, I, I, I, I, I, P, P, P], I),
         "mla_absorb_q": ([P, P, P, I, I, I, I, I, I, P, P], I),
         "mla_out_uv": ([P, P, I, I, I, I, I, P, P], I),
+        "mla_fp8_workspace_size": ([Z], Z),
+        "mla_quantize_e4m3": ([P, Z, P, Z, P, P, P], I),
+        "mla_absorb_q_fp8": ([P, P, P, F, I, I, I, I, I, P, Z, P, P], I),
+        "mla_out_uv_fp8": ([P, P, F, I, I, I, I, P, Z, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -539,3 +547,66 @@ def mla_attention_fwd(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: torc
     o_lat, lse = mla_decode_fwd(q_lat.view(B, s_q, H, -1), kv_cache, block_table, seqlens, softmax_scale, True, **kw)
     o = mla_out_uv(o_lat.view(B * s_q, H, -1), w_uv)
     return o.view(B, s_q, H, -1), lse
+
+
+# ---- FP8 products for the absorption -------------------------------------
+
+def fp8_workspace_size(n_elems: int) -> int:
+    return int(load_library().mla_fp8_workspace_size(int(n_elems)))
+
+
+def quantize_e4m3(x: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Per-tensor e4m3 quantisation (mla_quantize_e4m3): codes (uint8, x's
+    shape) and the scale (one-element fp32 tensor) on x's device."""
+    _need(x, "x", dtype=torch.bfloat16)
+    dev = x.device
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(1024, dtype=torch.uint8, device=dev)
+    st = load_library().mla_quantize_e4m3(_ptr(x), x.numel(), _ptr(workspace), workspace.numel(), _ptr(codes),
+                                          _ptr(scale), _stream())
+    _check("mla_quantize_e4m3", st)
+    return codes, scale
+
+
+def mla_absorb_q_fp8(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk_codes: torch.Tensor, w_scale: float,
+                     q_lat: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_lat [N,H,d_c+d_rope] bf16 from bf16 q_nope/q_rope and e4m3 W_UK codes [H,d_c,d_nope] (mla_absorb_q_fp8)."""
+    N, H, dn = q_nope.shape
+    dr = q_rope.shape[2]
+    dc = w_uk_codes.shape[1]
+    dev = q_nope.device
+    _need(q_nope, "q_nope", dtype=torch.bfloat16, device=dev)
+    _need(q_rope, "q_rope", dtype=torch.bfloat16, device=dev)
+    _need(w_uk_codes, "w_uk_codes", dtype=torch.uint8, device=dev)
+    if tuple(w_uk_codes.shape) != (H, dc, dn) or tuple(q_rope.shape[:2]) != (N, H):
+        raise ValueError("expected w_uk_codes [H, d_c, d_nope] and q_rope [N, H, d_rope]")
+    if q_lat is None:
+        q_lat = torch.empty((N, H, dc + dr), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(fp8_workspace_size(N * H * dn), dtype=torch.uint8, device=dev)
+    st = load_library().mla_absorb_q_fp8(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk_codes), float(w_scale), N, H, dn, dr,
+                                         dc, _ptr(workspace), workspace.numel(), _ptr(q_lat), _stream())
+    _check("mla_absorb_q_fp8", st)
+    return q_lat
+
+
+def mla_out_uv_fp8(o_lat: torch.Tensor, w_uv_t_codes: torch.Tensor, w_scale: float,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out [N,H,d_v] bf16 from bf16 o_lat [N,H,d_c] and e4m3 W_UV^T codes [H,d_v,d_c] (mla_out_uv_fp8)."""
+    N, H, dc = o_lat.shape
+    dv = w_uv_t_codes.shape[1]
+    dev = o_lat.device
+    _need(o_lat, "o_lat", dtype=torch.bfloat16, device=dev)
+    _need(w_uv_t_codes, "w_uv_t_codes", dtype=torch.uint8, device=dev)
+    if tuple(w_uv_t_codes.shape) != (H, dv, dc):
+        raise ValueError("expected w_uv_t_codes [H, d_v, d_c]")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(fp8_workspace_size(N * H * dc), dtype=torch.uint8, device=dev)
+    st = load_library().mla_out_uv_fp8(_ptr(o_lat), _ptr(w_uv_t_codes), float(w_scale), N, H, dc, dv,
+                                       _ptr(workspace), workspace.numel(), _ptr(out), _stream())
+    _check("mla_out_uv_fp8", st)
+    return out

@@ -45,7 +45,7 @@ const char* mla_status_string(mla_status_t status) {
   return "unknown status";
 }
 
-int mla_abi_version(void) { return 4; }
+int mla_abi_version(void) { return 5; }
 
 size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
   return workspace_size(total_splits, s_q, H);
@@ -319,6 +319,74 @@ mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d
   if ((long long)N > 65535LL * 64) return MLA_ERR_UNSUPPORTED;
   return from_hip(mla::launch_out_uv(o_lat, w_uv, N, H, d_c, d_v, dtype == MLA_BF16, out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+// ---- FP8 products for the absorption ----
+
+namespace {
+constexpr size_t kFp8ScaleOff = (size_t)mla::kFp8QuantParts * 4;  // after the partial maxima
+constexpr size_t kFp8CodesOff = kFp8ScaleOff + 256;                 // after the scale
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+mla_status_t quantize_into(const void* x, size_t n, void* workspace, uint8_t* codes, float* scale,
+                           hipStream_t st) {
+  return from_hip(mla::launch_quantize_e4m3(x, n, static_cast<float*>(workspace), codes, scale, st));
+}
+}  // namespace
+
+size_t mla_fp8_workspace_size(size_t n_elems) {
+  if (n_elems == 0) return 0;
+  return kFp8CodesOff + (n_elems + 255) / 256 * 256;
+}
+
+mla_status_t mla_quantize_e4m3(const void* x, size_t n, void* workspace, size_t workspace_bytes, uint8_t* codes,
+                               float* scale, void* stream) {
+  if (!x || !codes || !scale || n == 0) return MLA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < kFp8ScaleOff) return MLA_ERR_WORKSPACE;
+  return quantize_into(x, n, workspace, codes, scale, static_cast<hipStream_t>(stream));
+}
+
+mla_status_t mla_absorb_q_fp8(const void* q_nope, const void* q_rope, const uint8_t* w_uk, float w_scale, int N,
+                              int H, int d_nope, int d_rope, int d_c, void* workspace, size_t workspace_bytes,
+                              void* q_lat, void* stream) {
+  if (!q_nope || !w_uk || !q_lat || (d_rope > 0 && !q_rope)) return MLA_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || d_nope <= 0 || d_c <= 0 || d_rope < 0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(w_scale) || !(w_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (H > kMaxBmmHeads || d_nope > kMaxBmmDim || d_c > kMaxBmmDim || d_rope > kMaxBmmDim) return MLA_ERR_UNSUPPORTED;
+  if (d_nope % 16 || d_c % 4 || d_rope % 4) return MLA_ERR_UNSUPPORTED;
+  if ((long long)N > 65535LL * 32) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(q_nope, 16) || !aligned(w_uk, 8) || !aligned(q_lat, 8)) return MLA_ERR_INVALID_ARG;
+  const size_t n = (size_t)N * H * d_nope;
+  if (!workspace || workspace_bytes < mla_fp8_workspace_size(n)) return MLA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* scale = reinterpret_cast<float*>(ws + kFp8ScaleOff);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + kFp8CodesOff);
+  const mla_status_t q = quantize_into(q_nope, n, ws, codes, scale, st);
+  if (q != MLA_OK) return q;
+  return from_hip(mla::launch_bmm_fp8(codes, scale, w_uk, w_scale, N, H, d_nope, d_c, q_lat, d_c + d_rope, q_rope,
+                                      d_rope, st));
+}
+
+mla_status_t mla_out_uv_fp8(const void* o_lat, const uint8_t* w_uv_t, float w_scale, int N, int H, int d_c, int d_v,
+                            void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  if (!o_lat || !w_uv_t || !out) return MLA_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || d_c <= 0 || d_v <= 0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(w_scale) || !(w_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (H > kMaxBmmHeads || d_c > kMaxBmmDim || d_v > kMaxBmmDim) return MLA_ERR_UNSUPPORTED;
+  if (d_c % 16 || d_v % 4) return MLA_ERR_UNSUPPORTED;
+  if ((long long)N > 65535LL * 32) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(o_lat, 16) || !aligned(w_uv_t, 8) || !aligned(out, 8)) return MLA_ERR_INVALID_ARG;
+  const size_t n = (size_t)N * H * d_c;
+  if (!workspace || workspace_bytes < mla_fp8_workspace_size(n)) return MLA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* scale = reinterpret_cast<float*>(ws + kFp8ScaleOff);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + kFp8CodesOff);
+  const mla_status_t q = quantize_into(o_lat, n, ws, codes, scale, st);
+  if (q != MLA_OK) return q;
+  return from_hip(mla::launch_bmm_fp8(codes, scale, w_uv_t, w_scale, N, H, d_c, d_v, out, d_v, nullptr, 0, st));
 }
 
 }  // extern "C"

@@ -1,0 +1,163 @@
+// FP8 (e4m3) batched products around absorbed-MLA decode, gfx950.
+//
+// "DeepSeekV2之MLA", the SGLang history section: with FP8 weights w_kc and
+// w_vc, the query absorption and the output projection run as bmm_fp8 of an
+// activation quantised to e4m3 on the fly (one scale per tensor) against the
+// e4m3 weights and their scale, with a bf16 result.
+//
+//   amax_kernel      per-workgroup max |x| of a bf16 tensor
+//   quantize_kernel  s = max|x| / 448 (1 for an all-zero tensor), codes =
+//                    e4m3(x / s), nearest with ties to even, |x / s| clamped
+//                    to 448 (v_cvt_pk_fp8_f32 on the fp32 quotient)
+//   bmm_kernel       out[n,h,j] = s_x * s_w * sum_k X[n,h,k] W[h,j,k] over
+//                    e4m3 codes, v_mfma_f32_32x32x16_fp8_fp8 with fp32
+//                    accumulation, bf16 result; optionally a bf16 tail copied
+//                    after the j columns of each row (the RoPE part of q_lat).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+
+constexpr int kAmaxThreads = 256;
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float m = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+// partials[blockIdx.x] = max |x| over the elements this workgroup visits.
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const __bf16* __restrict__ x, size_t n,
+                                                           float* __restrict__ partials) {
+  __shared__ float red[kAmaxThreads / 64];
+  float m = 0.f;
+  const size_t stride = (size_t)gridDim.x * kAmaxThreads;
+  const size_t n8 = n / 8;
+  for (size_t i = (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n8; i += stride) {
+    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(x + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
+  }
+  for (size_t i = 8 * n8 + (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n; i += stride)
+    m = fmaxf(m, fabsf((float)x[i]));
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// codes[i] = e4m3(x[i] / s) with s from the partial maxima; workgroup 0 writes s.
+__global__ __launch_bounds__(kAmaxThreads) void quantize_kernel(const __bf16* __restrict__ x, size_t n,
+                                                               const float* __restrict__ partials, int n_parts,
+                                                               uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scale_out) {
+  __shared__ float red[kAmaxThreads / 64];
+  float m = (int)threadIdx.x < n_parts ? partials[threadIdx.x] : 0.f;
+  m = block_max(m, red);
+  const float s = m > 0.f ? m / 448.f : 1.f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  const size_t stride = (size_t)gridDim.x * kAmaxThreads;
+  const size_t n8 = n / 8;
+  for (size_t i = (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n8; i += stride) {
+    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(x + 8 * i);
+    uint32_t lo = e4m3_pair((float)v[0] / s, (float)v[1] / s) | (e4m3_pair((float)v[2] / s, (float)v[3] / s) << 16);
+    uint32_t hi = e4m3_pair((float)v[4] / s, (float)v[5] / s) | (e4m3_pair((float)v[6] / s, (float)v[7] / s) << 16);
+    *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(lo, hi);
+  }
+  for (size_t i = 8 * n8 + (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n; i += stride)
+    codes[i] = (uint8_t)e4m3_pair((float)x[i] / s, 0.f);
+}
+
+// One wave per 32 (j) x 32 (n) output tile of one head; four waves per
+// workgroup cover 128 consecutive j. A = W rows (j), B = X rows (n), both as
+// 8 consecutive codes per lane (k = 8 * (lane >> 5) .. +8 of a 16-deep step).
+__global__ __launch_bounds__(256) void bmm_kernel(const uint8_t* __restrict__ X, const float* __restrict__ x_scale,
+                                                 const uint8_t* __restrict__ W, float w_scale, int N, int H, int K,
+                                                 int J, __bf16* __restrict__ out, int out_stride,
+                                                 const __bf16* __restrict__ tail_src, int tail) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hi32 = lane >> 5;
+  const int h = blockIdx.z;
+  const int n0 = blockIdx.y * 32;
+  const int j0 = blockIdx.x * 128 + wave * 32;
+  const int n = n0 + r32;
+  const int nc = min(n, N - 1);
+  const int jc = min(j0 + r32, J - 1);
+  const uint8_t* xa = X + ((size_t)nc * H + h) * K + 8 * hi32;
+  const uint8_t* wa = W + ((size_t)h * J + jc) * K + 8 * hi32;
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int k = 0; k < K; k += 16) {
+    const long a = *reinterpret_cast<const long*>(wa + k);
+    const long b = *reinterpret_cast<const long*>(xa + k);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, acc, 0, 0, 0);
+  }
+  const float sc = *x_scale * w_scale;
+  // acc[r] = out^T[j0 + 8(r>>2) + 4*hi32 + (r&3)][n].
+  if (n < N) {
+    __bf16* orow = out + ((size_t)n * H + h) * out_stride;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int j = j0 + 8 * q4 + 4 * hi32;
+      if (j + 3 < J) {
+        bf16x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * q4 + e] * sc);
+        *reinterpret_cast<bf16x4_t*>(orow + j) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < J) orow[j + e] = (__bf16)(acc[4 * q4 + e] * sc);
+      }
+    }
+    // The tail (q_lat's RoPE part) once per row, by the first column block.
+    if (tail > 0 && blockIdx.x == 0 && wave == 0)
+      for (int e = hi32; e < tail; e += 2) orow[J + e] = tail_src[((size_t)n * H + h) * tail + e];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_e4m3(const void* x, size_t n, float* partials, uint8_t* codes, float* scale,
+                                hipStream_t stream) {
+  const size_t groups = (n / 8 + kAmaxThreads - 1) / kAmaxThreads;
+  const int parts = (int)(groups < 1 ? 1 : (groups > kFp8QuantParts ? kFp8QuantParts : groups));
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)parts), dim3(kAmaxThreads), 0, stream,
+                     static_cast<const __bf16*>(x), n, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)parts), dim3(kAmaxThreads), 0, stream,
+                     static_cast<const __bf16*>(x), n, partials, parts, codes, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bmm_fp8(const uint8_t* X, const float* x_scale, const uint8_t* W, float w_scale, int N, int H,
+                          int K, int J, void* out, int out_stride, const void* tail_src, int tail,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)((J + 127) / 128), (unsigned)((N + 31) / 32), (unsigned)H);
+  hipLaunchKernelGGL(bmm_kernel, grid, dim3(256), 0, stream, X, x_scale, W, w_scale, N, H, K, J,
+                     static_cast<__bf16*>(out), out_stride, static_cast<const __bf16*>(tail_src), tail);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -54,6 +54,15 @@ hipError_t launch_expand(const void* cache, const int32_t* btab_row, int t0, int
 hipError_t launch_prefill_attn(const void* q_nope, const void* q_rope, int s_q, int H, const void* K, const void* V,
                                const void* R, int n, int n_stride, int k_pos0, int q_pos0, int causal, float scale,
                                void* o, float* lse, hipStream_t stream);
+// FP8 products for the absorption: per-tensor e4m3 quantisation of a bf16
+// tensor (partials: kFp8QuantParts floats of scratch) and the per-head e4m3
+// product out[n,h,j] = x_scale * w_scale * sum_k X[n,h,k] W[h,j,k].
+constexpr int kFp8QuantParts = 256;
+hipError_t launch_quantize_e4m3(const void* x, size_t n, float* partials, uint8_t* codes, float* scale,
+                                hipStream_t stream);
+hipError_t launch_bmm_fp8(const uint8_t* X, const float* x_scale, const uint8_t* W, float w_scale, int N, int H,
+                          int K, int J, void* out, int out_stride, const void* tail_src, int tail,
+                          hipStream_t stream);
 hipError_t launch_prefill_merge(const void* o_part, const float* lse_part, int n_parts, int rows, void* o, float* lse,
                                 hipStream_t stream);
 

@@ -78,8 +78,8 @@ def kernel_stats(folder: str):
              float(r["Percentage"])) for r in rows]
 
 
-def counter_medians(folder: str, counter: str):
-    """Median counter value (KiB) per kernel name, and the largest copy kernel's value."""
+def counter_medians(folder: str, counter: str, need_copy: bool = True):
+    """Median counter value per kernel name, and the largest copy kernel's value."""
     rows = [r for r in csv.DictReader(open(_one(folder, "*counter_collection.csv")))
             if r["Counter_Name"] == counter]
     per = {}
@@ -90,9 +90,12 @@ def counter_medians(folder: str, counter: str):
             copy.append((int(r["Grid_Size"]), v))
         else:
             per.setdefault(r["Kernel_Name"], []).append(v)
+    meds = {k: statistics.median(v) for k, v in per.items()}
+    if not need_copy:
+        return meds, None
     big_grid = max(g for g, _ in copy)
     copy_vals = [v for g, v in copy if g == big_grid]
-    return {k: statistics.median(v) for k, v in per.items()}, statistics.median(copy_vals)
+    return meds, statistics.median(copy_vals)
 
 
 def main():
@@ -108,6 +111,8 @@ def main():
     ap.add_argument("--kernel", default=DECODE_KERNEL, help="the dominant kernel (a substring of its name)")
     ap.add_argument("--sources", default=",".join(DECODE_SOURCES),
                     help="its sources, relative to the package, for the hash")
+    ap.add_argument("--mfma", default=None,
+                    help="a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv` run of --pmc-command")
     ap.add_argument("--algorithmic-bytes", type=float, default=None)
     ap.add_argument("--bench-output", default=None,
                     help="stdout of the kernel-trace run (bench.py's JSON line), for the event-vs-trace check")
@@ -132,6 +137,9 @@ def main():
         lines += [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}",
                   f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}"]
         summary += f" --fetch <fetch> --write <write> --copy-mb {args.copy_mb} --pmc-command '{pmc_cmd}'"
+    if args.mfma:
+        lines += [f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d <mfma> -o run -- {pmc_cmd}"]
+        summary += " --mfma <mfma>"
     lines += [summary + " --out <this file>", "```", ""]
     lines += ["## Kernel durations (kernel trace)", "",
               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
@@ -177,6 +185,16 @@ def main():
                          f"{(rb + wb) / 1e6:.1f} |")
             if args.kernel in _demangle_nested(name):
                 total = rb + wb
+    if args.mfma:
+        busy, _ = counter_medians(args.mfma, "SQ_VALU_MFMA_BUSY_CYCLES", need_copy=False)
+        active, _ = counter_medians(args.mfma, "GRBM_GUI_ACTIVE", need_copy=False)
+        lines += ["", "## MFMA busy time (counters)", "",
+                  "SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs, over GRBM_GUI_ACTIVE x 1024 (the share "
+                  "of SIMD-cycles with the matrix unit busy while the kernel ran):", "",
+                  "| kernel | MFMA busy | GUI active cycles |", "|---|---|---|"]
+        for name in sorted(n for n in busy if _ours(n)):
+            if active.get(name):
+                lines.append(f"| {_short(name)} | {100 * busy[name] / (active[name] * 1024):.1f}% | {active[name]:.0f} |")
     lines += [""]
     if args.algorithmic_bytes:
         lines += [f"Algorithmic bytes per launch of {args.kernel}: {args.algorithmic_bytes / 1e6:.1f} MB.", ""]

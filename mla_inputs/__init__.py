@@ -323,3 +323,30 @@ def random_tiny_mla(seed: int, T: int = 5, D: int = 32, H: int = 3, NOPE: int = 
     )
     out.update(T=T, D=D, H=H, NOPE=NOPE, ROPE=ROPE, DV=DV, DC=DC)
     return out
+
+
+def fp8_bmm_case(N: int, H: int = 128, d_nope: int = 128, d_rope: int = 64, d_c: int = 512, d_v: int = 128,
+                 seed: int = 170) -> dict:
+    """Inputs of the FP8 absorption products: bf16 activations q_nope
+    [N,H,d_nope], q_rope [N,H,d_rope] ~ N(0,1) and o_lat [N,H,d_c] ~ N(0,1),
+    and FP8 weights: W_UK [H,d_c,d_nope] and W_UV [H,d_c,d_v] drawn
+    N(0, 1/d_c), each scaled by max|W| / 448 and rounded to e4m3 by torch's
+    float8_e4m3fn conversion (the weight stored once, as a serving engine
+    loads it). Keys: q_nope, q_rope, o_lat (bf16 tensors), w_uk_codes
+    [H,d_c,d_nope], w_uv_t_codes [H,d_v,d_c] (W_UV transposed) uint8, and the
+    float scales w_uk_scale, w_uv_scale."""
+    rng = np.random.default_rng(seed)
+
+    def weight(shape):
+        w = rng.standard_normal(shape, dtype=np.float32) * np.float32(1.0 / math.sqrt(d_c))
+        t = torch.from_numpy(w)
+        s = float(t.abs().max()) / FP8_E4M3_MAX
+        return (t / s).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), s
+
+    q_nope = _round_to(rng.standard_normal((N, H, d_nope), dtype=np.float32), torch.bfloat16)
+    q_rope = _round_to(rng.standard_normal((N, H, d_rope), dtype=np.float32), torch.bfloat16)
+    o_lat = _round_to(rng.standard_normal((N, H, d_c), dtype=np.float32), torch.bfloat16)
+    w_uk, s_uk = weight((H, d_c, d_nope))
+    w_uv, s_uv = weight((H, d_c, d_v))
+    return dict(q_nope=q_nope, q_rope=q_rope, o_lat=o_lat, w_uk_codes=w_uk, w_uk_scale=s_uk,
+                w_uv_t_codes=w_uv.transpose(1, 2).contiguous(), w_uv_scale=s_uv)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 4
+    assert mla.abi_version() == 5
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -223,3 +223,36 @@ def test_prefill_validation(lib):
     need = mla.prefill_workspace_size(4, 16, 64, 4)
     assert call(wsb=need - 1) == WORKSPACE
     assert mla.prefill_workspace_size(0, 16, 64, 4) == 0
+
+
+def test_fp8_products_validation(lib):
+    ws = mla.fp8_workspace_size(4 * 8 * 128)
+    assert ws >= 4 * 8 * 128 and mla.fp8_workspace_size(0) == 0
+
+    def absorb(**kw):
+        a = dict(qn=FAKE, qr=FAKE, w=FAKE, s=0.5, N=4, H=8, dn=128, dr=64, dc=512, ws=FAKE, wsb=1 << 30, out=FAKE)
+        a.update(kw)
+        return lib.mla_absorb_q_fp8(a["qn"], a["qr"], a["w"], a["s"], a["N"], a["H"], a["dn"], a["dr"], a["dc"],
+                                    a["ws"], a["wsb"], a["out"], None)
+    assert absorb(qn=None) == INVALID
+    assert absorb(qr=None) == INVALID
+    assert absorb(s=0.0) == INVALID and absorb(s=float("nan")) == INVALID
+    assert absorb(N=0) == INVALID
+    assert absorb(dn=120) == UNSUPPORTED     # not a multiple of 16
+    assert absorb(dc=510) == UNSUPPORTED     # not a multiple of 4
+    assert absorb(H=1025) == UNSUPPORTED
+    assert absorb(qn=ctypes.c_void_p(0x1008)) == INVALID  # q_nope not 16-byte aligned
+    assert absorb(ws=None) == WORKSPACE
+    assert absorb(wsb=mla.fp8_workspace_size(4 * 8 * 128) - 1) == WORKSPACE
+
+    def out_uv(**kw):
+        a = dict(o=FAKE, w=FAKE, s=0.5, N=4, H=8, dc=512, dv=128, ws=FAKE, wsb=1 << 30, out=FAKE)
+        a.update(kw)
+        return lib.mla_out_uv_fp8(a["o"], a["w"], a["s"], a["N"], a["H"], a["dc"], a["dv"], a["ws"], a["wsb"],
+                                  a["out"], None)
+    assert out_uv(w=None) == INVALID
+    assert out_uv(dc=100) == UNSUPPORTED
+    assert out_uv(out=ctypes.c_void_p(0x1004)) == INVALID
+    assert out_uv(wsb=mla.fp8_workspace_size(4 * 8 * 512) - 1) == WORKSPACE
+    assert lib.mla_quantize_e4m3(FAKE, 0, FAKE, 1024, FAKE, FAKE, None) == INVALID
+    assert lib.mla_quantize_e4m3(FAKE, 64, FAKE, 1023, FAKE, FAKE, None) == WORKSPACE

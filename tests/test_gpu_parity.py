@@ -554,3 +554,54 @@ def test_prefill_8k_sampled():
 def test_extend_32k_sampled():
     # The extend bench workload: 512 new tokens after 32K, five chunks merged by LSE.
     _prefill_sampled(32768 + 512, 512, 8192, (0, 127), seed=161)
+
+
+# ---------------------------------------------------------------------------
+# FP8 products for the absorption
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(3, 5, 16), (64, 128, 128), (7, 3, 37), (1, 1, 1)])
+def test_quantize_e4m3_codes_bitexact(shape):
+    # The codes are integers decided in fp32 on both sides: compare exactly.
+    rng = np.random.default_rng(171 + len(shape) + shape[-1])
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(3.0)
+    x.reshape(-1)[::11] *= np.float32(1e-3)   # values in the subnormal codes
+    x.reshape(-1)[1::13] = -0.0
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scale = mla.quantize_e4m3(xb.cuda())
+    torch.cuda.synchronize()
+    ref_codes, ref_scale = orc.quantize_e4m3(xb.float().numpy())
+    assert float(scale.item()) == float(ref_scale)
+    got = codes.cpu().numpy()
+    bad = np.flatnonzero(got.reshape(-1) != ref_codes.reshape(-1))
+    assert bad.size == 0, (bad[:8], got.reshape(-1)[bad[:8]], ref_codes.reshape(-1)[bad[:8]])
+
+
+def _fp8_compare(got, ref, label):
+    g = to_np(got)
+    rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+    mabs = np.max(np.abs(g - ref))
+    print(f"[parity] {label} rel_l2={rel:.3e} max_abs={mabs:.3e}", flush=True)
+    assert np.all(np.isfinite(g)) and rel <= 5e-3 and mabs <= 2e-2 * max(1.0, np.max(np.abs(ref))), (label, rel, mabs)
+
+
+@pytest.mark.parametrize("N,H", [(64, 128), (5, 3), (33, 16)])
+def test_absorb_q_fp8(N, H):
+    from mla_inputs import fp8_bmm_case
+    c = fp8_bmm_case(N, H=H, seed=172 + N)
+    q_lat = mla.mla_absorb_q_fp8(c["q_nope"].cuda(), c["q_rope"].cuda(), c["w_uk_codes"].cuda(), c["w_uk_scale"])
+    torch.cuda.synchronize()
+    ref = orc.absorb_q_fp8(c["q_nope"].float().numpy(), c["q_rope"].float().numpy(), c["w_uk_codes"].numpy(),
+                           c["w_uk_scale"])
+    _fp8_compare(q_lat[..., :512], ref[..., :512], f"absorb_q_fp8 N={N} H={H}")
+    assert torch.equal(q_lat[..., 512:].cpu(), c["q_rope"])  # the RoPE part is copied
+
+
+@pytest.mark.parametrize("N,H", [(64, 128), (5, 3), (33, 16)])
+def test_out_uv_fp8(N, H):
+    from mla_inputs import fp8_bmm_case
+    c = fp8_bmm_case(N, H=H, seed=173 + N)
+    out = mla.mla_out_uv_fp8(c["o_lat"].cuda(), c["w_uv_t_codes"].cuda(), c["w_uv_scale"])
+    torch.cuda.synchronize()
+    ref = orc.out_uv_fp8(c["o_lat"].float().numpy(), c["w_uv_t_codes"].numpy(), c["w_uv_scale"])
+    _fp8_compare(out, ref, f"out_uv_fp8 N={N} H={H}")
