@@ -53,7 +53,7 @@ DEFAULT_WORKLOAD_TEXT = ("batched absorbed-MLA decode B=64 x ctx 4096, s_q=1, H=
 # --workload name -> seeded input recipe (mla_inputs.config_case index, mtp<s_q>, or the
 # top-k shape: B=64 histories of 16384 tokens, 2048 selected per new token)
 WORKLOADS = {"batched": 2, "single": 1, "mtp": 3, "long": 4, "mtp4": "mtp4", "mtp8": "mtp8", "topk": "topk",
-             "fp8": "fp8", "prefill": "prefill", "extend": "extend"}
+             "fp8": "fp8", "prefill": "prefill", "extend": "extend", "absorb_fp8": "absorb_fp8"}
 TOPK_SHAPE = dict(B=64, L=16384, topk=2048)
 # Expanded path (prefill / extend), B=1, H=128: a fresh 8K-token prefill, and
 # 512 new tokens after a 32K-token prefix expanded 8192 tokens at a time.
@@ -280,6 +280,95 @@ def prefill_main(args):
     print(json.dumps(out), flush=True)
 
 
+def absorb_main(args):
+    """The absorption products around one decode step with FP8 weights
+    (mla_absorb_q_fp8 then mla_out_uv_fp8) at B=64 new tokens, H=128: weight
+    reads dominate, so the roofline is HBM. The bf16 pair (mla_absorb_q,
+    mla_out_uv) on the same shapes is timed beside it."""
+    import torch
+
+    import mla_decode_fwd_amd as mla
+    from mla_decode_fwd_amd import accounting as acc
+    from mla_inputs import fp8_bmm_case
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mla.load_library()
+    N, H, dn, dr, dc, dv = 64, 128, 128, 64, 512, 128
+    c = fp8_bmm_case(N, H=H, seed=175)
+    qn, qr, ol = c["q_nope"].to(dev), c["q_rope"].to(dev), c["o_lat"].to(dev)
+    wk, wv = c["w_uk_codes"].to(dev), c["w_uv_t_codes"].to(dev)
+    ws_a = torch.empty(mla.fp8_workspace_size(N * H * dn), dtype=torch.uint8, device=dev)
+    ws_o = torch.empty(mla.fp8_workspace_size(N * H * dc), dtype=torch.uint8, device=dev)
+    q_lat = torch.empty((N, H, dc + dr), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+    # bf16 weights of the same shapes for the comparison pair (values are not compared here)
+    w_uk16 = torch.randn((H, dc, dn), dtype=torch.bfloat16, device=dev)
+    w_uv16 = torch.randn((H, dc, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step_fp8():
+        mla.mla_absorb_q_fp8(qn, qr, wk, c["w_uk_scale"], q_lat=q_lat, workspace=ws_a)
+        mla.mla_out_uv_fp8(ol, wv, c["w_uv_scale"], out=out, workspace=ws_o)
+
+    def step_bf16():
+        mla.mla_absorb_q(qn, qr, w_uk16, q_lat=q_lat)
+        mla.mla_out_uv(ol, w_uv16, out=out)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
+
+    gpu_ms, ms_per_step = timed(step_fp8)
+    bf16_ms, _ = timed(step_bf16)
+    flops = 2.0 * N * H * dc * (dn + dv)
+    nbytes = float(H * dc * (dn + dv)          # e4m3 weights
+                   + N * H * (dn + dr + dc) * 2  # bf16 activations in
+                   + N * H * (dc + dr + dv) * 2)  # bf16 results out
+    rf = acc.roofline(flops, nbytes, gpu_ms / 1e3)
+    step_rf = acc.roofline(flops, nbytes, ms_per_step / 1e3)
+    out_json = {
+        "metric": "MLA absorption products with FP8 weights, GB/s (% HBM roofline)",
+        "value": round(step_rf["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32, bf16 in/out", "data": "synthetic",
+        "config": {"workload": f"mla_absorb_q_fp8 + mla_out_uv_fp8, N={N} new tokens, H={H}, d_nope={dn}, "
+                               f"d_rope={dr}, d_c={dc}, d_v={dv}, per-tensor activation scales, e4m3 weights",
+                   "N": N, "H": H, "parallelism": "single GPU"},
+        "roofline": {"bound": rf["bound"], "achieved": round(rf["achieved"], 1), "peak": rf["peak"],
+                     "unit": rf["unit"], "frac": round(rf["frac"], 4), "traffic": None,
+                     "kernel": "amax + quantise + bmm, twice", "call_us": round(gpu_ms * 1e3, 2),
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
+        "bf16_pair_us": round(bf16_ms * 1e3, 2),
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle ...")
+        from oracle import mla_oracle as orc
+        args_a = (c["q_nope"].float().numpy(), c["q_rope"].float().numpy(), c["w_uk_codes"].numpy(), c["w_uk_scale"])
+        args_o = (c["o_lat"].float().numpy(), c["w_uv_t_codes"].numpy(), c["w_uv_scale"])
+        secs, n = 0.0, 0
+        while secs < min(args.cpu_budget, 10.0) or n == 0:
+            t0 = time.perf_counter()
+            orc.absorb_q_fp8(*args_a)
+            orc.out_uv_fp8(*args_o)
+            secs += time.perf_counter() - t0
+            n += 1
+        out_json["cpu_baseline"] = {"value": n * nbytes / secs / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+                                    "kind": "oracle", "cpu": cpu_model(),
+                                    "sample": f"{n} x the whole workload (absorb_q_fp8 + out_uv_fp8), fp64 numpy, "
+                                              f"{secs:.1f} s"}
+    print(json.dumps(out_json), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +387,9 @@ def main():
         sys.exit(2)
     if args.workload in PREFILL_SHAPES:
         prefill_main(args)
+        return
+    if args.workload == "absorb_fp8":
+        absorb_main(args)
         return
 
     import torch

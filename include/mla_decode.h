@@ -332,13 +332,15 @@ mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d
  *
  * Codes are e4m3 "fn" (bias 7, no infinities, NaN 0x7F/0xFF, largest finite
  * 448). Per-tensor dynamic quantisation of a bf16 tensor x:
- *   s = max|x| / 448 (fp32; 1 when x is all zero),
- *   code = nearest e4m3 value of the fp32 quotient x / s, ties to even,
- *          magnitudes clamped to 448.
+ *   r = 448 / max|x| (fp32; max|x| taken as at least 2^-100; r = 1 when x is
+ *       all zero), code = nearest e4m3 value of the fp32 product x * r, ties
+ *       to even, magnitudes clamped to 448; the dequantisation scale is
+ *       s = 1 / r (fp32).
  */
 
-/* Workspace bytes for quantising n_elems elements inside mla_absorb_q_fp8 /
-   mla_out_uv_fp8 (partial maxima, the scale and the codes); 0 for 0. */
+/* Workspace bytes of mla_absorb_q_fp8 / mla_out_uv_fp8 for an activation of
+   n_elems elements: the partial maxima of the per-tensor scale (1 KB; the
+   products quantise the activation as they load it); 0 for 0. */
 size_t mla_fp8_workspace_size(size_t n_elems);
 
 /*
@@ -351,7 +353,7 @@ mla_status_t mla_quantize_e4m3(const void* x, size_t n, void* workspace, size_t 
 
 /*
  * mla_absorb_q with FP8 operands:
- *   q_lat[n,h,0:d_c] = bf16( s_q * w_scale * sum_d e4m3(q_nope)[n,h,d] * w_uk[h,c,d] )
+ *   q_lat[n,h,0:d_c] = bf16( s * w_scale * sum_d e4m3(q_nope)[n,h,d] * w_uk[h,c,d] )
  *   q_lat[n,h,d_c:]  = q_rope[n,h,:]  (copied)
  * where q_nope is quantised per tensor as above.
  *   q_nope [N, H, d_nope] bf16 (16-byte aligned), q_rope [N, H, d_rope] bf16;
@@ -366,7 +368,7 @@ mla_status_t mla_absorb_q_fp8(const void* q_nope, const void* q_rope, const uint
 
 /*
  * mla_out_uv with FP8 operands:
- *   out[n,h,e] = bf16( s_o * w_scale * sum_c e4m3(o_lat)[n,h,c] * w_uv_t[h,e,c] )
+ *   out[n,h,e] = bf16( s * w_scale * sum_c e4m3(o_lat)[n,h,c] * w_uv_t[h,e,c] )
  * where o_lat is quantised per tensor as above and the weight is W_UV stored
  * transposed, [H, d_v, d_c] e4m3 codes (prepared once, as the pages' history
  * transposes the MLA weights offline), so that both operands run along d_c.

@@ -324,8 +324,7 @@ mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d
 // ---- FP8 products for the absorption ----
 
 namespace {
-constexpr size_t kFp8ScaleOff = (size_t)mla::kFp8QuantParts * 4;  // after the partial maxima
-constexpr size_t kFp8CodesOff = kFp8ScaleOff + 256;                 // after the scale
+constexpr size_t kFp8ScaleOff = (size_t)mla::kFp8QuantParts * 4;  // the partial maxima
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 mla_status_t quantize_into(const void* x, size_t n, void* workspace, uint8_t* codes, float* scale,
@@ -336,7 +335,7 @@ mla_status_t quantize_into(const void* x, size_t n, void* workspace, uint8_t* co
 
 size_t mla_fp8_workspace_size(size_t n_elems) {
   if (n_elems == 0) return 0;
-  return kFp8CodesOff + (n_elems + 255) / 256 * 256;
+  return kFp8ScaleOff;  // the partial maxima; the activation is quantised as the product loads it
 }
 
 mla_status_t mla_quantize_e4m3(const void* x, size_t n, void* workspace, size_t workspace_bytes, uint8_t* codes,
@@ -359,14 +358,8 @@ mla_status_t mla_absorb_q_fp8(const void* q_nope, const void* q_rope, const uint
   if (!aligned(q_nope, 16) || !aligned(w_uk, 8) || !aligned(q_lat, 8)) return MLA_ERR_INVALID_ARG;
   const size_t n = (size_t)N * H * d_nope;
   if (!workspace || workspace_bytes < mla_fp8_workspace_size(n)) return MLA_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* scale = reinterpret_cast<float*>(ws + kFp8ScaleOff);
-  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + kFp8CodesOff);
-  const mla_status_t q = quantize_into(q_nope, n, ws, codes, scale, st);
-  if (q != MLA_OK) return q;
-  return from_hip(mla::launch_bmm_fp8(codes, scale, w_uk, w_scale, N, H, d_nope, d_c, q_lat, d_c + d_rope, q_rope,
-                                      d_rope, st));
+  return from_hip(mla::launch_bmm_fp8(q_nope, static_cast<float*>(workspace), w_uk, w_scale, N, H, d_nope, d_c,
+                                      q_lat, d_c + d_rope, q_rope, d_rope, static_cast<hipStream_t>(stream)));
 }
 
 mla_status_t mla_out_uv_fp8(const void* o_lat, const uint8_t* w_uv_t, float w_scale, int N, int H, int d_c, int d_v,
@@ -380,13 +373,8 @@ mla_status_t mla_out_uv_fp8(const void* o_lat, const uint8_t* w_uv_t, float w_sc
   if (!aligned(o_lat, 16) || !aligned(w_uv_t, 8) || !aligned(out, 8)) return MLA_ERR_INVALID_ARG;
   const size_t n = (size_t)N * H * d_c;
   if (!workspace || workspace_bytes < mla_fp8_workspace_size(n)) return MLA_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* scale = reinterpret_cast<float*>(ws + kFp8ScaleOff);
-  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + kFp8CodesOff);
-  const mla_status_t q = quantize_into(o_lat, n, ws, codes, scale, st);
-  if (q != MLA_OK) return q;
-  return from_hip(mla::launch_bmm_fp8(codes, scale, w_uv_t, w_scale, N, H, d_c, d_v, out, d_v, nullptr, 0, st));
+  return from_hip(mla::launch_bmm_fp8(o_lat, static_cast<float*>(workspace), w_uv_t, w_scale, N, H, d_c, d_v, out,
+                                      d_v, nullptr, 0, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -6,11 +6,13 @@
 // e4m3 weights and their scale, with a bf16 result.
 //
 //   amax_kernel      per-workgroup max |x| of a bf16 tensor
-//   quantize_kernel  s = max|x| / 448 (1 for an all-zero tensor), codes =
-//                    e4m3(x / s), nearest with ties to even, |x / s| clamped
-//                    to 448 (v_cvt_pk_fp8_f32 on the fp32 quotient)
+//   quantize_kernel  r = 448 / max|x| (max|x| at least 2^-100; r = 1 for an
+//                    all-zero tensor), codes = e4m3(x * r), nearest with ties
+//                    to even, |x * r| clamped to 448 (v_cvt_pk_fp8_f32 on the
+//                    fp32 product), dequantisation scale s = 1 / r
 //   bmm_kernel       out[n,h,j] = s_x * s_w * sum_k X[n,h,k] W[h,j,k] over
-//                    e4m3 codes, v_mfma_f32_32x32x16_fp8_fp8 with fp32
+//                    e4m3 codes (X quantised as it is loaded, from the
+//                    partial maxima), v_mfma_f32_32x32x16_fp8_fp8 with fp32
 //                    accumulation, bf16 result; optionally a bf16 tail copied
 //                    after the j columns of each row (the RoPE part of q_lat).
 
@@ -64,7 +66,7 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-// codes[i] = e4m3(x[i] / s) with s from the partial maxima; workgroup 0 writes s.
+// codes[i] = e4m3(x[i] * r) with r from the partial maxima; workgroup 0 writes s = 1 / r.
 __global__ __launch_bounds__(kAmaxThreads) void quantize_kernel(const __bf16* __restrict__ x, size_t n,
                                                                const float* __restrict__ partials, int n_parts,
                                                                uint8_t* __restrict__ codes,
@@ -72,27 +74,36 @@ __global__ __launch_bounds__(kAmaxThreads) void quantize_kernel(const __bf16* __
   __shared__ float red[kAmaxThreads / 64];
   float m = (int)threadIdx.x < n_parts ? partials[threadIdx.x] : 0.f;
   m = block_max(m, red);
-  const float s = m > 0.f ? m / 448.f : 1.f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  const float r = m > 0.f ? 448.f / fmaxf(m, 0x1p-100f) : 1.f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = 1.f / r;
   const size_t stride = (size_t)gridDim.x * kAmaxThreads;
   const size_t n8 = n / 8;
   for (size_t i = (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n8; i += stride) {
     const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(x + 8 * i);
-    uint32_t lo = e4m3_pair((float)v[0] / s, (float)v[1] / s) | (e4m3_pair((float)v[2] / s, (float)v[3] / s) << 16);
-    uint32_t hi = e4m3_pair((float)v[4] / s, (float)v[5] / s) | (e4m3_pair((float)v[6] / s, (float)v[7] / s) << 16);
+    uint32_t lo = e4m3_pair((float)v[0] * r, (float)v[1] * r) | (e4m3_pair((float)v[2] * r, (float)v[3] * r) << 16);
+    uint32_t hi = e4m3_pair((float)v[4] * r, (float)v[5] * r) | (e4m3_pair((float)v[6] * r, (float)v[7] * r) << 16);
     *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(lo, hi);
   }
   for (size_t i = 8 * n8 + (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n; i += stride)
-    codes[i] = (uint8_t)e4m3_pair((float)x[i] / s, 0.f);
+    codes[i] = (uint8_t)e4m3_pair((float)x[i] * r, 0.f);
 }
 
 // One wave per 32 (j) x 32 (n) output tile of one head; four waves per
 // workgroup cover 128 consecutive j. A = W rows (j), B = X rows (n), both as
 // 8 consecutive codes per lane (k = 8 * (lane >> 5) .. +8 of a 16-deep step).
-__global__ __launch_bounds__(256) void bmm_kernel(const uint8_t* __restrict__ X, const float* __restrict__ x_scale,
-                                                 const uint8_t* __restrict__ W, float w_scale, int N, int H, int K,
-                                                 int J, __bf16* __restrict__ out, int out_stride,
+// The activation arrives in bf16 and is quantised as it is loaded: every
+// workgroup first reduces the partial maxima to the tensor's scale s, then
+// converts its operand exactly as quantize_kernel does (so the codes equal
+// mla_quantize_e4m3's).
+__global__ __launch_bounds__(256) void bmm_kernel(const __bf16* __restrict__ X, const float* __restrict__ partials,
+                                                 int n_parts, const uint8_t* __restrict__ W, float w_scale, int N,
+                                                 int H, int K, int J, __bf16* __restrict__ out, int out_stride,
                                                  const __bf16* __restrict__ tail_src, int tail) {
+  __shared__ float red[4];
+  float m = (int)threadIdx.x < n_parts ? partials[threadIdx.x] : 0.f;
+  m = block_max(m, red);
+  const float r = m > 0.f ? 448.f / fmaxf(m, 0x1p-100f) : 1.f;
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi32 = lane >> 5;
@@ -102,17 +113,32 @@ __global__ __launch_bounds__(256) void bmm_kernel(const uint8_t* __restrict__ X,
   const int n = n0 + r32;
   const int nc = min(n, N - 1);
   const int jc = min(j0 + r32, J - 1);
-  const uint8_t* xa = X + ((size_t)nc * H + h) * K + 8 * hi32;
+  const __bf16* xa = X + ((size_t)nc * H + h) * K + 8 * hi32;
   const uint8_t* wa = W + ((size_t)h * J + jc) * K + 8 * hi32;
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int k = 0; k < K; k += 16) {
-    const long a = *reinterpret_cast<const long*>(wa + k);
-    const long b = *reinterpret_cast<const long*>(xa + k);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, acc, 0, 0, 0);
+  // Eight k-steps per round, all loads of a round issued before its
+  // products, so that the round waits on memory once.
+  auto step = [&](long a, const bf16x8_t& v) {
+    const uint32_t lo = e4m3_pair((float)v[0] * r, (float)v[1] * r) | (e4m3_pair((float)v[2] * r, (float)v[3] * r) << 16);
+    const uint32_t hi = e4m3_pair((float)v[4] * r, (float)v[5] * r) | (e4m3_pair((float)v[6] * r, (float)v[7] * r) << 16);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, (long)(((uint64_t)hi << 32) | lo), acc, 0, 0, 0);
+  };
+  int k = 0;
+  for (; k + 128 <= K; k += 128) {
+    long a[8];
+    bf16x8_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = *reinterpret_cast<const long*>(wa + k + 16 * u);
+      v[u] = *reinterpret_cast<const bf16x8_t*>(xa + k + 16 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) step(a[u], v[u]);
   }
-  const float sc = *x_scale * w_scale;
+  for (; k < K; k += 16) step(*reinterpret_cast<const long*>(wa + k), *reinterpret_cast<const bf16x8_t*>(xa + k));
+  const float sc = (1.f / r) * w_scale;
   // acc[r] = out^T[j0 + 8(r>>2) + 4*hi32 + (r&3)][n].
   if (n < N) {
     __bf16* orow = out + ((size_t)n * H + h) * out_stride;
@@ -138,10 +164,11 @@ __global__ __launch_bounds__(256) void bmm_kernel(const uint8_t* __restrict__ X,
 
 }  // namespace
 
+int amax_parts(size_t n);
+
 hipError_t launch_quantize_e4m3(const void* x, size_t n, float* partials, uint8_t* codes, float* scale,
                                 hipStream_t stream) {
-  const size_t groups = (n / 8 + kAmaxThreads - 1) / kAmaxThreads;
-  const int parts = (int)(groups < 1 ? 1 : (groups > kFp8QuantParts ? kFp8QuantParts : groups));
+  const int parts = amax_parts(n);
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)parts), dim3(kAmaxThreads), 0, stream,
                      static_cast<const __bf16*>(x), n, partials);
   hipError_t e = hipGetLastError();
@@ -151,12 +178,23 @@ hipError_t launch_quantize_e4m3(const void* x, size_t n, float* partials, uint8_
   return hipGetLastError();
 }
 
-hipError_t launch_bmm_fp8(const uint8_t* X, const float* x_scale, const uint8_t* W, float w_scale, int N, int H,
-                          int K, int J, void* out, int out_stride, const void* tail_src, int tail,
-                          hipStream_t stream) {
+int amax_parts(size_t n) {
+  const size_t groups = (n / 8 + kAmaxThreads - 1) / kAmaxThreads;
+  return (int)(groups < 1 ? 1 : (groups > kFp8QuantParts ? kFp8QuantParts : groups));
+}
+
+hipError_t launch_bmm_fp8(const void* X, float* partials, const uint8_t* W, float w_scale, int N, int H, int K, int J,
+                          void* out, int out_stride, const void* tail_src, int tail, hipStream_t stream) {
+  const size_t n = (size_t)N * H * K;
+  const int parts = amax_parts(n);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)parts), dim3(kAmaxThreads), 0, stream,
+                     static_cast<const __bf16*>(X), n, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((J + 127) / 128), (unsigned)((N + 31) / 32), (unsigned)H);
-  hipLaunchKernelGGL(bmm_kernel, grid, dim3(256), 0, stream, X, x_scale, W, w_scale, N, H, K, J,
-                     static_cast<__bf16*>(out), out_stride, static_cast<const __bf16*>(tail_src), tail);
+  hipLaunchKernelGGL(bmm_kernel, grid, dim3(256), 0, stream, static_cast<const __bf16*>(X), partials, parts, W,
+                     w_scale, N, H, K, J, static_cast<__bf16*>(out), out_stride,
+                     static_cast<const __bf16*>(tail_src), tail);
   return hipGetLastError();
 }
 

@@ -60,9 +60,10 @@ hipError_t launch_prefill_attn(const void* q_nope, const void* q_rope, int s_q, 
 constexpr int kFp8QuantParts = 256;
 hipError_t launch_quantize_e4m3(const void* x, size_t n, float* partials, uint8_t* codes, float* scale,
                                 hipStream_t stream);
-hipError_t launch_bmm_fp8(const uint8_t* X, const float* x_scale, const uint8_t* W, float w_scale, int N, int H,
-                          int K, int J, void* out, int out_stride, const void* tail_src, int tail,
-                          hipStream_t stream);
+// X is the bf16 activation, quantised inside (its partial maxima go to
+// partials); two kernels on stream.
+hipError_t launch_bmm_fp8(const void* X, float* partials, const uint8_t* W, float w_scale, int N, int H, int K, int J,
+                          void* out, int out_stride, const void* tail_src, int tail, hipStream_t stream);
 hipError_t launch_prefill_merge(const void* o_part, const float* lse_part, int n_parts, int rows, void* o, float* lse,
                                 hipStream_t stream);
 

@@ -41,8 +41,8 @@ Function list and pins:
   e4m3_encode        value -> FP8 e4m3 code, nearest, ties   pinned (torch's float8_e4m3fn
                      to even, saturating at 448              conversion on every tie and a dense
                                                             sweep; round trip of all codes)
-  quantize_e4m3      per-tensor dynamic quantisation: scale  pinned (max element -> 448, zero
-                     = max|x| / 448, codes of x / scale      tensor, exact inputs round-trip)
+  quantize_e4m3      per-tensor dynamic quantisation: codes  pinned (max element -> 448, zero
+                     of x * 448 / max|x|, scale max|x| / 448 tensor, exact inputs round-trip)
   absorb_q_fp8       absorb_q with an e4m3 query and e4m3    pinned (== absorb_q on exactly
                      weights, both scaled                    representable inputs)
   out_uv_fp8         out_uv with an e4m3 latent output and   pinned (== out_uv on exactly
@@ -541,13 +541,16 @@ def e4m3_encode(x) -> np.ndarray:
 
 def quantize_e4m3(x):
     """Per-tensor dynamic quantisation to e4m3, the activation side of the
-    pages' bmm_fp8: one fp32 scale s = max|x| / 448 (1 for an all-zero tensor)
-    and codes e4m3_encode(x / s), the quotient taken in fp32 (the precision
-    the kernel decides the codes in). Returns (codes uint8, s float32)."""
+    pages' bmm_fp8: the multiplier r = 448 / max|x| (fp32; max|x| taken as at
+    least 2^-100, and r = 1 for an all-zero tensor), codes e4m3_encode(x * r)
+    with the product taken in fp32 (the precision the kernel decides the
+    codes in), and the dequantisation scale s = 1 / r (fp32).
+    Returns (codes uint8, s float32)."""
     x32 = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
-    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
-    return e4m3_encode((x32 / s).astype(np.float32)), s
+    r = np.float32(448.0) / np.maximum(amax, np.float32(2.0 ** -100)) if amax > 0 else np.float32(1.0)
+    s = np.float32(1.0) / r
+    return e4m3_encode((x32 * r).astype(np.float32)), s
 
 
 def absorb_q_fp8(q_n, q_r, w_uk_codes, w_scale: float) -> np.ndarray:

@@ -620,7 +620,7 @@ def test_quantize_e4m3_scale_and_extremes():
     x = rng.standard_normal((5, 3, 64)).astype(np.float32)
     x[2, 1, 7] = -9.5  # the largest magnitude
     codes, s = orc.quantize_e4m3(x)
-    assert s == np.float32(np.float32(9.5) / np.float32(448.0))
+    assert s == np.float32(1.0) / (np.float32(448.0) / np.float32(9.5))
     assert codes[2, 1, 7] == 0xFE and np.max(np.abs(orc.e4m3_decode(codes))) == 448.0
     deq = orc.e4m3_decode(codes) * np.float64(s)
     assert np.max(np.abs(deq - x) / np.maximum(np.abs(x), 2.0 ** -6 * s)) <= 2.0 ** -4  # half an ulp of 3 bits
