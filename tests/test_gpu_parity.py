@@ -316,6 +316,29 @@ def test_absorb_q_and_out_uv_deepseek_shape(dtype):
     assert torch.equal(ql[..., dc:].cpu(), q_r)  # the RoPE tail is copied unchanged
 
 
+@pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(5, 3, 48, 8, 40, 24), (33, 2, 16, 4, 136, 200), (7, 4, 24, 4, 12, 20)])
+def test_absorb_q_and_out_uv_bf16_odd_shapes(N, H, dn, dr, dc, dv):
+    # Partial column blocks, a partial last k slice, and (last case) shapes
+    # the MFMA form does not take, which run through the general kernel.
+    rng = np.random.default_rng(42 + N)
+    q_n = torch.from_numpy(rng.standard_normal((N, H, dn), dtype=np.float32)).to(torch.bfloat16)
+    q_r = torch.from_numpy(rng.standard_normal((N, H, dr), dtype=np.float32)).to(torch.bfloat16)
+    w_uk = torch.from_numpy(rng.standard_normal((H, dc, dn), dtype=np.float32) / 7).to(torch.bfloat16)
+    w_uv = torch.from_numpy(rng.standard_normal((H, dc, dv), dtype=np.float32) / 7).to(torch.bfloat16)
+    o_lat = torch.from_numpy(rng.standard_normal((N, H, dc), dtype=np.float32)).to(torch.bfloat16)
+    ql = mla.mla_absorb_q(q_n.cuda(), q_r.cuda(), w_uk.cuda())
+    ou = mla.mla_out_uv(o_lat.cuda(), w_uv.cuda())
+    torch.cuda.synchronize()
+    for got, ref, name in [(ql[..., :dc], orc.absorb_q(to_np(q_n), to_np(q_r), to_np(w_uk))[..., :dc], "absorb_q"),
+                           (ou, orc.out_uv(to_np(o_lat), to_np(w_uv)), "out_uv")]:
+        g = to_np(got)
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        mx = np.max(np.abs(g - ref))
+        print(f"[parity] {name} bf16 N={N} H={H} dn={dn} dc={dc} dv={dv} rel_l2={rel:.3e} max_abs={mx:.3e}", flush=True)
+        assert rel < 5e-3 and mx < 2e-2 * max(1.0, np.abs(ref).max())
+    assert torch.equal(ql[..., dc:].cpu(), q_r)
+
+
 def test_tiny_full_mla_fp32_end_to_end():
     """The tiny full MLA of the worked example, absorbed path on the GPU:
     mla_absorb_q -> mla_decode_fwd (fp32, latent and RoPE zero-padded to
