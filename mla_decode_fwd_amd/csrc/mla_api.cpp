@@ -11,6 +11,7 @@
 
 #include "mla_decode.h"
 #include "mla_internal.h"
+#include "mla_launch_aux.h"
 
 namespace {
 

@@ -19,6 +19,7 @@
 #include <cstdint>
 
 #include "mla_internal.h"
+#include "mla_launch_aux.h"
 
 namespace mla {
 namespace {

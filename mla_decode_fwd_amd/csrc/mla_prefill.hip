@@ -25,6 +25,7 @@
 
 #include "mla_decode_common.h"
 #include "mla_internal.h"
+#include "mla_launch_aux.h"
 
 namespace mla {
 namespace {
