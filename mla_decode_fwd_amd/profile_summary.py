@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--mfma", default=None,
                     help="a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv` run of --pmc-command")
     ap.add_argument("--algorithmic-bytes", type=float, default=None)
+    ap.add_argument("--call-kernels", default=None,
+                    help="comma-separated kernel names that make up one library call (default: all of ours)")
     ap.add_argument("--bench-output", default=None,
                     help="stdout of the kernel-trace run (bench.py's JSON line), for the event-vs-trace check")
     ap.add_argument("--out", required=True)
@@ -133,6 +135,8 @@ def main():
                f"--kernel {args.kernel} --sources {args.sources} --workload '{args.workload}'")
     if args.bench_output:
         summary += " --bench-output <stdout>"
+    if args.call_kernels:
+        summary += f" --call-kernels {args.call_kernels}"
     if args.fetch:
         lines += [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}",
                   f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {pmc_cmd} --copy-mb {args.copy_mb}"]
@@ -160,7 +164,9 @@ def main():
             # One library call launches several kernels: compare the events'
             # time per call with the traced kernel time per call.
             n_calls = rec["steps"] + rec["warmup"]
-            tr_us = sum(avg * calls for name, calls, avg, _, _, _ in stats if _ours(name)) / n_calls / 1e3
+            picked = [k for k in args.call_kernels.split(",")] if args.call_kernels else None
+            tr_us = sum(avg * calls for name, calls, avg, _, _, _ in stats
+                        if _ours(name) and (picked is None or _short(name) in picked)) / n_calls / 1e3
             ev_us = rec["roofline"]["call_us"]
             lines += ["", f"Cross-check in the same run: bench.py's HIP events give {ev_us:.2f} us per library call "
                           f"(back to back), the kernel trace {tr_us:.2f} us of kernel time per call over "
@@ -189,12 +195,15 @@ def main():
         busy, _ = counter_medians(args.mfma, "SQ_VALU_MFMA_BUSY_CYCLES", need_copy=False)
         active, _ = counter_medians(args.mfma, "GRBM_GUI_ACTIVE", need_copy=False)
         lines += ["", "## MFMA busy time (counters)", "",
-                  "SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs, over GRBM_GUI_ACTIVE x 1024 (the share "
-                  "of SIMD-cycles with the matrix unit busy while the kernel ran):", "",
-                  "| kernel | MFMA busy | GUI active cycles |", "|---|---|---|"]
+                  "SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) over 1024 x the kernel's cycles, where "
+                  "the kernel's cycles are GRBM_GUI_ACTIVE / 8 (the counter reads summed over the 8 XCDs): the "
+                  "share of SIMD-cycles with the matrix unit busy while the kernel ran, prologue and tail included.",
+                  "", "| kernel | MFMA busy | MFMA busy cycles per SIMD | kernel cycles |", "|---|---|---|---|"]
         for name in sorted(n for n in busy if _ours(n)):
             if active.get(name):
-                lines.append(f"| {_short(name)} | {100 * busy[name] / (active[name] * 1024):.1f}% | {active[name]:.0f} |")
+                cyc = active[name] / 8
+                lines.append(f"| {_short(name)} | {100 * busy[name] / (cyc * 1024):.1f}% | {busy[name] / 1024:.0f} | "
+                             f"{cyc:.0f} |")
     lines += [""]
     if args.algorithmic_bytes:
         lines += [f"Algorithmic bytes per launch of {args.kernel}: {args.algorithmic_bytes / 1e6:.1f} MB.", ""]
