@@ -27,9 +27,11 @@
 //     within each 16-lane group; B = P^T taken straight from the score
 //     registers: the score layout of a 16-token half tile is exactly the B
 //     layout of one k-step with the tokens of the k-step permuted, and the
-//     V^T reads use the same permutation). The two tiles are staggered so
-//     that each tile's exponentials run between the MFMAs of the other
-//     tile's product (MFMA and VALU work of one wave execute together).
+//     V^T reads use the same permutation). The two tiles are staggered in
+//     the source: each tile's exponentials are written between the MFMAs of
+//     the other tile's product. The compiler moves them down to just before
+//     the first PV MFMA that reads them; pinning them in place (an empty asm
+//     on each result) measured no faster.
 //   * Softmax in base 2 with a lazily updated reference max: O and l are
 //     rescaled only when a row's max grows by more than 8 (so P <= 2^8); the
 //     result is exact because P, l and O always share the reference.
@@ -355,9 +357,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     }
     const bool full_page = kSparse ? page_mask == ~0ull : (pg + 1) * kPage <= n_allowed_min;
 
-    // A page is two 32-token tiles, staggered so that the softmax work of
-    // one tile runs between the MFMAs of the other: QK(T0); QK(T1) with
-    // tile 0's exponentials; PV(T0) with tile 1's exponentials; PV(T1).
+    // A page is two 32-token tiles, staggered in the source so that the
+    // softmax work of one tile sits between the MFMAs of the other: QK(T0);
+    // QK(T1) with tile 0's exponentials; PV(T0) with tile 1's exponentials;
+    // PV(T1) (the compiler gathers each tile's exponentials just before its
+    // PV).
     // Tile 1's P uses a provisional reference taken before PV(T0); O and l
     // move to it only after PV(T0) has added tile 0 (which used the old one).
     auto k_frag = [&](int T, int s) {

@@ -10,8 +10,9 @@ FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch. They are scaled
 by what the same counter reads for the plain device copy of N MiB that
 `bench.py --copy-mb N` launches (`__amd_rocclr_copyBuffer`, N MiB read and N
 MiB written): factor = N MiB / counter reading. The summary records the
-SHA-256 of the dominant kernel's sources, so a reader (bench.py) can tell when
-the kernel has changed since the counters were taken.
+SHA-256 of the dominant kernel's sources (code only: comments and spacing are
+left out), so a reader (bench.py) can tell when the kernel has changed since
+the counters were taken.
 
 usage: python -m mla_decode_fwd_amd.profile_summary --trace D1 [--fetch D2 --write D3 --copy-mb N]
            --command "..." [--kernel NAME --sources a.hip,b.h] --out profiles/<kernel>_<workload>.md
@@ -23,6 +24,7 @@ import csv
 import glob
 import hashlib
 import os
+import re
 import statistics
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -31,11 +33,19 @@ DECODE_KERNEL = "mla_decode_bf16_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def _code_only(text: str) -> str:
+    """The source without comments or blank space, so that a change of wording
+    does not count as a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def decode_source_sha256(sources=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
