@@ -88,6 +88,16 @@ def kernel_stats(folder: str):
              float(r["Percentage"])) for r in rows]
 
 
+def dispatch_durations(folder: str, kernel: str):
+    """Durations (ns) of the dispatches of `kernel`, in dispatch order, from the kernel trace."""
+    paths = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        return []
+    rows = [r for r in csv.DictReader(open(paths[0])) if kernel in _demangle_nested(r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+
+
 def counter_medians(folder: str, counter: str, need_copy: bool = True):
     """Median counter value per kernel name, and the largest copy kernel's value."""
     rows = [r for r in csv.DictReader(open(_one(folder, "*counter_collection.csv")))
@@ -128,6 +138,8 @@ def main():
                     help="comma-separated kernel names that make up one library call (default: all of ours)")
     ap.add_argument("--bench-output", default=None,
                     help="stdout of the kernel-trace run (bench.py's JSON line), for the event-vs-trace check")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="leading dispatches of --kernel (the warm-up) left out of the steady-state average")
     ap.add_argument("--out", required=True)
     args = ap.parse_args()
     if (args.fetch is None) != (args.write is None) or (args.fetch and args.copy_mb <= 0):
@@ -145,6 +157,8 @@ def main():
                f"--kernel {args.kernel} --sources {args.sources} --workload '{args.workload}'")
     if args.bench_output:
         summary += " --bench-output <stdout>"
+    if args.skip:
+        summary += f" --skip {args.skip}"
     if args.call_kernels:
         summary += f" --call-kernels {args.call_kernels}"
     if args.fetch:
@@ -159,6 +173,14 @@ def main():
               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
         lines.append(f"| {_short(name)} | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {pct:.1f} |")
+    steady_us = None
+    if args.skip:
+        durs = dispatch_durations(args.trace, args.kernel)[args.skip:]
+        if durs:
+            steady_us = statistics.mean(durs) / 1e3
+            lines += ["", f"Steady state: the {len(durs)} dispatches of {args.kernel} after the first {args.skip} "
+                          f"(the warm-up, which spans the clock transient of a burst of launches) average "
+                          f"{steady_us:.2f} us (median {statistics.median(durs) / 1e3:.2f} us)."]
     if args.bench_output:
         import json
         rec = None
@@ -167,9 +189,11 @@ def main():
                 rec = json.loads(line)
         if rec and "kernel_us" in rec["roofline"]:
             ev_us = rec["roofline"]["kernel_us"]
-            tr_us = next(avg for name, _, avg, _, _, _ in stats if args.kernel in _demangle_nested(name)) / 1e3
+            tr_us = steady_us if steady_us is not None else \
+                next(avg for name, _, avg, _, _, _ in stats if args.kernel in _demangle_nested(name)) / 1e3
+            which = "steady-state average" if steady_us is not None else "average"
             lines += ["", f"Cross-check in the same run: bench.py's HIP events give {args.kernel} {ev_us:.2f} us "
-                          f"per launch, the kernel trace {tr_us:.2f} us ({100 * (ev_us / tr_us - 1):+.1f}%)."]
+                          f"per launch, the kernel trace's {which} {tr_us:.2f} us ({100 * (ev_us / tr_us - 1):+.1f}%)."]
         elif rec and "call_us" in rec["roofline"]:
             # One library call launches several kernels: compare the events'
             # time per call with the traced kernel time per call.
