@@ -126,7 +126,7 @@ __device__ __forceinline__ void dma_line_addr(uint64_t vaddr, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, off nt"
       :
       : "v"(vaddr), "s"(lds)
       : "memory", "m0");
