@@ -290,6 +290,48 @@ def test_prepared_calls_match_plain_calls():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_decode_graph_replays_match_eager():
+    # The split decode and its merge (two kernels on the caller's stream)
+    # captured once in a HIP graph and replayed several times, with eager
+    # calls on the same workspace between the replays: every replay gives
+    # the eager call's bits.
+    lens = [3000, 700, 130, 4096]
+    case = make_decode_case(lens, s_q=1, H=128, seed=52)
+    d = to_device(case)
+    p = mla.decode_plan(lens, 1, 128, num_cus=32)
+    assert p.any_split
+    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device="cuda")
+    args = (d["q_lat"], d["kv_cache"], d["block_table"], d["seqlens"], case.scale, case.causal)
+    kw = dict(split_offsets=p.device_offsets("cuda"), total_splits=p.total_splits, workspace=ws)
+    o_e, l_e = mla.mla_decode_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    o = torch.empty_like(o_e)
+    lse = torch.empty_like(l_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mla.mla_decode_fwd(*args, o_lat=o, lse=lse, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mla.mla_decode_fwd(*args, o_lat=o, lse=lse, **kw)
+    torch.cuda.synchronize()
+    for i in range(4):
+        o.zero_()
+        lse.zero_()
+        if i % 2 == 1:
+            o3, l3 = mla.mla_decode_fwd(*args, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(o3, o_e) and torch.equal(l3, l_e)
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {i}", flush=True)
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e), f"replay {i}"
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, "graph replays")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_absorb_q_and_out_uv_deepseek_shape(dtype):
     rng = np.random.default_rng(41)
