@@ -358,10 +358,15 @@ def test_absorb_q_and_out_uv_deepseek_shape(dtype):
     assert torch.equal(ql[..., dc:].cpu(), q_r)  # the RoPE tail is copied unchanged
 
 
-@pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(5, 3, 48, 8, 40, 24), (33, 2, 16, 4, 136, 200), (7, 4, 24, 4, 12, 20)])
+@pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(5, 3, 48, 8, 40, 24), (33, 2, 16, 4, 136, 200), (7, 4, 24, 4, 12, 20),
+                                            (70, 3, 128, 64, 208, 72), (130, 2, 128, 64, 512, 128)])
 def test_absorb_q_and_out_uv_bf16_odd_shapes(N, H, dn, dr, dc, dv):
-    # Partial column blocks, a partial last k slice, and (last case) shapes
-    # the MFMA form does not take, which run through the general kernel.
+    # Partial column blocks, a partial last k slice, and (third case) shapes
+    # the MFMA form does not take, which run through the general kernel. The
+    # last two take the staged d_nope = 128 absorption with a partial weight
+    # slab and partial token rounds, and the staged out_uv with partial
+    # column slabs, a k count that is not a multiple of 128 and three token
+    # tiles spread over the waves.
     rng = np.random.default_rng(42 + N)
     q_n = torch.from_numpy(rng.standard_normal((N, H, dn), dtype=np.float32)).to(torch.bfloat16)
     q_r = torch.from_numpy(rng.standard_normal((N, H, dr), dtype=np.float32)).to(torch.bfloat16)
