@@ -163,6 +163,153 @@ __global__ __launch_bounds__(256) void bmm_kernel(const __bf16* __restrict__ X, 
   }
 }
 
+// The same product with both operands staged in LDS, for K a multiple of 16
+// up to 512 (the DeepSeek shapes: K = 128 for the absorption, 512 for the
+// output projection). A workgroup owns one head's weight rows jb .. jb+JS-1
+// (JS = 128 for K <= 256, else 64, so the slab stays within 32 KB of codes),
+// reads them from HBM once with whole-line 16-byte loads and applies them to
+// every token; the token rows, 64 at a time, are loaded the same way and
+// quantised once per workgroup as they are staged. The grid runs head-major
+// (blockIdx.x = head), so the workgroups of one head share an XCD's L2 for
+// the token rows. Rows are padded by 8 bytes: the 32 rows of an 8-byte
+// operand read pass then start on 32 different bank pairs (for K a multiple
+// of 128). Output tiles (JS/32 row tiles x two token tiles) are dealt to the
+// four waves.
+constexpr int kF8MaxK = 512;
+constexpr int kF8Tokens = 64;
+constexpr int kF8SlabBytes = 128 * (256 + 8);      // >= 64 x (512 + 8)
+constexpr int kF8TokBytes = kF8Tokens * (kF8MaxK + 8);
+
+// kK: the contracted length when it is fixed at compile time (128 or 512:
+// the index arithmetic of the staging then reduces to shifts), 0 otherwise.
+template <int kK>
+__global__ __launch_bounds__(256) void bmm_lds_kernel(const __bf16* __restrict__ X, const float* __restrict__ partials,
+                                                     int n_parts, const uint8_t* __restrict__ W, float w_scale, int N,
+                                                     int H, int K_arg, int J, int JS_arg, __bf16* __restrict__ out,
+                                                     int out_stride, const __bf16* __restrict__ tail_src, int tail) {
+  const int K = kK ? kK : K_arg;
+  const int JS = kK ? (kK <= 256 ? 128 : 64) : JS_arg;
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) char sw[kF8SlabBytes];
+  __shared__ __attribute__((aligned(16))) char sx[kF8TokBytes];
+  float r = 1.f;  // the activation's quantisation factor, reduced once the first loads are in flight
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31, hi32 = lane >> 5;
+  const int h = blockIdx.x;
+  const int jb = blockIdx.y * JS;
+  const int S = K + 8;        // LDS row stride of both operands, bytes
+  const int wp = K / 16;      // 16-byte pieces per weight row (16 codes each)
+  const int xp = K / 8;       // 16-byte pieces per token row (8 bf16 each)
+
+  // Staging, all loads of a round issued before any LDS write: the weight
+  // slab (at most 2048 pieces of 16 bytes, 8 per thread) and the token rows
+  // (at most 64 x 64 pieces, 16 per thread).
+  auto load_tokens = [&](int n0, bf16x8_t (&v)[16]) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = u * 256 + tid;
+      if (idx < kF8Tokens * xp) {
+        const int row = idx / xp, p = idx - (idx / xp) * xp;
+        v[u] = *reinterpret_cast<const bf16x8_t*>(X + ((size_t)min(n0 + row, N - 1) * H + h) * K + 8 * p);
+      }
+    }
+  };
+  // Quantised exactly as quantize_kernel does.
+  auto store_tokens = [&](const bf16x8_t (&v)[16]) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = u * 256 + tid;
+      if (idx < kF8Tokens * xp) {
+        const int row = idx / xp, p = idx - (idx / xp) * xp;
+        const uint32_t lo =
+            e4m3_pair((float)v[u][0] * r, (float)v[u][1] * r) | (e4m3_pair((float)v[u][2] * r, (float)v[u][3] * r) << 16);
+        const uint32_t hi =
+            e4m3_pair((float)v[u][4] * r, (float)v[u][5] * r) | (e4m3_pair((float)v[u][6] * r, (float)v[u][7] * r) << 16);
+        *reinterpret_cast<uint2*>(sx + row * S + 8 * p) = make_uint2(lo, hi);
+      }
+    }
+  };
+  {
+    // Weight rows jb .. jb+JS-1 (past J: row J-1, outputs dropped).
+    uint4 wv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = u * 256 + tid;
+      if (idx < JS * wp) {
+        const int row = idx / wp, p = idx - (idx / wp) * wp;
+        wv[u] = *reinterpret_cast<const uint4*>(W + ((size_t)h * J + min(jb + row, J - 1)) * K + 16 * p);
+      }
+    }
+    bf16x8_t xv[16];
+    load_tokens(0, xv);
+    float m = (int)threadIdx.x < n_parts ? partials[threadIdx.x] : 0.f;
+    m = block_max(m, red);
+    r = m > 0.f ? 448.f / fmaxf(m, 0x1p-100f) : 1.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = u * 256 + tid;
+      if (idx < JS * wp) {
+        const int row = idx / wp, p = idx - (idx / wp) * wp;
+        *reinterpret_cast<uint2*>(sw + row * S + 16 * p) = make_uint2(wv[u].x, wv[u].y);
+        *reinterpret_cast<uint2*>(sw + row * S + 16 * p + 8) = make_uint2(wv[u].z, wv[u].w);
+      }
+    }
+    store_tokens(xv);
+  }
+  const float sc = (1.f / r) * w_scale;
+  const int row_tiles = JS / 32;
+  for (int n0 = 0; n0 < N; n0 += kF8Tokens) {
+    if (n0 > 0) {
+      bf16x8_t xv[16];
+      load_tokens(n0, xv);
+      store_tokens(xv);
+    }
+    __syncthreads();
+    const int n_tiles = min(N - n0 + 31, kF8Tokens) / 32;
+    for (int t = wave; t < row_tiles * n_tiles; t += 4) {
+      const int rt = t % row_tiles, nt = t / row_tiles;
+      const int j0 = jb + 32 * rt;
+      const int n = n0 + 32 * nt + r32;
+      if (j0 >= J) continue;
+      const char* wa = sw + (32 * rt + r32) * S + 8 * hi32;
+      const char* xa = sx + (32 * nt + r32) * S + 8 * hi32;
+      f32x16_t acc;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+#pragma unroll 4
+      for (int k = 0; k < K; k += 16)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(*reinterpret_cast<const long*>(wa + k),
+                                                         *reinterpret_cast<const long*>(xa + k), acc, 0, 0, 0);
+      if (n < N) {
+        __bf16* orow = out + ((size_t)n * H + h) * out_stride;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = j0 + 8 * q4 + 4 * hi32;
+          if (j + 3 < J) {
+            bf16x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * q4 + e] * sc);
+            *reinterpret_cast<bf16x4_t*>(orow + j) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j + e < J) orow[j + e] = (__bf16)(acc[4 * q4 + e] * sc);
+          }
+        }
+      }
+    }
+    __syncthreads();  // before the next token rows overwrite sx
+  }
+  if (tail > 0 && blockIdx.y == 0)
+    for (int idx = tid; idx < N * tail; idx += 256) {
+      const int n = idx / tail, e = idx - (idx / tail) * tail;
+      out[((size_t)n * H + h) * out_stride + J + e] = tail_src[((size_t)n * H + h) * tail + e];
+    }
+}
+
 }  // namespace
 
 int amax_parts(size_t n);
@@ -192,6 +339,15 @@ hipError_t launch_bmm_fp8(const void* X, float* partials, const uint8_t* W, floa
                      static_cast<const __bf16*>(X), n, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (K % 16 == 0 && K <= kF8MaxK && ((uintptr_t)W % 16) == 0 && ((uintptr_t)X % 16) == 0 &&
+      ((uintptr_t)out % 8) == 0 && out_stride % 4 == 0) {
+    const int JS = K <= 256 ? 128 : 64;
+    const dim3 grid((unsigned)H, (unsigned)((J + JS - 1) / JS));
+    auto kern = K == 128 ? bmm_lds_kernel<128> : K == 512 ? bmm_lds_kernel<512> : bmm_lds_kernel<0>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, static_cast<const __bf16*>(X), partials, parts, W, w_scale, N,
+                       H, K, J, JS, static_cast<__bf16*>(out), out_stride, static_cast<const __bf16*>(tail_src), tail);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((J + 127) / 128), (unsigned)((N + 31) / 32), (unsigned)H);
   hipLaunchKernelGGL(bmm_kernel, grid, dim3(256), 0, stream, static_cast<const __bf16*>(X), partials, parts, W,
                      w_scale, N, H, K, J, static_cast<__bf16*>(out), out_stride,

@@ -655,7 +655,25 @@ def _fp8_compare(got, ref, label):
     assert np.all(np.isfinite(g)) and rel <= 5e-3 and mabs <= 2e-2 * max(1.0, np.max(np.abs(ref))), (label, rel, mabs)
 
 
-@pytest.mark.parametrize("N,H", [(64, 128), (5, 3), (33, 16)])
+@pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(37, 3, 48, 8, 208, 72), (9, 2, 128, 64, 640, 40)])
+def test_fp8_products_odd_shapes(N, H, dn, dr, dc, dv):
+    # A contracted length other than the staged forms' fixed 128 / 512
+    # (generic staging), partial weight slabs, and (second case) a contracted
+    # length past 512, which takes the direct-load kernel.
+    from mla_inputs import fp8_bmm_case
+    c = fp8_bmm_case(N, H=H, d_nope=dn, d_rope=dr, d_c=dc, d_v=dv, seed=180 + N)
+    q_lat = mla.mla_absorb_q_fp8(c["q_nope"].cuda(), c["q_rope"].cuda(), c["w_uk_codes"].cuda(), c["w_uk_scale"])
+    out = mla.mla_out_uv_fp8(c["o_lat"].cuda(), c["w_uv_t_codes"].cuda(), c["w_uv_scale"])
+    torch.cuda.synchronize()
+    ref_q = orc.absorb_q_fp8(c["q_nope"].float().numpy(), c["q_rope"].float().numpy(), c["w_uk_codes"].numpy(),
+                             c["w_uk_scale"])
+    ref_o = orc.out_uv_fp8(c["o_lat"].float().numpy(), c["w_uv_t_codes"].numpy(), c["w_uv_scale"])
+    _fp8_compare(q_lat[..., :dc], ref_q[..., :dc], f"absorb_q_fp8 N={N} H={H} dn={dn} dc={dc}")
+    _fp8_compare(out, ref_o, f"out_uv_fp8 N={N} H={H} dc={dc} dv={dv}")
+    assert torch.equal(q_lat[..., dc:].cpu(), c["q_rope"])
+
+
+@pytest.mark.parametrize("N,H", [(64, 128), (5, 3), (33, 16), (130, 2)])
 def test_absorb_q_fp8(N, H):
     from mla_inputs import fp8_bmm_case
     c = fp8_bmm_case(N, H=H, seed=172 + N)
@@ -667,7 +685,7 @@ def test_absorb_q_fp8(N, H):
     assert torch.equal(q_lat[..., 512:].cpu(), c["q_rope"])  # the RoPE part is copied
 
 
-@pytest.mark.parametrize("N,H", [(64, 128), (5, 3), (33, 16)])
+@pytest.mark.parametrize("N,H", [(64, 128), (5, 3), (33, 16), (130, 2)])
 def test_out_uv_fp8(N, H):
     from mla_inputs import fp8_bmm_case
     c = fp8_bmm_case(N, H=H, seed=173 + N)
