@@ -351,7 +351,7 @@ def absorb_main(args):
                    "N": N, "H": H, "parallelism": "single GPU"},
         "roofline": {"bound": rf["bound"], "achieved": round(rf["achieved"], 1), "peak": rf["peak"],
                      "unit": rf["unit"], "frac": round(rf["frac"], 4), "traffic": None,
-                     "kernel": "amax + quantise + bmm, twice", "call_us": round(gpu_ms * 1e3, 2),
+                     "kernel": "amax + bmm_lds (quantising as it stages), twice", "call_us": round(gpu_ms * 1e3, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
         "bf16_pair_us": round(bf16_ms * 1e3, 2),
     }
