@@ -89,6 +89,16 @@ def test_small_fp32():
         compare(o, lse, o_ref, l_ref, torch.float32, f"fp32 plan={plan}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_many_chunks_merge(dtype):
+    """Eight or more chunks per sequence on average: the merge takes one
+    workgroup per row with the chunks split over its waves."""
+    case = make_decode_case([700, 300], s_q=2, H=16, seed=12, dtype=dtype, q_scale=1.0)
+    o, lse = run(case, plan="custom", split_offsets=[0, 11, 16])
+    o_ref, l_ref = oracle(case)
+    compare(o, lse, o_ref, l_ref, dtype, f"many chunks {dtype}", abs_relative=True)
+
+
 def test_chunks_with_no_pages_and_max_splits():
     """Explicit offsets: 64 chunks over 3 pages (most empty) and 1-page chunks."""
     case = make_decode_case([150, 64 * 64], s_q=1, H=128, seed=11)
