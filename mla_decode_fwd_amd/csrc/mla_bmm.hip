@@ -9,11 +9,18 @@
 //             q_lat[n,h,dc:dc+dr] = q_rope[n,h,:]
 //   out_uv:   out[n,h,e]      = sum_c o_lat[n,h,c] * w_uv[h,c,e]
 //
-// One kernel serves both: out[n,h,j] = sum_k A[n,h,k] * W(h,k,j), with W read
-// either as [H, J, K] (absorb, the weight row is the output index) or as
-// [H, K, J] (out_uv). A workgroup computes a 64 x 64 output tile of one head,
-// staging 32-deep slices of A and W through LDS in fp32; each thread owns a
-// 4 x 4 block of the tile. Accumulation is fp32 for both storage types.
+// Both are out[n,h,j] = sum_k A[n,h,k] * W(h,k,j), with W read either as
+// [H, J, K] (absorb, the weight row is the output index) or as [H, K, J]
+// (out_uv). Three forms, chosen by shape:
+//   * bf16 MFMA, operands staged in LDS (absorb at d_nope = 128, out_uv at
+//     d_c <= 512): a head-major workgroup reads a slab of one head's weights
+//     once and applies it to every token;
+//   * bf16 MFMA with operands loaded straight from global memory (absorb at
+//     other d_nope, a multiple of 16);
+//   * a general fp32-LDS tile kernel for every other shape and for fp32: a
+//     workgroup computes a 64 x 64 output tile of one head, staging 32-deep
+//     slices of A and W in fp32; each thread owns a 4 x 4 block.
+// Accumulation is fp32 in all of them.
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
