@@ -225,8 +225,12 @@ __global__ __launch_bounds__(kExpThreads, 1) void expand_kernel(
     const int tk = tok_begin + i * kTok + tok;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage0 + (i & 1) * kOutBytes + mat * kTok * kOutStride +
                                                         tok * kOutStride + 16 * c16);
+    // Non-temporal: the chunk's expanded keys and values (64 KB per token)
+    // are far larger than the caches and are read back once, by the
+    // attention kernel (extend: 2.73 -> 2.69 ms per call).
     if (tk < tok_end)
-      *reinterpret_cast<u32x4_t*>((mat ? v_out : k_out) + ((size_t)h * n_stride + tk) * kNope + 8 * c16) = v;
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4_t*>((mat ? v_out : k_out) + ((size_t)h * n_stride + tk) * kNope + 8 * c16));
   };
   for (int i = 0; i < n_tiles; ++i) {
     // Tile i has landed once at most the 4 loads of the next tile remain in
