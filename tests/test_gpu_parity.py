@@ -136,6 +136,21 @@ def test_mtp_two_tokens_sampled():
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("plan", ["auto", None])
+def test_max_new_tokens_at_128_heads(plan):
+    # The largest row count the kernel takes: s_q = 16 causal new tokens at
+    # H = 128 (2048 rows, sixteen row groups per chunk), with a sequence that
+    # holds nothing but its new tokens (L = s_q: the first query sees one key)
+    # and one whose new tokens straddle a page boundary.
+    for q_scale in (None, 1.0):
+        kw = {} if q_scale is None else dict(q_scale=q_scale)
+        case = make_decode_case([16, 17, 100], s_q=16, H=128, seed=230, **kw)
+        o, lse = run(case, plan=plan, num_cus=64)
+        o_ref, l_ref = oracle(case)
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"s_q=16 H=128 plan={plan} q_scale={q_scale}",
+                abs_relative=True)
+
+
 @pytest.mark.parametrize("lens,s_q", [([1000, 300, 2000], 4), ([700, 129], 8), ([64, 65], 8)])
 def test_wider_mtp_small(lens, s_q):
     # Speculative verify with up to 8 causal new tokens at H=128 (one group of
