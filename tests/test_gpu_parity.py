@@ -461,6 +461,17 @@ def test_sparse_small(lens, s_q, topk, q_scale, plan):
     compare(o, lse, o_ref, l_ref, torch.bfloat16, f"{case.name} lens={lens} q_scale={q_scale} plan={plan}")
 
 
+def test_sparse_sixteen_query_tokens():
+    # Top-k lists for 16 new tokens per sequence (sixteen row groups), lists
+    # shorter than a page, sharp scores.
+    from gpu_helpers import oracle_sparse, run_sparse
+    from mla_inputs import sparse_case
+    case = sparse_case([900, 70], s_q=16, topk=40, seed=84, q_scale=1.0)
+    o, lse = run_sparse(case, plan="auto", num_cus=16)
+    o_ref, l_ref = oracle_sparse(case)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, "sparse s_q=16 topk=40", abs_relative=True)
+
+
 def test_sparse_padding_duplicates_and_empty_rows():
     # Lists shorter than topk (-1 padding), out-of-range entries, repeated
     # entries, and one query token with nothing selected (o = 0, lse = -inf).
