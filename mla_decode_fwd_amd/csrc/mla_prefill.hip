@@ -491,8 +491,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(const __bf16* __r
 }
 
 // ---------------------------------------------------------------------------
-// merge_kernel: one wave per (token, head) row; lanes 0..15 own 8 of the 128
-// columns; chunk k's weight exp(lse_k - lse).
+// merge_kernel: one wave per (token, head) row; its four 16-lane groups split
+// the chunks, each lane of a group owns 8 of the 128 columns; chunk k's
+// weight is exp(lse_k - lse).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const __bf16* __restrict__ o_part, const float* __restrict__ lse_part,
                                                    int n_parts, int rows, __bf16* __restrict__ o,
@@ -511,14 +512,36 @@ __global__ __launch_bounds__(256) void merge_kernel(const __bf16* __restrict__ o
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
   const float wn = S > 0.f ? w / S : 0.f;
+  // Lane group g = lane >> 4 takes chunks g, g + 4, ...; its 16 lanes own 8
+  // columns each. Sixteen chunks per round, all loads of a round issued
+  // before their products; slots past n_parts load nothing and weigh 0. The
+  // four groups' sums meet by lane swaps.
+  const int sub = lane & 15, grp = lane >> 4;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n_parts; ++k) {
-    const float wk = __shfl(wn, k, 64);
-    if (lane < 16) {
-      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(o_part + ((size_t)k * rows + row) * kHeadV + 8 * lane);
+  for (int k0 = 0; k0 < n_parts; k0 += 16) {
+    bf16x8_t x[4];
+    float wk[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, (float)x[e], acc[e]);
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + 4 * j + grp;
+      wk[j] = __shfl(wn, min(k, 63), 64);
+      if (k < n_parts) {
+        x[j] = *reinterpret_cast<const bf16x8_t*>(o_part + ((size_t)k * rows + row) * kHeadV + 8 * sub);
+      } else {
+        wk[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[j][e] = (__bf16)0.f;
+      }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk[j], (float)x[j][e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16, 64);
+    acc[e] += __shfl_xor(acc[e], 32, 64);
   }
   if (lane < 16) {
     bf16x8_t v;
