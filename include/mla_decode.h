@@ -25,6 +25,9 @@
  *               bmm of the attention output with w_vc).
  *   [AI-MTP]    "为什么 MLA + MTP 容易吃亏？从 Arithmetic Intensity 看 Attention",
  *               section 6: top-k sparse attention over gathered latents.
+ *   [SGL-compile] "MLA 与 torch.compile：v0.3 的两个来源", the weight-absorption
+ *               passage: with e4m3 weights w_kc / w_vc both per-head products
+ *               run as bmm_fp8 of an activation quantised on the fly.
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the name ends in _host. All tensors
@@ -325,8 +328,8 @@ mla_status_t mla_out_uv(const void* o_lat, const void* w_uv, int N, int H, int d
                         mla_dtype_t dtype, void* out, void* stream);
 
 /*
- * FP8 (e4m3) products for the absorption ([DSV2-MLA], the SGLang history
- * section: with FP8 weights w_kc and w_vc, both bmm's run as bmm_fp8 of an
+ * FP8 (e4m3) products for the absorption ([SGL-compile] "MLA 与 torch.compile：
+ * v0.3 的两个来源", the weight-absorption passage: with FP8 weights w_kc and w_vc, both bmm's run as bmm_fp8 of an
  * activation quantised to e4m3 on the fly, one scale per tensor, against the
  * e4m3 weights and their scale, with a bf16 result).
  *

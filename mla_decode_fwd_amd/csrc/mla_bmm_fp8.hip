@@ -1,7 +1,7 @@
 // FP8 (e4m3) batched products around absorbed-MLA decode, gfx950.
 //
-// "DeepSeekV2之MLA", the SGLang history section: with FP8 weights w_kc and
-// w_vc, the query absorption and the output projection run as bmm_fp8 of an
+// "MLA 与 torch.compile：v0.3 的两个来源", the weight-absorption passage (the
+// code run once the MLA weights are loaded): with FP8 weights w_kc and w_vc, the query absorption and the output projection run as bmm_fp8 of an
 // activation quantised to e4m3 on the fly (one scale per tensor) against the
 // e4m3 weights and their scale, with a bf16 result.
 //

@@ -16,12 +16,19 @@ Sources. Each citation names the page by its title and the section:
   [DSV2-MLA]  "DeepSeekV2之MLA" (blog post with the DeepSeek-V2 equations and SGLang code)
   [AI-MTP]    "为什么 MLA + MTP 容易吃亏？从 Arithmetic Intensity 看 Attention"
               (section 6 "Sparse attention 把方向反过来" for decode_sparse)
+  [SGL-compile] "MLA 与 torch.compile：v0.3 的两个来源" (the weight-absorption
+              passage: bmm_fp8 of an e4m3 activation against e4m3 w_kc / w_vc)
 
 Function list and pins:
   rope_adjacent      RoPE on adjacent pairs                 pinned (rotation identities)
-  project            hidden -> q_n, q_r, c, k_r             pinned (path equivalence)
+  project            hidden -> q_n, q_r, c, k_r             pinned (one-hot hidden rows read back
+                                                            weight entries block by block; cos/sin
+                                                            of t*theta along the tokens; rope
+                                                            scores depend on t - s only)
   expanded_attention path one: per-head K, V, ordinary MHA  pinned (path equivalence, SDPA)
-  mla_forward_*      both full tiny MLA paths to y          pinned (the page prints True)
+  mla_forward_*      both full tiny MLA paths to y          pinned (the page prints True; a
+                                                            selector W_o picks head h, element d
+                                                            at column h*DV + d)
   absorb_q           q_lat = [W_UK q^N ; q^R]               pinned (path equivalence)
   out_uv             o = o_lat W_UV[h]                      pinned (path equivalence)
   decode_absorbed    absorbed decode on a paged cache       pinned (brute force, SDPA, closed forms)
@@ -503,8 +510,8 @@ def crossover_tokens(L: int, H: int = 128, nope: int = 128, rope: int = 64, dv: 
 
 
 # ---------------------------------------------------------------------------
-# FP8 batched products for the absorption ([DSV2-MLA], the SGLang history
-# section: with FP8 weights w_kc and w_vc the absorbed query and the output
+# FP8 batched products for the absorption ([SGL-compile] "MLA 与 torch.compile：
+# v0.3 的两个来源", the weight-absorption passage: with FP8 weights w_kc and w_vc the absorbed query and the output
 # projection run as bmm_fp8 of an activation quantised to e4m3 on the fly,
 # one scale per tensor, against the e4m3 weights and their scale, with a
 # bf16 result).

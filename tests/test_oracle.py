@@ -130,6 +130,161 @@ def test_expanded_attention_matches_sdpa():
 
 
 # ---------------------------------------------------------------------------
+# Projections of the worked example ("两条等价的路径"): q = h W_q viewed per
+# head as [nope | rope], the nope block kept, the rope block rotated along the
+# token axis; c = h W_dkv; k_r = RoPE(h W_kr); y = out flattened head-major
+# (token t, head h, element d at column h*DV + d) times W_o. The checks take
+# the projection (or forward) function as an argument so that the mutation
+# tests below can run the same checks on planted mistakes.
+# ---------------------------------------------------------------------------
+
+def _project_dims():
+    return dict(T=7, D=10, H=3, NOPE=4, ROPE=6, DC=5)
+
+
+def check_project(project):
+    """Raise AssertionError unless ``project`` places and rotates each block
+    as the worked example defines. Expected values come from Python's
+    math.cos / math.sin and from reading weight entries, not from the oracle."""
+    d = _project_dims()
+    T, D, H, NOPE, ROPE, DC = (d[k] for k in ("T", "D", "H", "NOPE", "ROPE", "DC"))
+    W = NOPE + ROPE
+    rng = np.random.default_rng(123)
+    W_q = rng.standard_normal((D, H * W))
+    W_dkv = rng.standard_normal((D, DC))
+    W_kr = rng.standard_normal((D, ROPE))
+
+    # (1) One-hot hidden rows h[t] = e_t: h W = the first T rows of W, so every
+    # projected element is one weight entry. The nope block of head h, token
+    # t, element d is W_q[t, h*W + d]; the latent is W_dkv[t]; at position 0
+    # the rotation is the identity, so q_r[0] and k_r[0] are raw entries.
+    h = np.eye(T, D)
+    q_n, q_r, c, k_r = project(h, W_q, W_dkv, W_kr, H, NOPE, ROPE)
+    assert q_n.shape == (T, H, NOPE) and q_r.shape == (T, H, ROPE)
+    assert c.shape == (T, DC) and k_r.shape == (T, ROPE)
+    for t in range(T):
+        for hh in range(H):
+            for e in range(NOPE):
+                assert q_n[t, hh, e] == W_q[t, hh * W + e]
+    assert np.array_equal(c, W_dkv[:T])
+    for hh in range(H):
+        for e in range(ROPE):
+            assert abs(q_r[0, hh, e] - W_q[0, hh * W + NOPE + e]) <= 1e-15
+    assert np.allclose(k_r[0], W_kr[0], rtol=0, atol=1e-15)
+
+    # (2) Every token row equal to e_0 and one weight column of ones routed
+    # into element 2i of head hh's rope block: along the tokens that pair is
+    # (cos t*th_i, sin t*th_i), th_i = 10000^(-2i/R), and everything else is 0.
+    h = np.zeros((T, D))
+    h[:, 0] = 1.0
+    for hh, i in ((0, 0), (2, 1), (1, 2)):
+        Wq1 = np.zeros((D, H * W))
+        Wq1[0, hh * W + NOPE + 2 * i] = 1.0
+        Wkr1 = np.zeros((D, ROPE))
+        Wkr1[0, 2 * i] = 1.0
+        q_n, q_r, _, k_r = project(h, Wq1, W_dkv, Wkr1, H, NOPE, ROPE)
+        exp_q = np.zeros((T, H, ROPE))
+        exp_k = np.zeros((T, ROPE))
+        for t in range(T):
+            th = t / 10000.0 ** (2 * i / ROPE)
+            exp_q[t, hh, 2 * i] = exp_k[t, 2 * i] = math.cos(th)
+            exp_q[t, hh, 2 * i + 1] = exp_k[t, 2 * i + 1] = math.sin(th)
+        assert not np.any(q_n)
+        assert np.allclose(q_r, exp_q, rtol=0, atol=1e-14)
+        assert np.allclose(k_r, exp_k, rtol=0, atol=1e-14)
+
+    # (3) Random weights, every token row the same random vector: the rope
+    # score <q_r[t,h], k_r[s]> depends on t - s only, and differs between
+    # offsets (the rotation is not the identity).
+    h = np.tile(rng.standard_normal(D), (T, 1))
+    _, q_r, _, k_r = project(h, W_q, W_dkv, W_kr, H, NOPE, ROPE)
+    for hh in range(H):
+        dots = q_r[:, hh, :] @ k_r.T  # [t, s]
+        for off in range(-(T - 1), T):
+            diag = np.diagonal(dots, offset=-off)  # entries with t - s = off
+            assert np.max(np.abs(diag - diag[0])) <= 1e-12
+        assert abs(dots[3, 0] - dots[0, 0]) > 1e-6
+
+
+def check_output_flatten(forward):
+    """Raise AssertionError unless ``forward`` (a full tiny MLA path) applies
+    W_o to the per-head outputs flattened head-major. With W_o a selector of
+    column h*DV + d, output column j must equal head h's element d from
+    expanded_attention (pinned against torch SDPA above)."""
+    w = random_tiny_mla(9, T=5, D=12, H=3, NOPE=4, ROPE=4, DV=5, DC=6)
+    H, DV, D = w["H"], w["DV"], w["D"]
+    q_n, q_r, c, k_r = orc.project(w["h"], w["W_q"], w["W_dkv"], w["W_kr"], H, w["NOPE"], w["ROPE"])
+    out = orc.expanded_attention(q_n, q_r, c, k_r, w["W_uk"], w["W_uv"], causal=True)
+    picks = [(0, 1), (1, 0), (2, 4), (1, 3)]
+    W_o = np.zeros((H * DV, D))
+    for j, (hh, e) in enumerate(picks):
+        W_o[hh * DV + e, j] = 1.0
+    y = forward(w["h"], w["W_q"], w["W_dkv"], w["W_kr"], w["W_uk"], w["W_uv"], W_o,
+                H, w["NOPE"], w["ROPE"])
+    for j, (hh, e) in enumerate(picks):
+        assert np.max(np.abs(y[:, j] - out[:, hh, e])) <= 1e-12
+    assert not np.any(y[:, len(picks):])
+
+
+def test_project_places_and_rotates_blocks():
+    check_project(orc.project)
+
+
+@pytest.mark.parametrize("path", ["expanded", "absorbed"])
+def test_output_projection_is_head_major(path):
+    check_output_flatten(orc.mla_forward_expanded if path == "expanded" else orc.mla_forward_absorbed)
+
+
+def _project_rope_over_heads(h, W_q, W_dkv, W_kr, H, nope, rope_dim):
+    """Planted mistake: the query's rotation runs over the head axis."""
+    h = np.asarray(h, np.float64)
+    T = h.shape[0]
+    q = (h @ W_q).reshape(T, H, nope + rope_dim)
+    return q[..., :nope], orc.rope_adjacent(q[..., nope:]), h @ W_dkv, orc.rope_adjacent(h @ W_kr)
+
+
+def _project_swapped_halves(h, W_q, W_dkv, W_kr, H, nope, rope_dim):
+    """Planted mistake: the rope block taken from the front of each head."""
+    h = np.asarray(h, np.float64)
+    T = h.shape[0]
+    q = (h @ W_q).reshape(T, H, nope + rope_dim)
+    q_r = orc.rope_adjacent(np.transpose(q[..., :rope_dim], (1, 0, 2))).transpose(1, 0, 2)
+    return q[..., rope_dim:], q_r, h @ W_dkv, orc.rope_adjacent(h @ W_kr)
+
+
+def _project_token_head_transposed(h, W_q, W_dkv, W_kr, H, nope, rope_dim):
+    """Planted mistake: q viewed as [H, T, width] straight from h W_q."""
+    h = np.asarray(h, np.float64)
+    T = h.shape[0]
+    q = (h @ W_q).reshape(H, T, nope + rope_dim).transpose(1, 0, 2)
+    q_r = orc.rope_adjacent(np.transpose(q[..., nope:], (1, 0, 2))).transpose(1, 0, 2)
+    return q[..., :nope], q_r, h @ W_dkv, orc.rope_adjacent(h @ W_kr)
+
+
+def _project_unrotated_key(h, W_q, W_dkv, W_kr, H, nope, rope_dim):
+    """Planted mistake: the shared RoPE key left unrotated."""
+    q_n, q_r, c, _ = orc.project(h, W_q, W_dkv, W_kr, H, nope, rope_dim)
+    return q_n, q_r, c, np.asarray(h, np.float64) @ W_kr
+
+
+@pytest.mark.parametrize("mutant", [_project_rope_over_heads, _project_swapped_halves,
+                                    _project_token_head_transposed, _project_unrotated_key])
+def test_mutation_projection_mistakes_are_caught(mutant):
+    with pytest.raises(AssertionError):
+        check_project(mutant)
+
+
+def test_mutation_transposed_output_flatten_is_caught():
+    """Planted mistake: the per-head outputs flattened element-major."""
+    def forward_transposed(h, W_q, W_dkv, W_kr, W_uk, W_uv, W_o, H, nope, rope_dim):
+        q_n, q_r, c, k_r = orc.project(h, W_q, W_dkv, W_kr, H, nope, rope_dim)
+        out = orc.expanded_attention(q_n, q_r, c, k_r, W_uk, W_uv, True)
+        return out.transpose(0, 2, 1).reshape(out.shape[0], -1) @ W_o
+    with pytest.raises(AssertionError):
+        check_output_flatten(forward_transposed)
+
+
+# ---------------------------------------------------------------------------
 # RoPE: closed forms of the adjacent-pair rotation.
 # ---------------------------------------------------------------------------
 
