@@ -76,10 +76,10 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 5 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
+/* Library ABI version, currently 6 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
    4 the expanded path: mla_select_path, mla_prefill_workspace_size, mla_prefill_fwd,
    5 the FP8 products: mla_fp8_workspace_size, mla_quantize_e4m3, mla_absorb_q_fp8,
-   mla_out_uv_fp8). */
+   mla_out_uv_fp8, 6 mla_decode_noalloc_scratch_bytes and mla_decode_fwd_noalloc). */
 int mla_abi_version(void);
 
 /*
@@ -168,6 +168,38 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
                             int page_size, int max_pages_per_seq, int num_pages,
                             float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
                             size_t workspace_bytes, void* o_lat, float* lse, void* stream);
+
+/*
+ * mla_decode_fwd with a split plan but without a workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The call allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine); the chunk partials
+ * go to a static device array of MLA_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds from the first call on it until the process ends.
+ *
+ * Arguments and results are those of mla_decode_fwd, except:
+ *   - there is no workspace, and o_lat and lse are required (no
+ *     partials-only mode: the partials stay in the library's array);
+ *   - the partials need mla_decode_noalloc_scratch_bytes(total_splits, s_q,
+ *     H, dtype) bytes; above MLA_NOALLOC_SCRATCH_BYTES the call returns
+ *     MLA_ERR_WORKSPACE (e.g. bf16, H = 128, s_q = 1 allows up to 510
+ *     chunks: the B = 64 x 4096 plan of 256 chunks fits);
+ *   - `stream` must belong to the current device (else MLA_ERR_INVALID_ARG);
+ *     the first call on a device looks up that device's copy of the array
+ *     (MLA_ERR_HIP if that fails).
+ * With split_offsets == NULL it is mla_decode_fwd without a workspace.
+ * Every call on one GPU uses the same array and leaves the last call's
+ * partials in it (nothing needs clearing: every chunk writes its whole
+ * partial before the merge reads it). Calls that overlap in time on one GPU,
+ * on any streams or host threads, race on the array: serialize them.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+size_t mla_decode_noalloc_scratch_bytes(int total_splits, int s_q, int H, mla_dtype_t dtype);
+mla_status_t mla_decode_fwd_noalloc(const void* q_lat, const void* kv_cache, const int32_t* block_table,
+                                    const int32_t* seqlens, const int32_t* split_offsets, int total_splits,
+                                    int B, int s_q, int H, int d_qk, int d_v, int page_size,
+                                    int max_pages_per_seq, int num_pages, float softmax_scale, int causal,
+                                    mla_dtype_t dtype, void* o_lat, float* lse, void* stream);
 
 /*
  * Top-k (sparse) absorbed-MLA decode ([AI-MTP] section 6 "Sparse attention

@@ -27,6 +27,7 @@ __all__ = [
     "mla_decode_fwd_fp8", "prepare_decode_fp8",
     "select_path", "prefill_workspace_size", "mla_prefill_fwd", "mla_attention_fwd",
     "fp8_workspace_size", "quantize_e4m3", "mla_absorb_q_fp8", "mla_out_uv_fp8",
+    "mla_decode_fwd_noalloc", "noalloc_scratch_bytes", "NOALLOC_SCRATCH_BYTES",
     "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS", "MAX_DECODE_SQ",
 ]
 
@@ -87,6 +88,8 @@ def load_library():
         "mla_quantize_e4m3": ([P, Z, P, Z, P, P, P], I),
         "mla_absorb_q_fp8": ([P, P, P, F, I, I, I, I, I, P, Z, P, P], I),
         "mla_out_uv_fp8": ([P, P, F, I, I, I, I, P, Z, P, P], I),
+        "mla_decode_noalloc_scratch_bytes": ([I, I, I, I], Z),
+        "mla_decode_fwd_noalloc": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -226,6 +229,46 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
     if _prepare:
         return PreparedCall("mla_decode_fwd", args), (o_lat, lse)
     _check("mla_decode_fwd", load_library().mla_decode_fwd(*args))
+    return o_lat, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES
+
+
+def noalloc_scratch_bytes(total_splits: int, s_q: int, H: int, dtype=torch.bfloat16) -> int:
+    """Bytes of the library's static array that ``mla_decode_fwd_noalloc`` needs for a plan."""
+    return int(load_library().mla_decode_noalloc_scratch_bytes(int(total_splits), int(s_q), int(H),
+                                                               _DTYPES[dtype]))
+
+
+def mla_decode_fwd_noalloc(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                           seqlens: torch.Tensor, softmax_scale: float, causal: bool, o_lat: torch.Tensor,
+                           lse: torch.Tensor, split_offsets: Optional[torch.Tensor] = None,
+                           total_splits: Optional[int] = None):
+    """mla_decode_fwd_noalloc: the split decode and its merge with the chunk partials in the
+    library's static device array. The caller passes the outputs; the call allocates nothing."""
+    if q_lat.dim() != 4 or kv_cache.dim() != 3 or block_table.dim() != 2 or seqlens.dim() != 1:
+        raise ValueError("expected q_lat [B,s_q,H,576], kv_cache [pages,64,576], block_table [B,P], seqlens [B]")
+    dev = q_lat.device
+    dtype = q_lat.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    for t, name, dt in ((q_lat, "q_lat", None), (kv_cache, "kv_cache", dtype), (block_table, "block_table", torch.int32),
+                        (seqlens, "seqlens", torch.int32), (o_lat, "o_lat", dtype), (lse, "lse", torch.float32)):
+        _need(t, name, dtype=dt, device=dev)
+    B, s_q, H, dqk = q_lat.shape
+    if split_offsets is not None:
+        _need(split_offsets, "split_offsets", dtype=torch.int32, device=dev)
+        if split_offsets.shape[0] != B + 1 or total_splits is None:
+            raise ValueError("split_offsets must have B+1 entries and total_splits its last one")
+    else:
+        total_splits = B
+    st = load_library().mla_decode_fwd_noalloc(
+        _ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets), int(total_splits), B,
+        s_q, H, dqk, int(o_lat.shape[-1]), int(kv_cache.shape[1]), int(block_table.shape[1]),
+        int(kv_cache.shape[0]), float(softmax_scale), int(bool(causal)), _DTYPES[dtype], _ptr(o_lat), _ptr(lse),
+        _stream())
+    _check("mla_decode_fwd_noalloc", st)
     return o_lat, lse
 
 

@@ -46,7 +46,7 @@ const char* mla_status_string(mla_status_t status) {
   return "unknown status";
 }
 
-int mla_abi_version(void) { return 5; }
+int mla_abi_version(void) { return 6; }
 
 size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
   return workspace_size(total_splits, s_q, H);
@@ -92,15 +92,20 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
   return MLA_OK;
 }
 
-namespace {
+}  // extern "C"
 
-// Shared by the dense and the top-k entry points (indices == nullptr: dense).
+namespace mla {
+
+// Shared by the dense, top-k and FP8 entry points (indices == nullptr: dense)
+// and by the entry point without a workspace (parts != nullptr: the chunk
+// partials go to parts->o_part / parts->lse_part, already sized by the
+// caller, instead of the workspace).
 mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* row_scales,
                         const int32_t* block_table, const int32_t* seqlens, const int32_t* indices, int topk,
                         const int32_t* split_offsets, int total_splits, int B, int s_q, int H, int d_qk,
                         int d_v, int page_size, int max_pages_per_seq, int num_pages, float softmax_scale,
                         int causal, mla_dtype_t dtype, void* workspace, size_t workspace_bytes, void* o_lat,
-                        float* lse, void* stream) {
+                        float* lse, void* stream, const PartialBuffers* parts) {
   if (!q_lat || !kv_cache || !block_table || !seqlens) return MLA_ERR_INVALID_ARG;
   // Partials only: no outputs, which needs split offsets and a workspace.
   const bool partials_only = !o_lat && !lse;
@@ -118,8 +123,10 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
   } else {
     if (total_splits < B || (long long)total_splits > (long long)B * MLA_MAX_SPLITS)
       return MLA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < workspace_size(total_splits, s_q, H)) return MLA_ERR_WORKSPACE;
+    if (!parts && (!workspace || workspace_bytes < workspace_size(total_splits, s_q, H))) return MLA_ERR_WORKSPACE;
   }
+  if (parts && parts->check_only) return MLA_OK;
+  if (parts && (!parts->o_part || !parts->lse_part)) return MLA_ERR_INVALID_ARG;
   mla::DecodeArgs a{};
   a.q_lat = q_lat;
   a.kv_cache = kv_cache;
@@ -139,7 +146,10 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
   a.indices = indices;
   a.topk = topk;
   a.row_scales = row_scales;
-  if (split_offsets) {
+  if (split_offsets && parts) {
+    a.o_part = parts->o_part;
+    a.lse_part = parts->lse_part;
+  } else if (split_offsets) {
     const size_t rows = (size_t)total_splits * s_q * H;
     // The o_part region is sized for fp32 whatever the dtype, so the LSE
     // partials always start at the same byte offset.
@@ -158,7 +168,11 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
   return from_hip(e);
 }
 
-}  // namespace
+}  // namespace mla
+
+using mla::run_decode;
+
+extern "C" {
 
 mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,
                             const int32_t* seqlens, const int32_t* split_offsets,
@@ -168,7 +182,7 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
                             size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
   return run_decode(q_lat, kv_cache, nullptr, block_table, seqlens, nullptr, 0, split_offsets, total_splits, B, s_q, H,
                     d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, dtype, workspace,
-                    workspace_bytes, o_lat, lse, stream);
+                    workspace_bytes, o_lat, lse, stream, nullptr);
 }
 
 mla_status_t mla_sparse_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,
@@ -183,7 +197,7 @@ mla_status_t mla_sparse_decode_fwd(const void* q_lat, const void* kv_cache, cons
   if (dtype != MLA_BF16 || H != mla::kRowsPerGroup) return MLA_ERR_UNSUPPORTED;
   return run_decode(q_lat, kv_cache, nullptr, block_table, seqlens, indices, topk, split_offsets, total_splits, B, s_q,
                     H, d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, /*causal=*/0, dtype,
-                    workspace, workspace_bytes, o_lat, lse, stream);
+                    workspace, workspace_bytes, o_lat, lse, stream, nullptr);
 }
 
 mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, const float* row_scales,
@@ -194,7 +208,7 @@ mla_status_t mla_decode_fwd_fp8(const void* q_lat, const void* kv_cache_e4m3, co
   if (!row_scales) return MLA_ERR_INVALID_ARG;
   return run_decode(q_lat, kv_cache_e4m3, row_scales, block_table, seqlens, nullptr, 0, split_offsets, total_splits,
                     B, s_q, H, d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, MLA_BF16,
-                    workspace, workspace_bytes, o_lat, lse, stream);
+                    workspace, workspace_bytes, o_lat, lse, stream, nullptr);
 }
 
 // ---- expanded path (prefill / extend) ----

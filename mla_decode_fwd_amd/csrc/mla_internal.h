@@ -8,6 +8,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "mla_decode.h"
+
 namespace mla {
 
 constexpr int kDqk = 576;       // key width: latent 512 + RoPE 64
@@ -39,6 +41,25 @@ struct DecodeArgs {
 };
 
 constexpr int kSparseMaxTopk = 2048;  // selected tokens per query token at most
+
+// Chunk partials of a split decode placed by the caller: o_part [total_splits,
+// s_q, H, 512] in the decode dtype and lse_part [total_splits, s_q, H] fp32.
+struct PartialBuffers {
+  void* o_part;
+  float* lse_part;
+  bool check_only;  // run the argument checks, launch nothing
+};
+
+// The decode entry points' shared body (argument checks, then the decode and,
+// when outputs are given with split offsets, the merge). parts == nullptr:
+// the partials live in the workspace (layout of mla_decode_workspace_size);
+// otherwise in *parts and the workspace is not used.
+mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* row_scales,
+                        const int32_t* block_table, const int32_t* seqlens, const int32_t* indices, int topk,
+                        const int32_t* split_offsets, int total_splits, int B, int s_q, int H, int d_qk,
+                        int d_v, int page_size, int max_pages_per_seq, int num_pages, float softmax_scale,
+                        int causal, mla_dtype_t dtype, void* workspace, size_t workspace_bytes, void* o_lat,
+                        float* lse, void* stream, const PartialBuffers* parts);
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp32(const DecodeArgs& a, hipStream_t stream);

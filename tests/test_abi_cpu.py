@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 5
+    assert mla.abi_version() == 6
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -127,6 +127,38 @@ def test_decode_fwd_validation(lib):
     assert _fwd(lib, so=FAKE, total=4, ws=None, wsb=1 << 30) == WORKSPACE
     need = mla.decode_workspace_size(4, 1, 128)
     assert _fwd(lib, so=FAKE, total=4, ws=FAKE, wsb=need - 1) == WORKSPACE
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, so=FAKE, total=4, B=2, s_q=1, H=128, dqk=576, dv=512,
+             page=64, maxp=4, npages=8, scale=0.0722, causal=0, dtype=0, o=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_fwd_noalloc(a["q"], a["kv"], a["bt"], a["sl"], a["so"], a["total"], a["B"], a["s_q"],
+                                      a["H"], a["dqk"], a["dv"], a["page"], a["maxp"], a["npages"], a["scale"],
+                                      a["causal"], a["dtype"], a["o"], a["lse"], None)
+
+
+def test_noalloc_validation_and_scratch_size(lib):
+    # Every refusal below comes before any HIP call (none is possible here).
+    assert mla.NOALLOC_SCRATCH_BYTES == 64 << 20
+    bf16_rows = 510 * 128
+    assert mla.noalloc_scratch_bytes(510, 1, 128) == bf16_rows * 1024 + bf16_rows * 4
+    assert mla.noalloc_scratch_bytes(510, 1, 128) <= mla.NOALLOC_SCRATCH_BYTES
+    assert mla.noalloc_scratch_bytes(511, 1, 128) > mla.NOALLOC_SCRATCH_BYTES
+    assert lib.mla_decode_noalloc_scratch_bytes(4, 1, 128, 1) == 4 * 128 * 2048 + 4 * 128 * 4
+    assert lib.mla_decode_noalloc_scratch_bytes(0, 1, 128, 0) == 0
+    assert lib.mla_decode_noalloc_scratch_bytes(4, 1, 128, 9) == 0
+    assert _noalloc(lib, o=None) == INVALID          # outputs are required
+    assert _noalloc(lib, lse=None) == INVALID
+    assert _noalloc(lib, q=None) == INVALID
+    assert _noalloc(lib, dqk=128) == UNSUPPORTED
+    assert _noalloc(lib, dtype=7) == UNSUPPORTED
+    assert _noalloc(lib, H=129) == UNSUPPORTED
+    assert _noalloc(lib, total=1) == INVALID         # fewer chunks than sequences
+    assert _noalloc(lib, total=129) == INVALID       # more than 64 per sequence
+    assert _noalloc(lib, B=16, total=511) == WORKSPACE   # over the static array
+    assert _noalloc(lib, B=16, total=256, dtype=1) == WORKSPACE  # fp32 partials: 255 chunks at most
+    assert _noalloc(lib, so=None, total=3) == INVALID  # no split offsets: one chunk per sequence
 
 
 def test_combine_and_bmm_validation(lib):
