@@ -12,13 +12,21 @@ one shuffled pool; seeded synthetic inputs. Two copies of the cache and
 queries alternate between steps so no step finds the previous one's 302 MB of
 KV in the 256 MB last-level cache.
 
-Prints one JSON line. `roofline` describes the dominant kernel (the decode
-kernel): algorithmic bytes per launch over its average duration. Three
-timed regions run back to back on the stream the library launches on, each
+Prints one JSON line. `value` and `ms_per_step` come from the timed region
+the contract defines: --warmup untimed steps, then exactly --steps steps
+between two synchronizations (wall clock), on the stream the library launches
+on. `roofline` describes the dominant kernel (the decode kernel):
+algorithmic bytes per launch over its average duration. That duration and
+the merge's come from interleaved rounds run after the timed steps: each
+round is [10 steps | 10 decode launches | 10 merge launches], each region
 bracketed by one pair of HIP events (an event between kernels costs the GPU
-several microseconds, so none sits inside a region): the K steps (this gives
-`value` and `ms_per_step`), then K decode launches alone (the decode kernel's
-average duration), then K merge launches alone. `traffic` (measured HBM bytes per launch) is
+several microseconds, so none sits inside a region), so the three regions see
+the same phase of the GPU clock; the medians over the second half of 24
+rounds are reported, with the step time measured in the same rounds
+(`interleaved_step_us`), the gap between it and decode + merge
+(`launch_gap_us`), and the shader clock (`shader_clock_mhz`): the SMI's
+current clock, averaged over the XCDs, sampled every half millisecond while
+about 100 ms of decode launches run back to back. `traffic` (measured HBM bytes per launch) is
 the scaled FETCH_SIZE + WRITE_SIZE reading kept in
 profiles/mla_decode_bf16_b64_ctx4096.md (made by
 mla_decode_fwd_amd.profile_summary from rocprofv3 counter runs of this
@@ -32,10 +40,10 @@ starts a burst of back-to-back steps (the GPU first throttles below its
 sustained clock, then recovers over ~250 steps), so that the timed steps see
 the sustained state.
 
-After the three timed regions, two more (not used for `value`): the K steps
-with one event pair each (`step_us_percentiles`: p10, median, p90), and the K
-steps on one copy of the cache only (`warm_step_us`). `cpu_baseline.cpu` names
-the host CPU.
+After the interleaved rounds, two more regions (not used for `value`): the K
+steps with one event pair each (`step_us_percentiles`: p10, median, p90),
+and the K steps on one copy of the cache only (`warm_step_us`).
+`cpu_baseline.cpu` names the host CPU.
 
 --copy-mb N adds, after the timed steps, three plain device-to-device copies
 of N MiB: a kernel of known traffic, for scaling the memory counters.
@@ -374,6 +382,123 @@ def absorb_main(args):
     print(json.dumps(out_json), flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock from the SMI (amdsmi gpu metrics,
+    current_gfxclks: one value per XCD, in MHz) in a background thread while
+    GPU work runs. The SMI's figure is the power manager's own, refreshed
+    about every millisecond, so only bursts much longer than that are
+    measured. Gives None if amdsmi is missing or the device is not found."""
+
+    def __init__(self, period_s: float = 0.0005):
+        import threading
+
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            import torch
+
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            want = None
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            bus = getattr(props, "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                    want = h
+            if want is None and len(handles) == 1:
+                want = handles[0]
+            if want is None:
+                raise RuntimeError(f"device not identified among {len(handles)} SMI handles")
+            self._handle = want
+        except Exception as e:  # no SMI access: report null
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        vals = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 10000]
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [m["current_gfxclk"]]
+        return sum(vals) / len(vals) if vals else None
+
+    def _run(self):
+        import time as _t
+
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            _t.sleep(self.period)
+
+    def start(self):
+        import threading
+
+        if self._handle is None:
+            return
+        self.samples = []
+        self._stop.clear()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def median(self):
+        if not self.samples:
+            return None
+        s = sorted(self.samples)
+        return s[len(s) // 2]
+
+
+def interleaved_regions(step, decode, combine, stream, rounds: int, block: int) -> dict:
+    """The decode kernel's and the merge's average durations, measured in
+    interleaved rounds of [block steps | block decode launches | block merge
+    launches], each region bracketed by one event pair, so that all three see
+    the same phase of the GPU's clock. The medians over the second half of the
+    rounds are reported (the first half lets a burst settle). Then a burst of
+    decode launches alone (about 100 ms) runs while the SMI's shader clock is
+    sampled: the clock the decode kernel runs at under sustained load."""
+    import torch
+
+    per = {"step": [], "decode": [], "combine": []}
+    for r in range(rounds):
+        for name, fn in (("step", step), ("decode", decode), ("combine", lambda i: combine())):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(block):
+                fn(i)
+            e1.record(stream)
+            per[name].append((e0, e1))
+    torch.cuda.synchronize()
+    med = {}
+    for name, ev in per.items():
+        ms = sorted(a.elapsed_time(b) / block for a, b in ev[rounds // 2:])
+        med[name] = ms[len(ms) // 2]
+    sampler = ClockSampler()
+    n_burst = max(block, int(100.0 / max(med["decode"], 1e-3)))
+    sampler.start()
+    for i in range(n_burst):
+        decode(i)
+    torch.cuda.synchronize()
+    sampler.stop()
+    return {"step_ms": med["step"], "decode_ms": med["decode"], "combine_ms": med["combine"],
+            "clock_mhz": sampler.median(), "clock_samples": len(sampler.samples), "clock_error": sampler.error,
+            "burst": n_burst, "rounds": rounds, "block": block}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +512,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-mb", type=int, default=0)
+    ap.add_argument("--plan", default="schedule", choices=["schedule", "equal"],
+                    help="schedule: the balanced schedule (mla_decode_schedule, bf16 dense decode); equal: "
+                         "near-equal chunks per sequence (mla_decode_plan)")
+    ap.add_argument("--roofline-rounds", type=int, default=24,
+                    help="interleaved rounds of [steps | decodes | merges] for the per-kernel figures")
+    ap.add_argument("--roofline-block", type=int, default=10, help="launches per region in those rounds")
     ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS),
                     help="batched (default): B=64 x ctx 4096, the measured workload; the others "
                          "measure the remaining shapes with the same code")
@@ -436,10 +567,16 @@ def main():
         if fp8_mode:
             sc = case.meta["row_scales"]
             sets[-1]["sc"] = (sc if k == 0 else sc.roll(1, 0)).to(dev)
+    use_schedule = args.plan == "schedule" and not (topk_mode or fp8_mode)
     t0 = time.perf_counter()
-    plan = mla.sparse_decode_plan(B, case.meta["topk"], s_q, H) if topk_mode else mla.decode_plan(L, s_q, H)
+    if topk_mode:
+        plan = mla.sparse_decode_plan(B, case.meta["topk"], s_q, H)
+    elif use_schedule:
+        plan = mla.decode_schedule(L, s_q, H)
+    else:
+        plan = mla.decode_plan(L, s_q, H)
     plan_us = (time.perf_counter() - t0) * 1e6
-    offs = plan.device_offsets(dev)
+    offs = plan.device_arrays(dev)[0] if use_schedule else plan.device_offsets(dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     o_part, lse_part = mla.workspace_partials(ws, plan.total_splits, s_q, H)
     o = torch.empty((B, s_q, H, 512), dtype=torch.bfloat16, device=dev)
@@ -457,6 +594,9 @@ def main():
         dec_calls = [mla.prepare_sparse_decode(s["q"], s["kv"], s["bt"], s["sl"], idx_dev, case.scale,
                                                split_offsets=offs, total_splits=plan.total_splits, workspace=ws,
                                                partials_only=True)[0] for s in sets]
+    elif use_schedule:
+        dec_calls = [mla.prepare_decode(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal, schedule=plan,
+                                        workspace=ws, partials_only=True)[0] for s in sets]
     else:
         dec_calls = [mla.prepare_decode(s["q"], s["kv"], s["bt"], s["sl"], case.scale, case.causal,
                                         split_offsets=offs, total_splits=plan.total_splits, workspace=ws,
@@ -481,8 +621,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     step_gpu_ms, ms_per_step = timed(step)
-    decode_ms, _ = timed(lambda i: dec_calls[i % 2]())
-    combine_ms, _ = timed(lambda i: comb_call())
+    rr = interleaved_regions(step, lambda i: dec_calls[i % 2](), comb_call, stream, args.roofline_rounds,
+                             args.roofline_block)
+    decode_ms, combine_ms = rr["decode_ms"], rr["combine_ms"]
     # Distribution and warm-cache figures, from separate regions after the
     # timed ones: one event pair per step (each event costs the GPU a few
     # microseconds, so these steps read a little slower than ms_per_step),
@@ -550,6 +691,10 @@ def main():
                    "B": B, "ctx": int(max(L)) if args.workload != "batched" else 4096,
                    "ctx_total": int(sum(L)), "s_q": s_q, "H": H,
                    "splits_per_seq": int(plan.num_splits.max()), "parallelism": "single GPU",
+                   "plan": ((f"balanced schedule: {plan.num_segments} segments x "
+                             f"{-(-(s_q * H) // plan.rows_per_group)} row groups of {plan.rows_per_group} rows, "
+                             f"{plan.total_splits} chunks") if use_schedule else
+                            f"near-equal chunks per sequence, {plan.total_splits} chunks"),
                    "cache": "fp8-e4m3 + fp32 row scales" if fp8_mode else "bf16"},
         "hbm_gbs": round(step_rf["gbs"], 1),
         "roofline_frac": round(step_rf["frac"], 4),
@@ -560,6 +705,15 @@ def main():
                      "kernel": ("mla_decode_bf16_kernel<true>" if topk_mode else
                                 "mla_decode_fp8_kernel" if fp8_mode else "mla_decode_bf16_kernel"),
                      "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),
+                     "interleaved_step_us": round(rr["step_ms"] * 1e3, 2),
+                     "launch_gap_us": round((rr["step_ms"] - decode_ms - combine_ms) * 1e3, 2),
+                     "shader_clock_mhz": None if rr["clock_mhz"] is None else round(rr["clock_mhz"], 1),
+                     "timing": (f"medians of the last {rr['rounds'] - rr['rounds'] // 2} of {rr['rounds']} "
+                                f"interleaved rounds of [{rr['block']} steps | {rr['block']} decode launches | "
+                                f"{rr['block']} merge launches], after the timed steps; shader clock: median of "
+                                f"{rr['clock_samples']} SMI samples (mean over XCDs) during {rr['burst']} "
+                                "back-to-back decode launches" +
+                                (f" (SMI unavailable: {rr['clock_error']})" if rr["clock_error"] else "")),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},
         "plan_host_us": round(plan_us, 1),

@@ -76,10 +76,11 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 6 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
+/* Library ABI version, currently 7 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
    4 the expanded path: mla_select_path, mla_prefill_workspace_size, mla_prefill_fwd,
    5 the FP8 products: mla_fp8_workspace_size, mla_quantize_e4m3, mla_absorb_q_fp8,
-   mla_out_uv_fp8, 6 mla_decode_noalloc_scratch_bytes and mla_decode_fwd_noalloc). */
+   mla_out_uv_fp8, 6 mla_decode_noalloc_scratch_bytes and mla_decode_fwd_noalloc, 7 the balanced
+   schedule: mla_decode_schedule_capacity, mla_decode_schedule, mla_decode_fwd_scheduled). */
 int mla_abi_version(void);
 
 /*
@@ -113,6 +114,49 @@ size_t mla_decode_workspace_size(int total_splits, int s_q, int H);
 mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H, int num_cus,
                              int max_splits, int32_t* num_splits_host,
                              int32_t* split_offsets_host, size_t* workspace_bytes);
+
+/*
+ * Balanced schedule (host only, no HIP call): the analogue of the pages'
+ * scheduling metadata ([MLA-推理] section "decode 注意力变成了计算问题":
+ * get_mla_metadata decides which KV segments each compute unit processes, so
+ * that every unit gets about the same work).
+ *
+ * The pages of all sequences are laid end to end (sequence 0 first) and cut
+ * into equal contiguous segments, one per workgroup slot; a segment's
+ * intersection with one sequence is a chunk (one partial of the LSE merge),
+ * so a segment may cover the end of one sequence and the start of the next,
+ * and every workgroup gets the same page count (the last one possibly
+ * fewer). A workgroup covers one row group of rows_per_group (query token,
+ * head) rows: 128 (all heads of one new token), or 64, where two waves share
+ * each 32-row slice and take one 32-token half of every page each, merging
+ * their softmax states at the end. With R = ceil(s_q*H / rows_per_group) row
+ * groups there are at most num_cus / R segments, each processed by R
+ * workgroups at once. 64-row groups are chosen when the chunk cap
+ * (max_splits per sequence) would otherwise leave compute units idle: with
+ * them each segment holds twice the pages of half the rows. If the cap
+ * still binds, segments are lengthened until no sequence is cut into more
+ * than max_splits chunks.
+ *
+ *   seqlens_host[B]     L_b, each >= s_q (the same values as the device seqlens
+ *                       passed to mla_decode_fwd_scheduled).
+ *   num_cus             compute units (<= 0: 256).   max_splits: 1..64.
+ *   rows_per_group      0 (choose), 64 or 128 (force).
+ *   split_offsets_host  out [B+1]: chunks of sequence b are
+ *                       split_offsets_host[b] .. [b+1]-1 (the merge layout).
+ *   schedule_host       out: [num_segments + 1] first chunk of each segment,
+ *                       then [total_splits][4] = (b, first page, end page, L_b)
+ *                       of every chunk. Needs at most
+ *                       mla_decode_schedule_capacity(B, num_cus) int32 entries;
+ *                       schedule_capacity smaller than what the plan needs is
+ *                       MLA_ERR_WORKSPACE.
+ *   num_segments, rows_per_group_out   out: launch shape for the decode.
+ *   workspace_bytes     out (may be NULL): mla_decode_workspace_size of the plan.
+ */
+size_t mla_decode_schedule_capacity(int B, int num_cus);
+mla_status_t mla_decode_schedule(const int32_t* seqlens_host, int B, int s_q, int H, int num_cus,
+                                 int max_splits, int rows_per_group, int32_t* split_offsets_host,
+                                 int32_t* schedule_host, size_t schedule_capacity, int* num_segments,
+                                 int* rows_per_group_out, size_t* workspace_bytes);
 
 /*
  * Absorbed-MLA decode: o_lat and LSE for every (sequence, new token, head).
@@ -200,6 +244,28 @@ mla_status_t mla_decode_fwd_noalloc(const void* q_lat, const void* kv_cache, con
                                     int B, int s_q, int H, int d_qk, int d_v, int page_size,
                                     int max_pages_per_seq, int num_pages, float softmax_scale, int causal,
                                     mla_dtype_t dtype, void* o_lat, float* lse, void* stream);
+
+/*
+ * mla_decode_fwd under a balanced schedule from mla_decode_schedule (bf16
+ * only): the same results, with the work laid out by the schedule instead of
+ * cut into near-equal chunks per sequence. split_offsets (device, [B+1]) and
+ * schedule (device, the schedule_host entries) are the planner's outputs
+ * copied to the device; num_segments, rows_per_group (64 or 128) and
+ * total_splits = split_offsets[B] come from the planner on the host. The
+ * workspace needs mla_decode_workspace_size(total_splits, s_q, H) bytes and
+ * holds the partials in the same layout; o_lat = lse = NULL writes only the
+ * partials. dtype must be MLA_BF16 (else MLA_ERR_UNSUPPORTED); every other
+ * argument and error is as for mla_decode_fwd. Chunk descriptors are
+ * clamped to the sequence and the page table, so an inconsistent schedule
+ * gives wrong results but never reads or writes outside the buffers.
+ */
+mla_status_t mla_decode_fwd_scheduled(const void* q_lat, const void* kv_cache, const int32_t* block_table,
+                                      const int32_t* seqlens, const int32_t* split_offsets,
+                                      const int32_t* schedule, int num_segments, int rows_per_group,
+                                      int total_splits, int B, int s_q, int H, int d_qk, int d_v,
+                                      int page_size, int max_pages_per_seq, int num_pages,
+                                      float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
+                                      size_t workspace_bytes, void* o_lat, float* lse, void* stream);
 
 /*
  * Top-k (sparse) absorbed-MLA decode ([AI-MTP] section 6 "Sparse attention

@@ -28,6 +28,7 @@ __all__ = [
     "select_path", "prefill_workspace_size", "mla_prefill_fwd", "mla_attention_fwd",
     "fp8_workspace_size", "quantize_e4m3", "mla_absorb_q_fp8", "mla_out_uv_fp8",
     "mla_decode_fwd_noalloc", "noalloc_scratch_bytes", "NOALLOC_SCRATCH_BYTES",
+    "DecodeSchedule", "decode_schedule",
     "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS", "MAX_DECODE_SQ",
 ]
 
@@ -89,6 +90,9 @@ def load_library():
         "mla_absorb_q_fp8": ([P, P, P, F, I, I, I, I, I, P, Z, P, P], I),
         "mla_out_uv_fp8": ([P, P, F, I, I, I, I, P, Z, P, P], I),
         "mla_decode_noalloc_scratch_bytes": ([I, I, I, I], Z),
+        "mla_decode_schedule_capacity": ([I, I], Z),
+        "mla_decode_schedule": ([P, I, I, I, I, I, I, P, P, Z, P, P, P], I),
+        "mla_decode_fwd_scheduled": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, F, I, I, P, Z, P, P, P], I),
         "mla_decode_fwd_noalloc": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, P, P], I),
     }
     for name, (args, res) in sig.items():
@@ -170,19 +174,79 @@ def decode_plan(seqlens: Sequence[int], s_q: int, H: int, num_cus: int = 256,
     return DecodePlan(ns, off, ws.value, s_q, H)
 
 
+class DecodeSchedule(DecodePlan):
+    """A balanced schedule (mla_decode_schedule): the split offsets of its
+    chunks, the schedule entries (segment -> first chunk, then per chunk b,
+    first page, end page, L_b), the segment count and the row-group size.
+    ``device_arrays(device)`` copies the offsets and the entries to the
+    device once and keeps them."""
+
+    def __init__(self, split_offsets: np.ndarray, workspace_bytes: int, s_q: int, H: int, schedule: np.ndarray,
+                 num_segments: int, rows_per_group: int):
+        super().__init__(np.diff(split_offsets).astype(np.int32), split_offsets, workspace_bytes, s_q, H)
+        self.schedule = schedule
+        self.num_segments = int(num_segments)
+        self.rows_per_group = int(rows_per_group)
+        self._dev = {}
+
+    @property
+    def chunks(self) -> np.ndarray:
+        """[total_splits, 4]: b, first page, end page, L_b of every chunk."""
+        return self.schedule[self.num_segments + 1:].reshape(-1, 4)
+
+    @property
+    def segment_first_chunk(self) -> np.ndarray:
+        return self.schedule[:self.num_segments + 1]
+
+    def device_arrays(self, device):
+        key = str(torch.device(device))
+        if key not in self._dev:
+            self._dev[key] = (torch.from_numpy(self.split_offsets).to(device),
+                              torch.from_numpy(self.schedule).to(device))
+        return self._dev[key]
+
+
+def decode_schedule(seqlens: Sequence[int], s_q: int, H: int, num_cus: int = 256, max_splits: int = MAX_SPLITS,
+                    rows_per_group: int = 0) -> DecodeSchedule:
+    """Host balanced-schedule planner (mla_decode_schedule); rows_per_group 0 lets it choose."""
+    lib = load_library()
+    L = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B = int(L.shape[0])
+    cap = int(lib.mla_decode_schedule_capacity(B, int(num_cus)))
+    off = np.zeros(B + 1, dtype=np.int32)
+    sched = np.zeros(max(cap, 1), dtype=np.int32)
+    nseg, rpg, ws = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_size_t(0)
+    st = lib.mla_decode_schedule(L.ctypes.data_as(ctypes.c_void_p), B, int(s_q), int(H), int(num_cus),
+                                 int(max_splits), int(rows_per_group), off.ctypes.data_as(ctypes.c_void_p),
+                                 sched.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(nseg), ctypes.byref(rpg),
+                                 ctypes.byref(ws))
+    _check("mla_decode_schedule", st)
+    n = nseg.value + 1 + 4 * int(off[-1])
+    return DecodeSchedule(off, ws.value, s_q, H, np.ascontiguousarray(sched[:n]), nseg.value, rpg.value)
+
+
 def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                    seqlens: torch.Tensor, softmax_scale: float, causal: bool,
                    split_offsets: Optional[torch.Tensor] = None, total_splits: Optional[int] = None,
                    workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, partials_only: bool = False, _prepare: bool = False):
+                   lse: Optional[torch.Tensor] = None, partials_only: bool = False,
+                   schedule: Optional[DecodeSchedule] = None, _prepare: bool = False):
     """Absorbed-MLA decode (mla_decode_fwd). Returns (o_lat [B,s_q,H,512], lse [B,s_q,H] fp32).
 
     split_offsets: int32 device [B+1] from ``decode_plan`` (or None for one
     chunk per sequence); total_splits: its last entry (host int).
-    partials_only (needs split_offsets): write only the per-chunk partials
-    into ``workspace`` and return (None, None); ``workspace_partials`` views
-    them for ``mla_splitkv_combine``.
+    schedule: a ``decode_schedule`` result instead (mla_decode_fwd_scheduled;
+    its own offsets are used, split_offsets and total_splits must be None).
+    partials_only (needs split_offsets or a schedule): write only the
+    per-chunk partials into ``workspace`` and return (None, None);
+    ``workspace_partials`` views them for ``mla_splitkv_combine``.
     """
+    sched_t = None
+    if schedule is not None:
+        if split_offsets is not None or total_splits is not None:
+            raise ValueError("a schedule carries its own split offsets")
+        split_offsets, sched_t = schedule.device_arrays(q_lat.device)
+        total_splits = schedule.total_splits
     if q_lat.dim() != 4 or kv_cache.dim() != 3 or block_table.dim() != 2 or seqlens.dim() != 1:
         raise ValueError("expected q_lat [B,s_q,H,576], kv_cache [pages,64,576], block_table [B,P], seqlens [B]")
     dev = q_lat.device
@@ -222,13 +286,18 @@ def mla_decode_fwd(q_lat: torch.Tensor, kv_cache: torch.Tensor, block_table: tor
         _need(o_lat, "o_lat", dtype=dtype, device=dev)
         _need(lse, "lse", dtype=torch.float32, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets),
-            int(total_splits), B, s_q, H, dqk, D_V if o_lat is None else int(o_lat.shape[-1]),
-            int(kv_cache.shape[1]), int(block_table.shape[1]), int(kv_cache.shape[0]), float(softmax_scale),
-            int(bool(causal)), _DTYPES[dtype], _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
+    head = (_ptr(q_lat), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(split_offsets))
+    if sched_t is not None:
+        fn = "mla_decode_fwd_scheduled"
+        head = head + (_ptr(sched_t), schedule.num_segments, schedule.rows_per_group)
+    else:
+        fn = "mla_decode_fwd"
+    args = head + (int(total_splits), B, s_q, H, dqk, D_V if o_lat is None else int(o_lat.shape[-1]),
+                   int(kv_cache.shape[1]), int(block_table.shape[1]), int(kv_cache.shape[0]), float(softmax_scale),
+                   int(bool(causal)), _DTYPES[dtype], _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream())
     if _prepare:
-        return PreparedCall("mla_decode_fwd", args), (o_lat, lse)
-    _check("mla_decode_fwd", load_library().mla_decode_fwd(*args))
+        return PreparedCall(fn, args), (o_lat, lse)
+    _check(fn, getattr(load_library(), fn)(*args))
     return o_lat, lse
 
 

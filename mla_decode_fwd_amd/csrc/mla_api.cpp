@@ -46,7 +46,7 @@ const char* mla_status_string(mla_status_t status) {
   return "unknown status";
 }
 
-int mla_abi_version(void) { return 6; }
+int mla_abi_version(void) { return 7; }
 
 size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
   return workspace_size(total_splits, s_q, H);
@@ -92,6 +92,141 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
   return MLA_OK;
 }
 
+size_t mla_decode_schedule_capacity(int B, int num_cus) {
+  if (B <= 0) return 0;
+  if (num_cus <= 0) num_cus = 256;
+  // Segments <= num_cus; each segment boundary inside a sequence adds one
+  // chunk, so chunks <= B + num_cus.
+  return (size_t)num_cus + 1 + 4 * ((size_t)B + (size_t)num_cus);
+}
+
+mla_status_t mla_decode_schedule(const int32_t* seqlens_host, int B, int s_q, int H, int num_cus, int max_splits,
+                                 int rows_per_group, int32_t* split_offsets_host, int32_t* schedule_host,
+                                 size_t schedule_capacity, int* num_segments, int* rows_per_group_out,
+                                 size_t* workspace_bytes) {
+  if (!seqlens_host || !split_offsets_host || !schedule_host || !num_segments || !rows_per_group_out)
+    return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0) return MLA_ERR_INVALID_ARG;
+  if (max_splits < 1 || max_splits > MLA_MAX_SPLITS) return MLA_ERR_INVALID_ARG;
+  if (rows_per_group != 0 && rows_per_group != 64 && rows_per_group != 128) return MLA_ERR_INVALID_ARG;
+  if (num_cus <= 0) num_cus = 256;
+  if (num_cus > 65536) return MLA_ERR_INVALID_ARG;
+  long long total_pages = 0, max_pages = 0;
+  for (int b = 0; b < B; ++b) {
+    const long long L = seqlens_host[b];
+    if (L < s_q) return MLA_ERR_INVALID_ARG;
+    const long long P = (L + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+    total_pages += P;
+    if (P > max_pages) max_pages = P;
+  }
+  if (total_pages > INT_MAX / 2) return MLA_ERR_INVALID_ARG;
+  const long long rows = (long long)s_q * H;
+  // Chunks of sequence b for segments of `seg` pages laid end to end over the
+  // concatenated pages: the segments overlapping [S_b, S_b + P_b).
+  const auto max_chunks = [&](long long seg) {
+    long long start = 0, worst = 0;
+    for (int b = 0; b < B; ++b) {
+      const long long P = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+      const long long n = (start + P - 1) / seg - start / seg + 1;
+      if (n > worst) worst = n;
+      start += P;
+    }
+    return worst;
+  };
+  // Candidate row-group sizes. A 64-row group halves the rows a workgroup
+  // holds, so twice as many workgroups share each page range and the
+  // segments are twice as long for the same number of workgroups; it is
+  // taken when the chunk cap would otherwise leave compute units idle, and
+  // its per-page cost is taken as 0.6 of a 128-row group's (two waves share
+  // each page tile's rows and merge at the end).
+  long long best_seg = 0;
+  int best_rpg = 0;
+  double best_cost = 0.0;
+  for (int rpg : {128, 64}) {
+    if (rows_per_group != 0 && rpg != rows_per_group) continue;
+    const long long groups = (rows + rpg - 1) / rpg;
+    long long G = num_cus / groups;
+    if (G < 1) G = 1;
+    long long seg = (total_pages + G - 1) / G;
+    if (seg < 1) seg = 1;
+    if (max_splits == 1) {
+      seg = -1;  // one chunk per sequence: segments are the sequences
+    } else if (max_chunks(seg) > max_splits) {
+      // The chunk cap binds: lengthen the segments until it holds
+      // (ceil(P / seg) + 1 segments can overlap a sequence).
+      long long lo = seg, hi = (max_pages + max_splits - 2) / (max_splits - 1);
+      if (hi < lo) hi = lo;
+      while (lo < hi) {
+        const long long mid = lo + (hi - lo) / 2;
+        if (max_chunks(mid) <= max_splits) hi = mid; else lo = mid + 1;
+      }
+      seg = lo;
+    }
+    const double per_page = rpg == 128 ? 1.0 : 0.6;
+    const double cost = (seg < 0 ? (double)max_pages : (double)seg) * per_page;
+    if (best_rpg == 0 || cost < best_cost) {
+      best_cost = cost;
+      best_seg = seg;
+      best_rpg = rpg;
+    }
+  }
+  // Build the chunks in the global page order (sequence-major), and the
+  // chunk range of every segment.
+  const size_t need_segs = best_seg < 0 ? (size_t)B : (size_t)((total_pages + best_seg - 1) / best_seg);
+  long long total_chunks = 0;
+  if (best_seg < 0) {
+    total_chunks = B;
+  } else {
+    long long start = 0;
+    for (int b = 0; b < B; ++b) {
+      const long long P = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+      total_chunks += (start + P - 1) / best_seg - start / best_seg + 1;
+      start += P;
+    }
+  }
+  if (total_chunks > INT_MAX / 4) return MLA_ERR_INVALID_ARG;
+  if (need_segs + 1 + 4 * (size_t)total_chunks > schedule_capacity) return MLA_ERR_WORKSPACE;
+  int32_t* seg_first = schedule_host;                    // [segments + 1]
+  int32_t* desc = schedule_host + need_segs + 1;         // [chunks][4]: b, first page, end page, L_b
+  long long c = 0, start = 0;
+  split_offsets_host[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    const long long L = seqlens_host[b];
+    const long long P = (L + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+    long long p = 0;
+    while (p < P) {
+      const long long seg_end = best_seg < 0 ? P : ((start + p) / best_seg + 1) * best_seg - start;
+      const long long e = seg_end < P ? seg_end : P;
+      desc[4 * c + 0] = b;
+      desc[4 * c + 1] = (int32_t)p;
+      desc[4 * c + 2] = (int32_t)e;
+      desc[4 * c + 3] = (int32_t)L;
+      ++c;
+      p = e;
+    }
+    split_offsets_host[b + 1] = (int32_t)c;
+    start += P;
+  }
+  // Segment s holds the chunks whose first page lies in it.
+  long long s = 0;
+  seg_first[0] = 0;
+  start = 0;
+  long long ci = 0;
+  for (int b = 0; b < B; ++b) {
+    const long long P = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+    for (long long k = split_offsets_host[b]; k < split_offsets_host[b + 1]; ++k, ++ci) {
+      const long long g = best_seg < 0 ? b : (start + desc[4 * k + 1]) / best_seg;
+      while (s < g) seg_first[++s] = (int32_t)ci;
+    }
+    start += P;
+  }
+  while (s < (long long)need_segs) seg_first[++s] = (int32_t)ci;
+  *num_segments = (int)need_segs;
+  *rows_per_group_out = best_rpg;
+  if (workspace_bytes) *workspace_bytes = workspace_size(total_chunks, s_q, H);
+  return MLA_OK;
+}
+
 }  // extern "C"
 
 namespace mla {
@@ -105,7 +240,8 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
                         const int32_t* split_offsets, int total_splits, int B, int s_q, int H, int d_qk,
                         int d_v, int page_size, int max_pages_per_seq, int num_pages, float softmax_scale,
                         int causal, mla_dtype_t dtype, void* workspace, size_t workspace_bytes, void* o_lat,
-                        float* lse, void* stream, const PartialBuffers* parts) {
+                        float* lse, void* stream, const PartialBuffers* parts, const int32_t* schedule,
+                        int num_segments, int rows_per_group) {
   if (!q_lat || !kv_cache || !block_table || !seqlens) return MLA_ERR_INVALID_ARG;
   // Partials only: no outputs, which needs split offsets and a workspace.
   const bool partials_only = !o_lat && !lse;
@@ -124,6 +260,15 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
     if (total_splits < B || (long long)total_splits > (long long)B * MLA_MAX_SPLITS)
       return MLA_ERR_INVALID_ARG;
     if (!parts && (!workspace || workspace_bytes < workspace_size(total_splits, s_q, H))) return MLA_ERR_WORKSPACE;
+  }
+  if (schedule) {
+    // Balanced schedule: bf16 dense decode only, with its own launch shape.
+    if (!split_offsets) return MLA_ERR_INVALID_ARG;
+    if (indices || row_scales || dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+    if (rows_per_group != 64 && rows_per_group != 128) return MLA_ERR_INVALID_ARG;
+    if (num_segments < 1 || num_segments > total_splits) return MLA_ERR_INVALID_ARG;
+    const long long groups = ((long long)s_q * H + rows_per_group - 1) / rows_per_group;
+    if (((long long)num_segments + 7) / 8 * 8 * groups > INT_MAX) return MLA_ERR_INVALID_ARG;
   }
   if (parts && parts->check_only) return MLA_OK;
   if (parts && (!parts->o_part || !parts->lse_part)) return MLA_ERR_INVALID_ARG;
@@ -146,6 +291,9 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
   a.indices = indices;
   a.topk = topk;
   a.row_scales = row_scales;
+  a.schedule = schedule;
+  a.num_segments = num_segments;
+  a.rows_per_group = schedule ? rows_per_group : mla::kRowsPerGroup;
   if (split_offsets && parts) {
     a.o_part = parts->o_part;
     a.lse_part = parts->lse_part;
@@ -183,6 +331,19 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* kv_cache, const int32
   return run_decode(q_lat, kv_cache, nullptr, block_table, seqlens, nullptr, 0, split_offsets, total_splits, B, s_q, H,
                     d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, dtype, workspace,
                     workspace_bytes, o_lat, lse, stream, nullptr);
+}
+
+mla_status_t mla_decode_fwd_scheduled(const void* q_lat, const void* kv_cache, const int32_t* block_table,
+                                      const int32_t* seqlens, const int32_t* split_offsets,
+                                      const int32_t* schedule, int num_segments, int rows_per_group,
+                                      int total_splits, int B, int s_q, int H, int d_qk, int d_v,
+                                      int page_size, int max_pages_per_seq, int num_pages,
+                                      float softmax_scale, int causal, mla_dtype_t dtype, void* workspace,
+                                      size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
+  if (!schedule) return MLA_ERR_INVALID_ARG;
+  return run_decode(q_lat, kv_cache, nullptr, block_table, seqlens, nullptr, 0, split_offsets, total_splits, B, s_q, H,
+                    d_qk, d_v, page_size, max_pages_per_seq, num_pages, softmax_scale, causal, dtype, workspace,
+                    workspace_bytes, o_lat, lse, stream, nullptr, schedule, num_segments, rows_per_group);
 }
 
 mla_status_t mla_sparse_decode_fwd(const void* q_lat, const void* kv_cache, const int32_t* block_table,

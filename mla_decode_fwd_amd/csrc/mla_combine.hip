@@ -8,8 +8,9 @@
 // and a chunk with lse_k = -inf (no allowed key) adds nothing.
 //
 // One wave per row: lane k < n reads lse_k, two wave reductions give M and
-// the sum, then every lane owns 8 of the 512 columns and streams the chunks'
-// partial rows (in the output dtype: bf16 or fp32) eight chunks at a time.
+// the sum, and every lane owns 8 of the 512 columns of the chunks' partial
+// rows (in the output dtype: bf16 or fp32), read eight chunks at a time, the
+// first eight together with the LSEs.
 
 #include <hip/hip_runtime.h>
 #include <cmath>
@@ -51,7 +52,34 @@ __global__ __launch_bounds__(64 * kWaves) void combine_kernel(const void* __rest
   const int n = min(min(max(split_offsets[b + 1] - s0, 0), kMaxSplits), total_splits - s0);
   if (n == 0 || (skip_single && n == 1)) return;
 
+  // Lane l owns columns 8l .. 8l+7. The first eight chunks' rows are
+  // requested together with the LSEs (they do not depend on the weights),
+  // so the two loads' latencies overlap; later chunks follow eight at a time.
+  float v[8][8];
+  const auto load_round = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      if (k < n) {
+        const size_t off = ((size_t)(s0 + k) * rows + row) * kDv + 8 * lane;
+        if (kBf16) {
+          const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(o_part) + off);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] = (float)x[e];
+        } else {
+          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(o_part) + off);
+          const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[j][e] = x0[e]; v[j][4 + e] = x1[e]; }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+      }
+    }
+  };
   const float lk = lane < n ? lse_part[(size_t)(s0 + lane) * rows + row] : -INFINITY;
+  load_round(0);
   const float M = wave_max(lk);
   const float Mf = (M == -INFINITY) ? 0.f : M;
   const float w = (lane < n) ? expf(lk - Mf) : 0.f;
@@ -59,33 +87,15 @@ __global__ __launch_bounds__(64 * kWaves) void combine_kernel(const void* __rest
   const float lse_v = (S > 0.f) ? Mf + logf(S) : -INFINITY;
   const float wn = (S > 0.f) ? w / S : 0.f;  // exp(lse_k - lse); lanes >= n hold 0
 
-  // Lane l owns columns 8l .. 8l+7. The chunks are read eight at a time with
-  // independent loads, so their latencies overlap.
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < n; k0 += 8) {
-    float v[8][8];
-    float wk[8];
+    if (k0 > 0) load_round(k0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int k = k0 + j;
-      wk[j] = __shfl(wn, k & 63, 64);
-      const size_t off = ((size_t)(s0 + min(k, n - 1)) * rows + row) * kDv + 8 * lane;
-      if (kBf16) {
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(o_part) + off);
+      const float wk = __shfl(wn, (k0 + j) & 63, 64);  // 0 past n
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = (float)x[e];
-      } else {
-        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(o_part) + off);
-        const f32x4_t x0 = src[0], x1 = src[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { v[j][e] = x0[e]; v[j][4 + e] = x1[e]; }
-      }
-      if (k >= n) wk[j] = 0.f;  // re-read of the last chunk, weighted out
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, v[j][e], acc[e]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk[j], v[j][e], acc[e]);
   }
   if (kBf16) {
     bf16x8_t o;

@@ -54,6 +54,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "mla_decode_common.h"
 #include "mla_internal.h"
@@ -77,6 +78,7 @@ __device__ __forceinline__ int swz(int t) {
 __device__ __forceinline__ int slot_bytes(int t, int c) {
   return (64 * (9 * (t >> 3) + (c >> 3)) + 8 * (t & 7) + ((c & 7) ^ swz(t))) * 16;
 }
+
 
 // The loads of one page into an LDS buffer. Wave w fills blocks 18w .. 18w+17:
 // token octets 2w and 2w+1, lines j = 0..8 each. Lane l takes token
@@ -161,52 +163,49 @@ __device__ __forceinline__ void issue_page(const GatherLoad& p) {
   for (int n = 0; n < kBlocksPerWave; ++n) issue_line(p, n);
 }
 
-// kSparse: top-k decode. The chunk walks "pages" of 64 consecutive entries of
-// the query token's selected-token list instead of the sequence's pages: the
-// prologue resolves the chunk's entries through the block table into
-// physical row numbers (kept in LDS after the page buffers, with one 64-bit
-// validity mask per page), each page is then gathered row by row, and
-// entries outside [0, L_b) are masked out of the softmax (their slot is
+// One chunk of work: query rows of row group `rgrp` of sequence b against
+// pages [pg0, pg1) of the sequence (dense), or against 64-entry "pages"
+// [pg0, pg1) of the query token's selected-token list (kSparse: top-k
+// decode; the prologue resolves the chunk's entries through the block table
+// into physical row numbers, kept in LDS after the page buffers with one
+// 64-bit validity mask per page, each page is then gathered row by row, and
+// entries outside [0, L_b) are masked out of the softmax; their slot is
 // loaded from the sequence's token 0, so P = 0 meets finite values).
-template <bool kSparse>
-__global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a, int row_groups) {
-  constexpr int kSparseBytes = kSparse ? kSparseMaxTopk * 4 + (kSparseMaxTopk / kPage) * 8 : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + kSparseBytes];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it in an SGPR
+//
+// kHalf: a 64-row group. Waves w and w^2 hold the same 32 rows; wave w takes
+// the 32-token tile w>>1 of every page (its own QK, softmax and PV), and at
+// the end the tile-1 wave hands its running max, sum and O to the tile-0
+// wave through LDS, which merges them and writes the rows. Every page is
+// still loaded whole by all four waves.
+//
+// part: the partial's index (the chunk's index in the merge layout); direct:
+// the chunk is its sequence's only one and outputs go straight to o_lat/lse.
+template <bool kSparse, bool kHalf>
+__device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, const int b, const int L, const int pg0,
+                                             const int pg1, const int part, const bool direct, const int rgrp,
+                                             const int wave) {
+  // The lane index and H are made opaque here, so that the per-lane LDS
+  // offsets and the row arithmetic derived from them are computed inside
+  // each chunk rather than hoisted out of a workgroup's chunk loop, where
+  // they would stay live (and spill) across every chunk's page loop.
+  const int lane = lane_id();
+  const int tid = wave * 64 + lane;
+  int H = a.H;
+  asm volatile("" : "+s"(H));
+  const char* q_base = static_cast<const char*>(a.q_lat);
+  asm volatile("" : "+s"(q_base));
   const int r32 = lane & 31;   // the row this lane owns in MFMA outputs
   const int hi32 = lane >> 5;  // upper half of the wave
-
-  // XCD-aware mapping: workgroups x and x+8j run on the same XCD (its own
-  // L2). Each XCD takes a contiguous range of chunks, so the chunks of one
-  // sequence (which load the same Q rows) and the row groups of one chunk
-  // (which read the same pages) share an L2.
-  const int x = blockIdx.x;
-  const int xcd = x & 7;
-  const int rest = x >> 3;
-  const int rgrp = rest % row_groups;
-  const int per_xcd = (a.total_splits + 7) / 8;
-  const int g = xcd * per_xcd + rest / row_groups;
-  if (rest / row_groups >= per_xcd || g >= a.total_splits) return;
-
-  const WorkItem wi = find_work(a.split_offsets, a.seqlens, a.B, g, lane);
-  const int b = wi.b;
-  // Top-k: the chunks split the list (topk entries); positions must be < L.
-  const int L = max(kSparse ? 1 : a.s_q, min(wi.L, a.max_pages * kPage));
-  const int P = ((kSparse ? a.topk : L) + kPage - 1) / kPage;
-  const int n_chunks = min(max(wi.n, 1), kMaxSplits);
-  const int kk = min(max(wi.k, 0), n_chunks - 1);
-  // kk * P < 64 * 2^25: exact in 32-bit unsigned arithmetic.
-  const int pg0 = (int)((unsigned)kk * (unsigned)P / (unsigned)n_chunks);
-  const int pg1 = (int)((unsigned)(kk + 1) * (unsigned)P / (unsigned)n_chunks);
+  constexpr int kGroupRows = kHalf ? kRowsPerGroup / 2 : kRowsPerGroup;
+  const int slice = kHalf ? (wave & 1) : wave;  // 32-row slice of the row group
+  const int my_tile = wave >> 1;                // kHalf: the page tile this wave takes
 
   // Rows past the end (H*s_q not a multiple of 32) compute on a clamped row
   // and write nothing.
-  const int rows = a.s_q * a.H;
-  const int row = rgrp * kRowsPerGroup + wave * kWaveRows + r32;
+  const int rows = a.s_q * H;
+  const int row = rgrp * kGroupRows + slice * kWaveRows + r32;
   const int row_c = min(row, rows - 1);
-  const int qi = row_c / a.H;
+  const int qi = row_c / H;
   const int n_allowed = a.causal ? (L - a.s_q + qi + 1) : L;
   // Smallest allowed count over all rows (query 0's), the same for every wave.
   const int n_allowed_min = a.causal ? (L - a.s_q + 1) : L;
@@ -231,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     const int n_tok = (pg1 - pg0) * kPage;  // <= kSparseMaxTopk
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int t = it * kThreads + (int)threadIdx.x;
+      const int t = it * kThreads + tid;
       const int e = pg0 * kPage + t;
       lpos[it] = (t < n_tok && e < a.topk) ? list[e] : -1;
     }
@@ -252,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   // of column l&31).
   bf16x8_t qf[kQSteps];
   {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q_lat) + ((size_t)b * rows + row_c) * kDqk + 8 * hi32;
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(q_base) + ((size_t)b * rows + row_c) * kDqk + 8 * hi32;
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
   }
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     const int n_tok = (pg1 - pg0) * kPage;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int t = it * kThreads + (int)threadIdx.x;
+      const int t = it * kThreads + tid;
       const bool valid = lpos[it] >= 0 && lpos[it] < L;
       const unsigned long long m = __ballot(valid);  // wave w of round it holds page 4*it + w
       if (t < n_tok) {
@@ -321,8 +320,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     // and also guarantees every wave is done with the other buffer.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    // The next page's 18 loads per wave are issued one per four QK k-steps
-    // over both tiles: in a denser burst the four waves' loads queue up in the
+    // The next page's 18 loads per wave are spread over this page's QK
+    // k-steps: in a denser burst the four waves' loads queue up in the
     // address unit and stall the MFMA stream behind them. (Built
     // unconditionally, from a clamped table index, so that its bases stay
     // wave-uniform SGPRs.)
@@ -347,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       if (valid < kPage) {
         // Zero the token slots past the end of the sequence: their scores are
         // masked, but 0 * NaN in PV would still poison the sum.
-        for (int idx = threadIdx.x; idx < (kPage - valid) * 72; idx += kThreads) {
+        for (int idx = tid; idx < (kPage - valid) * 72; idx += kThreads) {
           const int t = valid + idx / 72;
           const int c = idx % 72;
           *reinterpret_cast<uint4*>(buf + slot_bytes(t, c)) = make_uint4(0, 0, 0, 0);
@@ -357,13 +356,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     }
     const bool full_page = kSparse ? page_mask == ~0ull : (pg + 1) * kPage <= n_allowed_min;
 
-    // A page is two 32-token tiles, staggered in the source so that the
-    // softmax work of one tile sits between the MFMAs of the other: QK(T0);
-    // QK(T1) with tile 0's exponentials; PV(T0) with tile 1's exponentials;
-    // PV(T1) (the compiler gathers each tile's exponentials just before its
-    // PV).
-    // Tile 1's P uses a provisional reference taken before PV(T0); O and l
-    // move to it only after PV(T0) has added tile 0 (which used the old one).
     auto k_frag = [&](int T, int s) {
       return *reinterpret_cast<const bf16x8_t*>(buf + qk_x[s & 3] + 36864 * T + 1024 * (s >> 2));
     };
@@ -429,90 +421,147 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     constexpr int kKDepth = 3;
     constexpr int kPvDepth = 4;
 
-    // ---- QK(T0), with half of the next page's loads.
-    f32x16_t st0;
+    if constexpr (kHalf) {
+      // ---- One tile per wave: QK(T) with all 18 of the wave's next-page
+      // loads (one every two k-steps), then the tile's P (the first k-step's
+      // eight values up front, the other eight between PV MFMAs) and PV(T).
+      const int T = my_tile;
+      f32x16_t st;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st0[r] = 0.f;
-    {
-      bf16x8_t kf[kKDepth];
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      {
+        bf16x8_t kf[kKDepth];
 #pragma unroll
-      for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(0, s);
+        for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(T, s);
 #pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        const bf16x8_t cur = kf[s % kKDepth];
-        if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(0, s + kKDepth);
-        st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st0, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (has_next && (s & 3) == 0) issue_line(next, s >> 2);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < kQSteps; ++s) {
+          const bf16x8_t cur = kf[s % kKDepth];
+          if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(T, s + kKDepth);
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (has_next && (s & 1) == 0) issue_line(next, s >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    const float mt0 = tile_max(st0, 0);
-    move_reference((mt0 > m_ref + 8.0f) ? mt0 : m_ref);
-    const float neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
-
-    // ---- QK(T1), with tile 0's P (two values every four k-steps) and the
-    // other half of the next page's loads.
-    f32x16_t st1;
+      const float mt = tile_max(st, T);
+      move_reference((mt > m_ref + 8.0f) ? mt : m_ref);
+      const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+      bf16x8_t pf[2];
+      float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st1[r] = 0.f;
-    bf16x8_t pf0[2];
-    float psum0 = 0.f;
-    {
-      bf16x8_t kf[kKDepth];
+      for (int e = 0; e < 8; e += 2) p_pair(st, e, neg, pf, psum);
+      {
+        bf16x8_t vf[kPvDepth];
 #pragma unroll
-      for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(1, s);
+        for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(2 * T + (n >> 4), n & 15);
 #pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        const bf16x8_t cur = kf[s % kKDepth];
-        if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(1, s + kKDepth);
-        st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st1, 0, 0, 0);
-        if ((s & 3) == 0 && s < 32) p_pair(st0, s >> 1, neg0, pf0, psum0);
-        if (has_next && (s & 3) == 2) issue_line(next, 9 + (s >> 2));
-        __builtin_amdgcn_sched_barrier(0);
+        for (int n = 0; n < 2 * kColTiles; ++n) {
+          const bf16x8_t cur = vf[n % kPvDepth];
+          if (n + kPvDepth < 2 * kColTiles)
+            vf[n % kPvDepth] = v_frag(2 * T + ((n + kPvDepth) >> 4), (n + kPvDepth) & 15);
+          if ((n & 15) == 0)
+            mfma_pv<true>(acc_o[n & 15], cur, pf[n >> 4]);  // first use of this P fragment
+          else
+            mfma_pv<false>(acc_o[n & 15], cur, pf[n >> 4]);
+          if (n < kColTiles && (n & 3) == 0) p_pair(st, 8 + (n >> 1), neg, pf, psum);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    l_loc += psum0;
-    const float mt1 = tile_max(st1, 1);
-    const float m1 = (mt1 > m_ref + 8.0f) ? mt1 : m_ref;  // provisional reference of tile 1
-    const float neg1 = (m1 == -INFINITY) ? 0.f : -m1;
+      l_loc += psum;
+    } else {
+      // A page is two 32-token tiles, staggered in the source so that the
+      // softmax work of one tile sits between the MFMAs of the other: QK(T0);
+      // QK(T1) with tile 0's exponentials; PV(T0) with tile 1's exponentials;
+      // PV(T1) (the compiler gathers each tile's exponentials just before its
+      // PV). Tile 1's P uses a provisional reference taken before PV(T0); O
+      // and l move to it only after PV(T0) has added tile 0 (which used the
+      // old one).
 
-    // ---- PV(T0), with tile 1's P.
-    bf16x8_t pf1[2];
-    float psum1 = 0.f;
-    {
-      bf16x8_t vf[kPvDepth];
+      // ---- QK(T0), with half of the next page's loads.
+      f32x16_t st0;
 #pragma unroll
-      for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(n >> 4, n & 15);
+      for (int r = 0; r < 16; ++r) st0[r] = 0.f;
+      {
+        bf16x8_t kf[kKDepth];
 #pragma unroll
-      for (int n = 0; n < 2 * kColTiles; ++n) {
-        const bf16x8_t cur = vf[n % kPvDepth];
-        if (n + kPvDepth < 2 * kColTiles) vf[n % kPvDepth] = v_frag((n + kPvDepth) >> 4, (n + kPvDepth) & 15);
-        if ((n & 15) == 0)
-          mfma_pv<true>(acc_o[n & 15], cur, pf0[n >> 4]);  // first use of this P fragment
-        else
-          mfma_pv<false>(acc_o[n & 15], cur, pf0[n >> 4]);
-        if ((n & 3) == 0) p_pair(st1, n >> 1, neg1, pf1, psum1);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(0, s);
+#pragma unroll
+        for (int s = 0; s < kQSteps; ++s) {
+          const bf16x8_t cur = kf[s % kKDepth];
+          if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(0, s + kKDepth);
+          st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (has_next && (s & 3) == 0) issue_line(next, s >> 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    move_reference(m1);
-    l_loc += psum1;
+      const float mt0 = tile_max(st0, 0);
+      move_reference((mt0 > m_ref + 8.0f) ? mt0 : m_ref);
+      const float neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
 
-    // ---- PV(T1).
-    {
-      bf16x8_t vf[kPvDepth];
+      // ---- QK(T1), with tile 0's P (two values every four k-steps) and the
+      // other half of the next page's loads.
+      f32x16_t st1;
 #pragma unroll
-      for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(2 + (n >> 4), n & 15);
+      for (int r = 0; r < 16; ++r) st1[r] = 0.f;
+      bf16x8_t pf0[2];
+      float psum0 = 0.f;
+      {
+        bf16x8_t kf[kKDepth];
 #pragma unroll
-      for (int n = 0; n < 2 * kColTiles; ++n) {
-        const bf16x8_t cur = vf[n % kPvDepth];
-        if (n + kPvDepth < 2 * kColTiles) vf[n % kPvDepth] = v_frag(2 + ((n + kPvDepth) >> 4), (n + kPvDepth) & 15);
-        if ((n & 15) == 0)
-          mfma_pv<true>(acc_o[n & 15], cur, pf1[n >> 4]);
-        else
-          mfma_pv<false>(acc_o[n & 15], cur, pf1[n >> 4]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < kKDepth; ++s) kf[s] = k_frag(1, s);
+#pragma unroll
+        for (int s = 0; s < kQSteps; ++s) {
+          const bf16x8_t cur = kf[s % kKDepth];
+          if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(1, s + kKDepth);
+          st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st1, 0, 0, 0);
+          if ((s & 3) == 0 && s < 32) p_pair(st0, s >> 1, neg0, pf0, psum0);
+          if (has_next && (s & 3) == 2) issue_line(next, 9 + (s >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      l_loc += psum0;
+      const float mt1 = tile_max(st1, 1);
+      const float m1 = (mt1 > m_ref + 8.0f) ? mt1 : m_ref;  // provisional reference of tile 1
+      const float neg1 = (m1 == -INFINITY) ? 0.f : -m1;
+
+      // ---- PV(T0), with tile 1's P.
+      bf16x8_t pf1[2];
+      float psum1 = 0.f;
+      {
+        bf16x8_t vf[kPvDepth];
+#pragma unroll
+        for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(n >> 4, n & 15);
+#pragma unroll
+        for (int n = 0; n < 2 * kColTiles; ++n) {
+          const bf16x8_t cur = vf[n % kPvDepth];
+          if (n + kPvDepth < 2 * kColTiles) vf[n % kPvDepth] = v_frag((n + kPvDepth) >> 4, (n + kPvDepth) & 15);
+          if ((n & 15) == 0)
+            mfma_pv<true>(acc_o[n & 15], cur, pf0[n >> 4]);  // first use of this P fragment
+          else
+            mfma_pv<false>(acc_o[n & 15], cur, pf0[n >> 4]);
+          if ((n & 3) == 0) p_pair(st1, n >> 1, neg1, pf1, psum1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      move_reference(m1);
+      l_loc += psum1;
+
+      // ---- PV(T1).
+      {
+        bf16x8_t vf[kPvDepth];
+#pragma unroll
+        for (int n = 0; n < kPvDepth; ++n) vf[n] = v_frag(2 + (n >> 4), n & 15);
+#pragma unroll
+        for (int n = 0; n < 2 * kColTiles; ++n) {
+          const bf16x8_t cur = vf[n % kPvDepth];
+          if (n + kPvDepth < 2 * kColTiles) vf[n % kPvDepth] = v_frag(2 + ((n + kPvDepth) >> 4), (n + kPvDepth) & 15);
+          if ((n & 15) == 0)
+            mfma_pv<true>(acc_o[n & 15], cur, pf1[n >> 4]);
+          else
+            mfma_pv<false>(acc_o[n & 15], cur, pf1[n >> 4]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
@@ -520,7 +569,99 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   // ---- finalize: o = O / l, lse = ln2 * (m_ref + log2 l); l is split over
   // the two lanes of a row.
   agpr_fence();
-  const float l_tot = l_loc + other_half(l_loc);
+  float l_tot = l_loc + other_half(l_loc);
+  __syncthreads();  // every wave is done with the page buffers
+  // The lane position is taken afresh (mbcnt) rather than kept live through
+  // the page loop, where every VGPR is taken.
+  const int ln = lane_id();
+  const int r32f = ln & 31, hi32f = ln >> 5;
+  const int rowf = rgrp * kGroupRows + slice * kWaveRows + r32f;
+  if constexpr (kHalf) {
+    // The two waves of a pair hold the same 32 rows with (m, l, O) over
+    // complementary halves of every page. Wave t of the pair finalizes
+    // columns 256t .. 256t+255: each hands the other half of its O (fp32,
+    // lane-contiguous 16-byte pieces) and its m and l to its partner through
+    // LDS, merges what it receives with its own half by the textbook
+    // two-way rule straight into bf16 registers, then stages 512-byte half
+    // rows and stores them.
+    // One straight-line copy per t (acc_o is indexed with constants only: a
+    // runtime index would move it to scratch); both copies pass the same
+    // three barriers.
+    const int pair = wave & 1;
+    const auto finalize_half = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      char* const area = smem + pair * 65536;
+      float* const give = reinterpret_cast<float*>(area + t * 32768);
+      const float* const take = reinterpret_cast<const float*>(area + (t ^ 1) * 32768);
+      float* const ml = reinterpret_cast<float*>(smem + 131072 + pair * 512);  // [2][m 32 | l 32]
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc_o[(t ^ 1) * 8 + k][4 * q4 + e];  // the partner's columns
+          *reinterpret_cast<f32x4_t*>(give + ((4 * k + q4) * 64 + ln) * 4) = v;
+        }
+      if (hi32f == 0) {
+        ml[64 * t + r32f] = m_ref;
+        ml[64 * t + 32 + r32f] = l_tot;
+      }
+      __syncthreads();
+      const float m_o = ml[64 * (t ^ 1) + r32f];
+      const float l_o = ml[64 * (t ^ 1) + 32 + r32f];
+      const float m_new = fmaxf(m_ref, m_o);
+      const float a_s = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      const float a_o = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_o - m_new);
+      const float l_m = l_tot * a_s + l_o * a_o;
+      const bool any = l_m > 0.f;
+      const float inv = any ? 1.f / l_m : 0.f;
+      const float c_s = a_s * inv, c_o = a_o * inv;
+      const float lse_v = any ? (m_new + __log2f(l_m)) * 0.6931471805599453f : -INFINITY;
+      bf16x4_t res[32];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(take + ((4 * k + q4) * 64 + ln) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            res[4 * k + q4][e] = (__bf16)(acc_o[t * 8 + k][4 * q4 + e] * c_s + x[e] * c_o);  // this wave's columns
+        }
+      __syncthreads();  // both halves of every pair read; the areas are free
+      // Half row r of the wave: 512 bytes at r*512 in its 16 KB staging
+      // area, 16-byte piece p at (p ^ r) so a write's 32 rows spread over
+      // the banks.
+      char* const stage = area + t * 32768;
+#pragma unroll
+      for (int p = 0; p < 32; ++p)
+        *reinterpret_cast<bf16x4_t*>(stage + r32f * 512 + ((p ^ r32f) * 16) + 8 * hi32f) = res[p];
+      __syncthreads();
+      __bf16* const out = direct ? static_cast<__bf16*>(a.o_lat) + (size_t)b * rows * kDv
+                                 : static_cast<__bf16*>(a.o_part) + (size_t)part * rows * kDv;
+      const int row0 = rgrp * kGroupRows + slice * kWaveRows;
+#pragma unroll 4
+      for (int r = 0; r < kWaveRows; r += 2) {
+        const int rr = r + hi32f;  // two half rows per store instruction
+        if (row0 + rr < rows) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + rr * 512 + (((ln & 31) ^ rr) * 16));
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + rr) * kDv + 256 * t + 8 * (ln & 31)));
+        }
+      }
+      if (t == 0 && hi32f == 0 && rowf < rows) {
+        if (direct)
+          a.lse[(size_t)b * rows + rowf] = lse_v;
+        else
+          a.lse_part[(size_t)part * rows + rowf] = lse_v;
+      }
+    };
+    if (wave < 2)
+      finalize_half(std::integral_constant<int, 0>{});
+    else
+      finalize_half(std::integral_constant<int, 1>{});
+    return;
+  }
   const bool any = l_tot > 0.f;
   const float inv = any ? 1.f / l_tot : 0.f;
   const float lse_v = any ? (m_ref + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
@@ -530,15 +671,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   // would touch 32 rows per instruction, 16 bytes each: partial 128-byte lines
   // that stay dirty in L2 until the end of the kernel and then cost
   // microseconds to write back. Staged, every store instruction writes one
-  // whole 1 KB row, non-temporal: nothing reads it again in this kernel. Row r of a wave's 32 KB staging area keeps its 64 16-byte
-  // pieces XOR-permuted by r so that the 32 rows of a write do not fall on the
-  // same LDS banks.
-  __syncthreads();  // every wave is done with the page buffers
-  // The lane position is taken afresh (mbcnt) rather than kept live through
-  // the page loop, where every VGPR is taken.
-  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  const int r32f = ln & 31, hi32f = ln >> 5;
-  const int rowf = rgrp * kRowsPerGroup + wave * kWaveRows + r32f;
+  // whole 1 KB row, non-temporal: nothing reads it again in this kernel. Row r
+  // of a wave's 32 KB staging area keeps its 64 16-byte pieces XOR-permuted
+  // by r so that the 32 rows of a write do not fall on the same LDS banks.
   char* stage = smem + wave * (kWaveRows * kDv * 2);
 #pragma unroll
   for (int i = 0; i < kColTiles; ++i)
@@ -552,10 +687,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     }
   __syncthreads();
 
-  const bool direct = n_chunks == 1 && a.o_lat != nullptr;
   __bf16* const out = direct ? static_cast<__bf16*>(a.o_lat) + (size_t)b * rows * kDv
-                             : static_cast<__bf16*>(a.o_part) + (size_t)g * rows * kDv;
-  const int row0 = rgrp * kRowsPerGroup + wave * kWaveRows;
+                             : static_cast<__bf16*>(a.o_part) + (size_t)part * rows * kDv;
+  const int row0 = rgrp * kGroupRows + slice * kWaveRows;
 #pragma unroll 4
   for (int r = 0; r < kWaveRows; ++r) {
     if (row0 + r >= rows) break;
@@ -566,23 +700,97 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     if (direct)
       a.lse[(size_t)b * rows + rowf] = lse_v;
     else
-      a.lse_part[(size_t)g * rows + rowf] = lse_v;
+      a.lse_part[(size_t)part * rows + rowf] = lse_v;
   }
 }
 
-template <bool kSparse>
+// One schedule entry's four words (b, first page, end page, L_b), read by
+// four lanes side by side and broadcast.
+__device__ __forceinline__ void load_chunk_desc(const int32_t* desc, int c, int& b, int& p0, int& p1, int& L) {
+  const int lane = lane_id();
+  const int v = lane < 4 ? desc[4 * (size_t)c + lane] : 0;
+  b = __builtin_amdgcn_readlane(v, 0);
+  p0 = __builtin_amdgcn_readlane(v, 1);
+  p1 = __builtin_amdgcn_readlane(v, 2);
+  L = __builtin_amdgcn_readlane(v, 3);
+}
+
+template <bool kSparse, bool kHalf>
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a, int row_groups, int n_units) {
+  constexpr int kSparseBytes = kSparse ? kSparseMaxTopk * 4 + (kSparseMaxTopk / kPage) * 8 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + kSparseBytes];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it in an SGPR
+
+  // XCD-aware mapping: workgroups x and x+8j run on the same XCD (its own
+  // L2). Each XCD takes a contiguous range of work units (chunks, or the
+  // schedule's segments), so the chunks of one sequence (which load the same
+  // Q rows) and the row groups of one unit (which read the same pages) share
+  // an L2.
+  const int x = blockIdx.x;
+  const int xcd = x & 7;
+  const int rest = x >> 3;
+  const int rgrp = rest % row_groups;
+  const int per_xcd = (n_units + 7) / 8;
+  const int g = xcd * per_xcd + rest / row_groups;
+  if (rest / row_groups >= per_xcd || g >= n_units) return;
+
+  if (a.schedule != nullptr) {
+    // Balanced schedule: unit g is segment g; its chunks are consecutive
+    // entries, each a page range of one sequence with its own partial.
+    const int32_t* desc = a.schedule + a.num_segments + 1;
+    int c0 = g, c1 = g + 1;
+    if (a.num_segments != a.total_splits) {  // some segment holds several chunks
+      const int lane = lane_id();
+      const int v = lane < 2 ? a.schedule[g + lane] : 0;
+      c0 = min(max(__builtin_amdgcn_readlane(v, 0), 0), a.total_splits);
+      c1 = min(max(__builtin_amdgcn_readlane(v, 1), c0), a.total_splits);
+    }
+    for (int c = c0; c < c1; ++c) {
+      int b, p0, p1, Ld;
+      load_chunk_desc(desc, c, b, p0, p1, Ld);
+      b = min(max(b, 0), a.B - 1);
+      const int L = max(a.s_q, min(Ld, a.max_pages * kPage));
+      const int P = (L + kPage - 1) / kPage;
+      p1 = min(max(p1, 0), P);
+      p0 = min(max(p0, 0), p1);
+      const bool direct = p0 == 0 && p1 == P && a.o_lat != nullptr;
+      decode_chunk<false, kHalf>(a, smem, b, L, p0, p1, c, direct, rgrp, wave);
+      __syncthreads();  // the staging area is the next chunk's first page buffer
+    }
+    return;
+  }
+
+  const WorkItem wi = find_work(a.split_offsets, a.seqlens, a.B, g, lane_id());
+  // Top-k: the chunks split the list (topk entries); positions must be < L.
+  const int L = max(kSparse ? 1 : a.s_q, min(wi.L, a.max_pages * kPage));
+  const int P = ((kSparse ? a.topk : L) + kPage - 1) / kPage;
+  const int n_chunks = min(max(wi.n, 1), kMaxSplits);
+  const int kk = min(max(wi.k, 0), n_chunks - 1);
+  // kk * P < 64 * 2^25: exact in 32-bit unsigned arithmetic.
+  const int pg0 = (int)((unsigned)kk * (unsigned)P / (unsigned)n_chunks);
+  const int pg1 = (int)((unsigned)(kk + 1) * (unsigned)P / (unsigned)n_chunks);
+  decode_chunk<kSparse, kHalf>(a, smem, wi.b, L, pg0, pg1, g, n_chunks == 1 && a.o_lat != nullptr, rgrp, wave);
+}
+
+template <bool kSparse, bool kHalf>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   const int rows = a.s_q * a.H;
-  const int row_groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
-  const int padded = (a.total_splits + 7) / 8 * 8;
+  const int group_rows = kHalf ? kRowsPerGroup / 2 : kRowsPerGroup;
+  const int row_groups = (rows + group_rows - 1) / group_rows;
+  const int units = a.schedule != nullptr ? a.num_segments : a.total_splits;
+  const int padded = (units + 7) / 8 * 8;
   const dim3 grid((unsigned)(padded * row_groups));
-  hipLaunchKernelGGL(mla_decode_bf16_kernel<kSparse>, grid, dim3(kThreads), 0, stream, a, row_groups);
+  hipLaunchKernelGGL((mla_decode_bf16_kernel<kSparse, kHalf>), grid, dim3(kThreads), 0, stream, a, row_groups, units);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch<false>(a, stream); }
-hipError_t launch_sparse_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch<true>(a, stream); }
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+  if (a.schedule != nullptr && a.rows_per_group == kRowsPerGroup / 2) return launch<false, true>(a, stream);
+  return launch<false, false>(a, stream);
+}
+hipError_t launch_sparse_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch<true, false>(a, stream); }
 
 }  // namespace mla

@@ -38,6 +38,13 @@ struct DecodeArgs {
   const int32_t* indices = nullptr;  // top-k decode: [B, s_q, topk] token positions
   int topk = 0;
   const float* row_scales = nullptr;  // FP8 cache: [num_pages, 64] fp32, one per cache row
+  // Balanced schedule (bf16 dense decode only): [num_segments + 1] first
+  // chunk of each segment, then [total_splits][4] = (b, first page, end
+  // page, L_b) per chunk. nullptr: one chunk per workgroup, near-equal page
+  // counts per sequence (split_offsets alone).
+  const int32_t* schedule = nullptr;
+  int num_segments = 0;
+  int rows_per_group = kRowsPerGroup;  // 128, or 64 (two waves share each 32-row slice)
 };
 
 constexpr int kSparseMaxTopk = 2048;  // selected tokens per query token at most
@@ -59,7 +66,8 @@ mla_status_t run_decode(const void* q_lat, const void* kv_cache, const float* ro
                         const int32_t* split_offsets, int total_splits, int B, int s_q, int H, int d_qk,
                         int d_v, int page_size, int max_pages_per_seq, int num_pages, float softmax_scale,
                         int causal, mla_dtype_t dtype, void* workspace, size_t workspace_bytes, void* o_lat,
-                        float* lse, void* stream, const PartialBuffers* parts);
+                        float* lse, void* stream, const PartialBuffers* parts, const int32_t* schedule = nullptr,
+                        int num_segments = 0, int rows_per_group = 0);
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp32(const DecodeArgs& a, hipStream_t stream);

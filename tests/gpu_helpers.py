@@ -47,12 +47,17 @@ def to_device(case, dev="cuda"):
                 block_table=case.block_table.to(dev), seqlens=case.seqlens.to(dev))
 
 
-def run(case, plan="auto", dev_inputs=None, num_cus=256, max_splits=64, split_offsets=None):
+def run(case, plan="auto", dev_inputs=None, num_cus=256, max_splits=64, split_offsets=None, rows_per_group=0):
     """Decode on the GPU. plan: "auto" (library planner), None (one chunk per
-    sequence) or "custom" with explicit host split_offsets."""
+    sequence), "custom" with explicit host split_offsets, or "schedule" (the
+    balanced schedule, mla_decode_fwd_scheduled; rows_per_group 0 lets the
+    planner choose 64 or 128)."""
     d = dev_inputs or to_device(case)
     kw = {}
-    if plan == "auto":
+    if plan == "schedule":
+        kw = dict(schedule=mla.decode_schedule(case.seqlens.tolist(), case.s_q, case.H, num_cus=num_cus,
+                                               max_splits=max_splits, rows_per_group=rows_per_group))
+    elif plan == "auto":
         p = mla.decode_plan(case.seqlens.tolist(), case.s_q, case.H, num_cus=num_cus, max_splits=max_splits)
         if p.any_split:
             kw = dict(split_offsets=p.device_offsets("cuda"), total_splits=p.total_splits)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 6
+    assert mla.abi_version() == 7
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -288,3 +288,111 @@ def test_fp8_products_validation(lib):
     assert out_uv(wsb=mla.fp8_workspace_size(4 * 8 * 512) - 1) == WORKSPACE
     assert lib.mla_quantize_e4m3(FAKE, 0, FAKE, 1024, FAKE, FAKE, None) == INVALID
     assert lib.mla_quantize_e4m3(FAKE, 64, FAKE, 1023, FAKE, FAKE, None) == WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# Balanced schedule (mla_decode_schedule)
+# ---------------------------------------------------------------------------
+
+def _check_schedule(s, lens, s_q, H, num_cus, max_splits):
+    """Structural invariants of a schedule: every sequence's pages are tiled
+    by its chunks in order, within the cap; each segment is a run of
+    consecutive chunks over consecutive global pages; the launch fits."""
+    P = [(int(L) + 63) // 64 for L in lens]
+    ch = s.chunks
+    off = s.split_offsets
+    assert off[0] == 0 and off[-1] == len(ch) == s.total_splits
+    for b, L in enumerate(lens):
+        mine = ch[off[b]:off[b + 1]]
+        assert 1 <= len(mine) <= max_splits
+        assert (mine[:, 0] == b).all() and (mine[:, 3] == L).all()
+        assert mine[0, 1] == 0 and mine[-1, 2] == P[b]
+        assert (mine[1:, 1] == mine[:-1, 2]).all() and (mine[:, 2] > mine[:, 1]).all()
+    start = np.concatenate([[0], np.cumsum(P)])
+    g0 = start[ch[:, 0]] + ch[:, 1]  # global first page of every chunk
+    sf = s.segment_first_chunk
+    assert sf[0] == 0 and sf[-1] == len(ch) and (np.diff(sf) >= 1).all()
+    seg_pages = []
+    for i in range(s.num_segments):
+        c = np.arange(sf[i], sf[i + 1])
+        assert (g0[c[1:]] == g0[c[:-1]] + (ch[c[:-1], 2] - ch[c[:-1], 1])).all()  # contiguous pages
+        seg_pages.append(int((ch[c, 2] - ch[c, 1]).sum()))
+    groups = -(-(s_q * H) // s.rows_per_group)
+    assert s.num_segments * groups <= max(num_cus, groups)
+    return seg_pages
+
+
+@pytest.mark.parametrize("lens,s_q,H,num_cus", [([4096] * 64, 1, 128, 256), ([65536, 32768, 16384, 8192, 4096, 2048,
+                                                                              1024, 513], 1, 128, 256),
+                                                 ([4096], 1, 128, 256), ([300, 64, 129, 7], 2, 128, 8),
+                                                 ([33, 250], 1, 1, 16), ([190], 16, 8, 64)])
+def test_schedule_structure(lens, s_q, H, num_cus):
+    s = mla.decode_schedule(lens, s_q, H, num_cus=num_cus)
+    _check_schedule(s, lens, s_q, H, num_cus, 64)
+    assert s.workspace_bytes == mla.decode_workspace_size(s.total_splits, s_q, H)
+
+
+def test_schedule_balances_the_workload_shapes():
+    # B=64 x 4096: 256 segments of exactly 16 pages, 128-row groups (the
+    # equal-split plan's shape).
+    s = mla.decode_schedule([4096] * 64, 1, 128)
+    assert s.rows_per_group == 128 and s.num_segments == 256 and s.total_splits == 256
+    assert set(_check_schedule(s, [4096] * 64, 1, 128, 256, 64)) == {16}
+    # Long context: with 128-row groups the 64K sequence would need 128
+    # chunks of 8 pages; 64-row groups give 128 segments of <= 16 pages (256
+    # workgroups) and exactly 64 chunks for it.
+    lens = [65536, 32768, 16384, 8192, 4096, 2048, 1024, 513]
+    s = mla.decode_schedule(lens, 1, 128)
+    pages = _check_schedule(s, lens, 1, 128, 256, 64)
+    assert s.rows_per_group == 64 and s.num_segments == 128 and max(pages) == 16
+    assert s.num_splits[0] == 64
+    # MTP s_q = 2, lengths U{1024..8192}: 128 segments (two row groups each)
+    # of the same page count, the last one shorter.
+    rng = np.random.default_rng(3)
+    lens = rng.integers(1024, 8193, 128).tolist()
+    s = mla.decode_schedule(lens, 2, 128)
+    pages = _check_schedule(s, lens, 2, 128, 256, 64)
+    assert s.rows_per_group == 128 and s.num_segments == 128
+    assert max(pages) == -(-sum((L + 63) // 64 for L in lens) // 128) and min(pages[:-1]) == max(pages)
+
+
+def test_schedule_cap_and_forced_row_groups():
+    lens = [64 * 1000, 64]
+    for rpg in (64, 128):
+        s = mla.decode_schedule(lens, 1, 128, rows_per_group=rpg)
+        assert s.rows_per_group == rpg
+        _check_schedule(s, lens, 1, 128, 256, 64)
+    s = mla.decode_schedule(lens, 1, 128, max_splits=5)
+    assert s.num_splits.max() <= 5
+    _check_schedule(s, lens, 1, 128, 256, 5)
+    s = mla.decode_schedule([500, 70, 3000], 1, 128, max_splits=1)
+    assert (s.num_splits == 1).all() and s.num_segments == 3
+
+
+def test_schedule_invalid_arguments(lib):
+    L = np.array([100, 3], np.int32)
+    off = np.zeros(3, np.int32)
+    sched = np.zeros(64, np.int32)
+    n, r = ctypes.c_int(0), ctypes.c_int(0)
+    c = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    call = lambda *a: lib.mla_decode_schedule(*a)
+    assert call(c(L), 2, 4, 128, 256, 64, 0, c(off), c(sched), 64, ctypes.byref(n), ctypes.byref(r), None) == INVALID
+    assert call(c(L), 2, 1, 128, 256, 65, 0, c(off), c(sched), 64, ctypes.byref(n), ctypes.byref(r), None) == INVALID
+    assert call(c(L), 2, 1, 128, 256, 64, 32, c(off), c(sched), 64, ctypes.byref(n), ctypes.byref(r), None) == INVALID
+    assert call(c(L), 2, 1, 128, 256, 64, 0, c(off), c(sched), 3, ctypes.byref(n), ctypes.byref(r), None) == WORKSPACE
+    assert call(c(L), 2, 1, 128, 256, 64, 0, c(off), c(sched), 64, ctypes.byref(n), ctypes.byref(r), None) == OK
+    # The scheduled decode's own checks (no launch): bf16 only, a schedule
+    # needs split offsets, a known row-group size and a plausible segment count.
+    f = lib.mla_decode_fwd_scheduled
+    base = dict(so=FAKE, sched=FAKE, nseg=2, rpg=128, total=4, dtype=0)
+
+    def fwd(**kw):
+        a = dict(base, **kw)
+        return f(FAKE, FAKE, FAKE, FAKE, a["so"], a["sched"], a["nseg"], a["rpg"], a["total"], 2, 1, 128, 576, 512, 64,
+                 4, 8, 0.0722, 0, a["dtype"], FAKE, 1 << 30, FAKE, FAKE, None)
+    assert fwd(sched=None) == INVALID
+    assert fwd(so=None) == INVALID
+    assert fwd(dtype=1) == UNSUPPORTED
+    assert fwd(rpg=32) == INVALID
+    assert fwd(nseg=0) == INVALID
+    assert fwd(nseg=5) == INVALID  # more segments than chunks
