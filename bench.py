@@ -24,9 +24,7 @@ several microseconds, so none sits inside a region), so the three regions see
 the same phase of the GPU clock; the medians over the second half of 24
 rounds are reported, with the step time measured in the same rounds
 (`interleaved_step_us`), the gap between it and decode + merge
-(`launch_gap_us`), and the shader clock (`shader_clock_mhz`): the SMI's
-current clock, averaged over the XCDs, sampled every half millisecond while
-about 100 ms of decode launches run back to back. `traffic` (measured HBM bytes per launch) is
+(`launch_gap_us`). `traffic` (measured HBM bytes per launch) is
 the scaled FETCH_SIZE + WRITE_SIZE reading kept in
 profiles/mla_decode_bf16_b64_ctx4096.md (made by
 mla_decode_fwd_amd.profile_summary from rocprofv3 counter runs of this
@@ -382,95 +380,12 @@ def absorb_main(args):
     print(json.dumps(out_json), flush=True)
 
 
-class ClockSampler:
-    """Samples the GPU's shader clock from the SMI (amdsmi gpu metrics,
-    current_gfxclks: one value per XCD, in MHz) in a background thread while
-    GPU work runs. The SMI's figure is the power manager's own, refreshed
-    about every millisecond, so only bursts much longer than that are
-    measured. Gives None if amdsmi is missing or the device is not found."""
-
-    def __init__(self, period_s: float = 0.0005):
-        import threading
-
-        self.period = period_s
-        self.samples = []
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._handle = None
-        try:
-            import amdsmi
-            import torch
-
-            self._amdsmi = amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            want = None
-            props = torch.cuda.get_device_properties(torch.cuda.current_device())
-            bus = getattr(props, "pci_bus_id", None)
-            for h in handles:
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
-                if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
-                    want = h
-            if want is None and len(handles) == 1:
-                want = handles[0]
-            if want is None:
-                raise RuntimeError(f"device not identified among {len(handles)} SMI handles")
-            self._handle = want
-        except Exception as e:  # no SMI access: report null
-            self.error = f"{type(e).__name__}: {e}"
-
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-        vals = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 10000]
-        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
-            vals = [m["current_gfxclk"]]
-        return sum(vals) / len(vals) if vals else None
-
-    def _run(self):
-        import time as _t
-
-        while not self._stop.is_set():
-            try:
-                v = self._read()
-                if v is not None:
-                    self.samples.append(v)
-            except Exception as e:
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            _t.sleep(self.period)
-
-    def start(self):
-        import threading
-
-        if self._handle is None:
-            return
-        self.samples = []
-        self._stop.clear()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-        self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-            self._thread = None
-
-    def median(self):
-        if not self.samples:
-            return None
-        s = sorted(self.samples)
-        return s[len(s) // 2]
-
-
 def interleaved_regions(step, decode, combine, stream, rounds: int, block: int) -> dict:
     """The decode kernel's and the merge's average durations, measured in
     interleaved rounds of [block steps | block decode launches | block merge
     launches], each region bracketed by one event pair, so that all three see
     the same phase of the GPU's clock. The medians over the second half of the
-    rounds are reported (the first half lets a burst settle). Then a burst of
-    decode launches alone (about 100 ms) runs while the SMI's shader clock is
-    sampled: the clock the decode kernel runs at under sustained load."""
+    rounds are reported (the first half lets a burst settle)."""
     import torch
 
     per = {"step": [], "decode": [], "combine": []}
@@ -487,16 +402,8 @@ def interleaved_regions(step, decode, combine, stream, rounds: int, block: int) 
     for name, ev in per.items():
         ms = sorted(a.elapsed_time(b) / block for a, b in ev[rounds // 2:])
         med[name] = ms[len(ms) // 2]
-    sampler = ClockSampler()
-    n_burst = max(block, int(100.0 / max(med["decode"], 1e-3)))
-    sampler.start()
-    for i in range(n_burst):
-        decode(i)
-    torch.cuda.synchronize()
-    sampler.stop()
-    return {"step_ms": med["step"], "decode_ms": med["decode"], "combine_ms": med["combine"],
-            "clock_mhz": sampler.median(), "clock_samples": len(sampler.samples), "clock_error": sampler.error,
-            "burst": n_burst, "rounds": rounds, "block": block}
+    return {"step_ms": med["step"], "decode_ms": med["decode"], "combine_ms": med["combine"], "rounds": rounds,
+            "block": block}
 
 
 def main():
@@ -512,6 +419,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-mb", type=int, default=0)
+    ap.add_argument("--skip-extra", action="store_true",
+                    help="leave out the per-step-event and warm-cache regions (for kernel-trace profiles)")
     ap.add_argument("--plan", default="schedule", choices=["schedule", "equal"],
                     help="schedule: the balanced schedule (mla_decode_schedule, bf16 dense decode); equal: "
                          "near-equal chunks per sequence (mla_decode_plan)")
@@ -630,15 +539,15 @@ def main():
     # and the K steps again on one copy of the cache only (part of its 302 MB
     # then stays in the 256 MB last-level cache between steps).
     per_step = []
-    for i in range(args.steps):
+    for i in range(0 if args.skip_extra else args.steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         step(i)
         e1.record(stream)
         per_step.append((e0, e1))
     torch.cuda.synchronize()
-    per_step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in per_step)
-    warm_ms, _ = timed(lambda i: step(0))
+    per_step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in per_step) or [float("nan")]
+    warm_ms = float("nan") if args.skip_extra else timed(lambda i: step(0))[0]
 
     if args.copy_mb > 0:
         n = args.copy_mb << 20
@@ -707,22 +616,18 @@ def main():
                      "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),
                      "interleaved_step_us": round(rr["step_ms"] * 1e3, 2),
                      "launch_gap_us": round((rr["step_ms"] - decode_ms - combine_ms) * 1e3, 2),
-                     "shader_clock_mhz": None if rr["clock_mhz"] is None else round(rr["clock_mhz"], 1),
                      "timing": (f"medians of the last {rr['rounds'] - rr['rounds'] // 2} of {rr['rounds']} "
                                 f"interleaved rounds of [{rr['block']} steps | {rr['block']} decode launches | "
-                                f"{rr['block']} merge launches], after the timed steps; shader clock: median of "
-                                f"{rr['clock_samples']} SMI samples (mean over XCDs) during {rr['burst']} "
-                                "back-to-back decode launches" +
-                                (f" (SMI unavailable: {rr['clock_error']})" if rr["clock_error"] else "")),
+                                f"{rr['block']} merge launches], after the timed steps"),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},
         "plan_host_us": round(plan_us, 1),
         "step_gpu_ms": round(step_gpu_ms, 5),
-        "step_us_percentiles": {"p10": round(per_step_us[len(per_step_us) // 10], 2),
+        "step_us_percentiles": None if args.skip_extra else {"p10": round(per_step_us[len(per_step_us) // 10], 2),
                                 "median": round(per_step_us[len(per_step_us) // 2], 2),
                                 "p90": round(per_step_us[(9 * len(per_step_us)) // 10], 2),
                                 "note": "one event pair per step, separate region"},
-        "warm_step_us": round(warm_ms * 1e3, 2),
+        "warm_step_us": None if args.skip_extra else round(warm_ms * 1e3, 2),
     }
     if not args.no_cpu_baseline:
         _log("timing the CPU oracle ...")

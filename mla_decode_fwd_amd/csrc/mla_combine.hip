@@ -111,8 +111,8 @@ __global__ __launch_bounds__(64 * kWaves) void combine_kernel(const void* __rest
 }
 
 // Many chunks per sequence (long contexts, small batches): one workgroup per
-// row, its four waves take every fourth chunk, and the four partial sums
-// meet in LDS. Each wave then waits on a quarter of the chunk loads, and the
+// row, its four waves take every fourth chunk (eight per round, the first
+// round issued with the LSE loads), and the four partial sums meet in LDS. Each wave then waits on a quarter of the chunk loads, and the
 // grid has four times the waves of the row-per-wave form. The weights and
 // the summation order of each wave's share are those of the row-per-wave
 // form; only the final four-way sum is added.
@@ -131,7 +131,34 @@ __global__ __launch_bounds__(64 * kWaves) void combine_wide_kernel(const void* _
   const int n = min(min(max(split_offsets[b + 1] - s0, 0), kMaxSplits), total_splits - s0);
   if (n == 0 || (skip_single && n == 1)) return;  // uniform over the workgroup
 
+  // This wave's chunks: wave, wave + 4, ..., eight per round, the first
+  // round requested together with the LSEs.
+  constexpr int kPer = 8;
+  float v[kPer][8];
+  const auto load_round = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = k0 + kWaves * j;
+      if (k < n) {
+        const size_t off = ((size_t)(s0 + k) * rows + row) * kDv + 8 * lane;
+        if (kBf16) {
+          const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(o_part) + off);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] = (float)x[e];
+        } else {
+          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(o_part) + off);
+          const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[j][e] = x0[e]; v[j][4 + e] = x1[e]; }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+      }
+    }
+  };
   const float lk = lane < n ? lse_part[(size_t)(s0 + lane) * rows + row] : -INFINITY;
+  load_round(wave);
   const float M = wave_max(lk);
   const float Mf = (M == -INFINITY) ? 0.f : M;
   const float w = (lane < n) ? expf(lk - Mf) : 0.f;
@@ -139,31 +166,15 @@ __global__ __launch_bounds__(64 * kWaves) void combine_wide_kernel(const void* _
   const float lse_v = (S > 0.f) ? Mf + logf(S) : -INFINITY;
   const float wn = (S > 0.f) ? w / S : 0.f;
 
-  // This wave's chunks: wave, wave + 4, ..., eight per round.
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k0 = wave; k0 < n; k0 += 8 * kWaves) {
-    float v[8][8];
-    float wk[8];
+  for (int k0 = wave; k0 < n; k0 += kPer * kWaves) {
+    if (k0 != wave) load_round(k0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + kWaves * j;
-      wk[j] = (k < n) ? __shfl(wn, k & 63, 64) : 0.f;
-      const size_t off = ((size_t)(s0 + min(k, n - 1)) * rows + row) * kDv + 8 * lane;
-      if (kBf16) {
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(o_part) + off);
+    for (int j = 0; j < kPer; ++j) {
+      const float wk = __shfl(wn, (k0 + kWaves * j) & 63, 64);  // 0 past n
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = (float)x[e];
-      } else {
-        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(o_part) + off);
-        const f32x4_t x0 = src[0], x1 = src[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { v[j][e] = x0[e]; v[j][4 + e] = x1[e]; }
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, v[j][e], acc[e]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk[j], v[j][e], acc[e]);
   }
   if (wave > 0) {
 #pragma unroll

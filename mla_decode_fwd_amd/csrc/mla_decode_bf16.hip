@@ -410,13 +410,20 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
       m_ref = m_new;
     };
     // Two P values of a tile (scores e and e+1), packed into the PV operand:
-    // k-step kk of the tile takes scores 8kk .. 8kk+7.
+    // k-step kk of the tile takes scores 8kk .. 8kk+7. The empty asm uses
+    // anchor the exponentials and the running sum where the call stands:
+    // between the MFMAs they are meant to hide under. Without them the
+    // compiler sinks every one of a tile's exponentials into the block of
+    // the first MFMA that reads them (the next-page load branches split the
+    // unrolled loop into blocks), where they run exposed.
     auto p_pair = [&](const f32x16_t& st, int e, float neg_ref, bf16x8_t* pf, float& psum) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e], sl2, neg_ref));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e + 1], sl2, neg_ref));
+      asm volatile("" ::"v"(p0), "v"(p1));
       pf[e >> 3][e & 7] = (__bf16)p0;
       pf[e >> 3][(e & 7) + 1] = (__bf16)p1;
       psum += p0 + p1;
+      asm volatile("" : "+v"(psum));
     };
     constexpr int kKDepth = 3;
     constexpr int kPvDepth = 4;
@@ -495,17 +502,15 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      const float mt0 = tile_max(st0, 0);
-      move_reference((mt0 > m_ref + 8.0f) ? mt0 : m_ref);
-      const float neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
-
-      // ---- QK(T1), with tile 0's P (two values every four k-steps) and the
-      // other half of the next page's loads.
+      // ---- QK(T1), with tile 0's max and reference move after its second
+      // MFMA, tile 0's P (two values every four k-steps from the fourth) and
+      // the other half of the next page's loads.
       f32x16_t st1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) st1[r] = 0.f;
       bf16x8_t pf0[2];
       float psum0 = 0.f;
+      float neg0 = 0.f;
       {
         bf16x8_t kf[kKDepth];
 #pragma unroll
@@ -515,19 +520,24 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
           const bf16x8_t cur = kf[s % kKDepth];
           if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(1, s + kKDepth);
           st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st1, 0, 0, 0);
-          if ((s & 3) == 0 && s < 32) p_pair(st0, s >> 1, neg0, pf0, psum0);
+          if (s == 1) {
+            const float mt0 = tile_max(st0, 0);
+            move_reference((mt0 > m_ref + 8.0f) ? mt0 : m_ref);
+            neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
+          }
+          if ((s & 3) == 0 && s >= 4) p_pair(st0, (s - 4) >> 1, neg0, pf0, psum0);
           if (has_next && (s & 3) == 2) issue_line(next, 9 + (s >> 2));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       l_loc += psum0;
-      const float mt1 = tile_max(st1, 1);
-      const float m1 = (mt1 > m_ref + 8.0f) ? mt1 : m_ref;  // provisional reference of tile 1
-      const float neg1 = (m1 == -INFINITY) ? 0.f : -m1;
 
-      // ---- PV(T0), with tile 1's P.
+      // ---- PV(T0), with tile 1's max (a provisional reference, applied to O
+      // and l only after PV(T0) has added tile 0) after its second MFMA and
+      // tile 1's P (two values every three MFMAs from the fifth).
       bf16x8_t pf1[2];
       float psum1 = 0.f;
+      float m1 = m_ref, neg1 = 0.f;
       {
         bf16x8_t vf[kPvDepth];
 #pragma unroll
@@ -540,7 +550,12 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
             mfma_pv<true>(acc_o[n & 15], cur, pf0[n >> 4]);  // first use of this P fragment
           else
             mfma_pv<false>(acc_o[n & 15], cur, pf0[n >> 4]);
-          if ((n & 3) == 0) p_pair(st1, n >> 1, neg1, pf1, psum1);
+          if (n == 1) {
+            const float mt1 = tile_max(st1, 1);
+            m1 = (mt1 > m_ref + 8.0f) ? mt1 : m_ref;
+            neg1 = (m1 == -INFINITY) ? 0.f : -m1;
+          }
+          if (n >= 4 && n < 28 && (n - 4) % 3 == 0) p_pair(st1, 2 * ((n - 4) / 3), neg1, pf1, psum1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
