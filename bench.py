@@ -25,10 +25,10 @@ the same phase of the GPU clock; the medians over the second half of 24
 rounds are reported, with the step time measured in the same rounds
 (`interleaved_step_us`), the gap between it and decode + merge
 (`launch_gap_us`). `traffic` (measured HBM bytes per launch) is
-the scaled FETCH_SIZE + WRITE_SIZE reading kept in
-profiles/mla_decode_bf16_b64_ctx4096.md (made by
-mla_decode_fwd_amd.profile_summary from rocprofv3 counter runs of this
-script); it is null when the decode kernel's source no longer has the hash
+the scaled FETCH_SIZE + WRITE_SIZE reading kept in the workload's summary
+under profiles/ (PROFILES below; made by mla_decode_fwd_amd.profile_summary
+from rocprofv3 counter runs of this script); it is null for a workload with
+no summary, and when the decode kernel's source no longer has the hash
 recorded there, i.e. when the kernel changed after the counters were taken.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload on this host's cores.
@@ -76,22 +76,39 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-PROFILE = os.path.join(ROOT, "profiles", "mla_decode_bf16_b64_ctx4096.md")
+_BF16_SOURCES = ("csrc/mla_decode_bf16.hip", "csrc/mla_decode_common.h", "csrc/mla_internal.h")
+_FP8_SOURCES = ("csrc/mla_decode_fp8.hip", "csrc/mla_decode_common.h", "csrc/mla_internal.h")
+# Counter summaries under profiles/ per decode workload: (file, the sources
+# the dominant kernel is built from, whose hash the summary records).
+PROFILES = {
+    "batched": ("mla_decode_bf16_b64_ctx4096.md", _BF16_SOURCES),
+    "long": ("mla_decode_bf16_long_b8_ctx65536.md", _BF16_SOURCES),
+    "mtp": ("mla_decode_bf16_mtp2_b128_ctx4096.md", _BF16_SOURCES),
+    "topk": ("mla_decode_bf16_topk2048_b64.md", _BF16_SOURCES),
+    "fp8": ("mla_decode_fp8_b64_ctx4096.md", _FP8_SOURCES),
+}
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter summary, or None
-    if there is none or the kernel source changed since it was taken."""
+def measured_traffic(workload: str, plan: str = "schedule"):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload, or None if there is none, the summary was taken under another
+    plan, or the kernel source changed since it was taken."""
     from mla_decode_fwd_amd.profile_summary import decode_source_sha256
 
-    if not os.path.exists(PROFILE):
+    if workload not in PROFILES:
+        return None
+    name, sources = PROFILES[workload]
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(PROFILE, encoding="utf-8"):
+    for line in open(path, encoding="utf-8"):
         if ":" in line and not line.startswith(("|", "#", " ")):
             k, _, v = line.partition(":")
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != decode_source_sha256():
+    if fields.get("kernel_source_sha256") != decode_source_sha256(sources):
+        return None
+    if workload in ("batched", "long", "mtp") and plan != "schedule":
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -610,7 +627,7 @@ def main():
         "roofline_frac_kv_only": round(kv_only / (ms_per_step / 1e3) / acc.PEAK_HBM_BYTES_PER_S, 4),
         "roofline": {"bound": dec_rf["bound"], "achieved": round(dec_rf["achieved"], 1),
                      "peak": dec_rf["peak"], "unit": dec_rf["unit"], "frac": round(dec_rf["frac"], 4),
-                     "traffic": measured_traffic() if args.workload == "batched" else None,
+                     "traffic": measured_traffic(args.workload, args.plan),
                      "kernel": ("mla_decode_bf16_kernel<true>" if topk_mode else
                                 "mla_decode_fp8_kernel" if fp8_mode else "mla_decode_bf16_kernel"),
                      "kernel_us": round(decode_ms * 1e3, 2), "combine_us": round(combine_ms * 1e3, 2),

@@ -403,7 +403,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
   for (int r = 0; r < kWaveRows; ++r) {
     if (row0 + r >= rows) break;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * (kDv * 2) + ((ln ^ r) * 16));
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln));
+    u32x4_t* const dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln);
+    if (direct)  // final rows: non-temporal; chunk partials: cacheable, the merge reads them next
+      __builtin_nontemporal_store(v, dst);
+    else
+      *dst = v;
   }
   if (hi32f == 0 && rowf < rows) {
     if (direct)
