@@ -111,10 +111,11 @@ __global__ __launch_bounds__(64 * kWaves) void combine_kernel(const void* __rest
                                                               const float* __restrict__ lse_part,
                                                               const int32_t* __restrict__ split_offsets,
                                                               int rows, int total_splits,
-                                                              int skip_single, void* o_lat, float* lse) {
+                                                              int skip_single, int rows_fast, void* o_lat,
+                                                              float* lse) {
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x;
-  const int row = blockIdx.y * kWaves + (threadIdx.x >> 6);
+  const int b = rows_fast ? blockIdx.y : blockIdx.x;
+  const int row = (rows_fast ? blockIdx.x : blockIdx.y) * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
   // Clamp so that malformed offsets can never index outside the partials.
   const int s0 = min(max(split_offsets[b], 0), total_splits);
@@ -163,12 +164,12 @@ __global__ __launch_bounds__(64 * kWaves) void combine_wide_kernel(const void* _
                                                                    const float* __restrict__ lse_part,
                                                                    const int32_t* __restrict__ split_offsets,
                                                                    int rows, int total_splits, int skip_single,
-                                                                   void* o_lat, float* lse) {
+                                                                   int rows_fast, void* o_lat, float* lse) {
   __shared__ float part[kWaves - 1][kDv];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int b = blockIdx.x;
-  const int row = blockIdx.y;
+  const int b = rows_fast ? blockIdx.y : blockIdx.x;
+  const int row = rows_fast ? blockIdx.x : blockIdx.y;
   const int s0 = min(max(split_offsets[b], 0), total_splits);
   const int n = min(min(max(split_offsets[b + 1] - s0, 0), kMaxSplits), total_splits - s0);
   if (n == 0 || (skip_single && n == 1)) return;  // uniform over the workgroup
@@ -217,24 +218,34 @@ hipError_t launch_combine(const void* o_part, const float* lse_part, const int32
                           int total_splits, int B, int s_q, int H, bool out_bf16, bool skip_single,
                           void* o_lat, float* lse, hipStream_t stream) {
   const int rows = s_q * H;
-  if (total_splits >= 8 * B && rows <= 65535) {
-    // Eight or more chunks per sequence on average: one workgroup per row.
-    const dim3 grid((unsigned)B, (unsigned)rows);
+  // Grid: (row block, sequence), rows fastest. Workgroups are dealt to the
+  // eight XCDs round robin in launch order, so the rows of one sequence
+  // spread over all of them; with the sequence fastest, every row of
+  // sequence b would go to XCD b mod 8, and one long sequence with many
+  // chunks would load a single XCD (measured on MI355X: the merge of eight
+  // sequences of 65536 ... 513 tokens took 9.6 us that way). The sequence
+  // index goes in y while it fits there (B <= 65535), else in x.
+  const bool wide = total_splits >= 8 * B && rows <= 65535;  // >= 8 chunks per sequence on average
+  const unsigned row_blocks = wide ? (unsigned)rows : (unsigned)((rows + kWaves - 1) / kWaves);
+  const bool rows_fast = B <= 65535;
+  const dim3 grid = rows_fast ? dim3(row_blocks, (unsigned)B) : dim3((unsigned)B, row_blocks);
+  const int rf = rows_fast ? 1 : 0, ss = skip_single ? 1 : 0;
+  if (wide) {
+    // One workgroup per row.
     if (out_bf16)
       hipLaunchKernelGGL(combine_wide_kernel<true>, grid, dim3(64 * kWaves), 0, stream, o_part, lse_part,
-                         split_offsets, rows, total_splits, skip_single ? 1 : 0, o_lat, lse);
+                         split_offsets, rows, total_splits, ss, rf, o_lat, lse);
     else
       hipLaunchKernelGGL(combine_wide_kernel<false>, grid, dim3(64 * kWaves), 0, stream, o_part, lse_part,
-                         split_offsets, rows, total_splits, skip_single ? 1 : 0, o_lat, lse);
+                         split_offsets, rows, total_splits, ss, rf, o_lat, lse);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)B, (unsigned)((rows + kWaves - 1) / kWaves));
   if (out_bf16)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(64 * kWaves), 0, stream, o_part, lse_part,
-                       split_offsets, rows, total_splits, skip_single ? 1 : 0, o_lat, lse);
+                       split_offsets, rows, total_splits, ss, rf, o_lat, lse);
   else
     hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(64 * kWaves), 0, stream, o_part, lse_part,
-                       split_offsets, rows, total_splits, skip_single ? 1 : 0, o_lat, lse);
+                       split_offsets, rows, total_splits, ss, rf, o_lat, lse);
   return hipGetLastError();
 }
 
