@@ -142,6 +142,18 @@ __device__ __forceinline__ void store_tile(const f32x16_t& acc, __bf16* orow, in
   }
 }
 
+// acc (as in store_tile) into an LDS row of bf16 outputs: the lane's four
+// 8-byte pieces at columns 8q4 + 4*hi32 of the tile's 32.
+__device__ __forceinline__ void stage_tile(const f32x16_t& acc, char* srow, int hi32) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    bf16x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+    *reinterpret_cast<bf16x4_t*>(srow + 2 * (8 * q4 + 4 * hi32)) = v;
+  }
+}
+
 // absorb_q, W as [H, J, K] (a weight row per output j, k contiguous): grid
 // (H, ceil(J/128)), wave w owns rows jb + 32w .. +31 and walks the tokens 32
 // at a time. Its A fragments are 16-byte loads straight from the weight rows
@@ -204,9 +216,10 @@ constexpr int kAbTokens = 64;             // token rows staged per round
 __global__ __launch_bounds__(256) void absorb_lds_kernel(const __bf16* __restrict__ A, const __bf16* __restrict__ W,
                                                         int N, int H, int J, __bf16* __restrict__ out,
                                                         int out_stride, const __bf16* __restrict__ tail_src,
-                                                        int tail) {
+                                                        int tail, int tail_vec) {
   __shared__ __attribute__((aligned(16))) char sw[128 * kAbStride];
   __shared__ __attribute__((aligned(16))) char sa[kAbTokens * kAbStride];
+  __shared__ __attribute__((aligned(16))) char so[kAbTokens * kAbStride];  // the round's output rows, 128 columns
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -253,11 +266,27 @@ __global__ __launch_bounds__(256) void absorb_lds_kernel(const __bf16* __restric
   }
   const int j0 = jb + 32 * wave;
   const int w_off = (32 * wave + r32) * kAbStride + 16 * hi32;  // A operand: row j0 + r32, k 16s + 8hi32
+  // The RoPE tail of the round's token rows, copied by the first column slab
+  // in 16-byte pieces (tail_vec: tail a multiple of 8, 16-byte aligned rows),
+  // requested before the round's products and stored after them.
+  const int tp = tail_vec ? tail / 8 : 0;  // 16-byte pieces per tail row
+  const bool copy_tail = tail_vec && blockIdx.y == 0;
   for (int n0 = 0; n0 < N; n0 += kAbTokens) {
     if (n0 > 0) {
       bf16x8_t av[kAPieces];
       load_tokens(n0, av);
       store_tokens(av);
+    }
+    constexpr int kTailPer = 4;  // pieces per thread per round: 64 rows x up to 16 pieces
+    bf16x8_t tv[kTailPer];
+    if (copy_tail) {
+#pragma unroll
+      for (int u = 0; u < kTailPer; ++u) {
+        const int idx = u * 256 + tid;
+        const int r = idx / 16, p = idx % 16;
+        if (p < tp && n0 + r < N)
+          tv[u] = *reinterpret_cast<const bf16x8_t*>(tail_src + ((size_t)(n0 + r) * H + h) * tail + 8 * p);
+      }
     }
     __syncthreads();
     if (j0 < J) {
@@ -266,7 +295,6 @@ __global__ __launch_bounds__(256) void absorb_lds_kernel(const __bf16* __restric
       for (int s = 0; s < 8; ++s) wf[s] = *reinterpret_cast<const bf16x8_t*>(sw + w_off + 32 * s);
 #pragma unroll
       for (int t = 0; t < kAbTokens / 32; ++t) {
-        const int n = n0 + 32 * t + r32;
         if (n0 + 32 * t >= N) break;
         f32x16_t acc;
 #pragma unroll
@@ -276,12 +304,33 @@ __global__ __launch_bounds__(256) void absorb_lds_kernel(const __bf16* __restric
           const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sa + (32 * t + r32) * kAbStride + 16 * hi32 + 32 * s);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], b, acc, 0, 0, 0);
         }
-        if (n < N) store_tile(acc, out + ((size_t)n * H + h) * out_stride, j0, hi32, J);
+        stage_tile(acc, so + (32 * t + r32) * kAbStride + 64 * wave, hi32);
+      }
+    }
+    __syncthreads();
+    // The round's output rows leave as whole 16-byte pieces, 256 contiguous
+    // bytes per token row (written from the MFMA layout, each store would
+    // cover 32 rows with 16 bytes each: measured 2.8 us slower at N = 64).
+#pragma unroll
+    for (int u = 0; u < kAbTokens * 16 / 256; ++u) {
+      const int idx = u * 256 + tid;
+      const int r = idx >> 4, p = idx & 15;
+      if (n0 + r < N && jb + 8 * p < J)
+        *reinterpret_cast<bf16x8_t*>(out + ((size_t)(n0 + r) * H + h) * out_stride + jb + 8 * p) =
+            *reinterpret_cast<const bf16x8_t*>(so + r * kAbStride + 16 * p);
+    }
+    if (copy_tail) {
+#pragma unroll
+      for (int u = 0; u < kTailPer; ++u) {
+        const int idx = u * 256 + tid;
+        const int r = idx / 16, p = idx % 16;
+        if (p < tp && n0 + r < N)
+          *reinterpret_cast<bf16x8_t*>(out + ((size_t)(n0 + r) * H + h) * out_stride + J + 8 * p) = tv[u];
       }
     }
     __syncthreads();  // before the next token rows overwrite sa
   }
-  if (tail > 0 && blockIdx.y == 0)
+  if (tail > 0 && !tail_vec && blockIdx.y == 0)
     for (int idx = tid; idx < N * tail; idx += 256) {
       const int n = idx / tail, e = idx - (idx / tail) * tail;
       out[((size_t)n * H + h) * out_stride + J + e] = tail_src[((size_t)n * H + h) * tail + e];
@@ -301,12 +350,14 @@ __global__ __launch_bounds__(256) void absorb_lds_kernel(const __bf16* __restric
 constexpr int kUvRows = 512;    // weight rows (contracted k) one workgroup stages
 constexpr int kUvTokens = 64;   // token rows staged per round
 constexpr int kUvAStride = kUvRows * 2 + 16;  // 1040
+constexpr int kUvOStride = 64 * 2 + 16;       // 144: a staged output row
 
 __global__ __launch_bounds__(256) void out_uv_mfma_kernel(const __bf16* __restrict__ A, const __bf16* __restrict__ W,
                                                          int N, int H, int K, int J, __bf16* __restrict__ out,
                                                          int out_stride) {
-  __shared__ __attribute__((aligned(16))) char smem[kUvRows * 128 + kUvTokens * kUvAStride];
+  __shared__ __attribute__((aligned(16))) char smem[kUvRows * 128 + kUvTokens * kUvAStride + kUvTokens * kUvOStride];
   char* const sa = smem + kUvRows * 128;
+  char* const so = sa + kUvTokens * kUvAStride;  // the round's output rows, 64 columns
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -379,7 +430,6 @@ __global__ __launch_bounds__(256) void out_uv_mfma_kernel(const __bf16* __restri
     const int n_tiles = min(N - n0 + 31, kUvTokens) / 32;
     for (int t = wave; t < 2 * n_tiles; t += 4) {
       const int c = t & 1, nt = t >> 1;
-      const int n = n0 + 32 * nt + r32;
       const int tr_off = 128 * row_in + 64 * (c ^ ((jj >> 1) & 1)) + col_b;
       const char* const bsrc = sa + (32 * nt + r32) * kUvAStride + 16 * hi32;  // B operand: token n, k 16s + 8hi32
       f32x16_t acc;
@@ -397,17 +447,28 @@ __global__ __launch_bounds__(256) void out_uv_mfma_kernel(const __bf16* __restri
         const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(bsrc + 32 * s4);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
-      if (n < N) store_tile(acc, out + ((size_t)n * H + h) * out_stride, jb + 32 * c, hi32, J);
+      stage_tile(acc, so + (32 * nt + r32) * kUvOStride + 64 * c, hi32);
     }
-    __syncthreads();  // before the next token rows overwrite sa
+    __syncthreads();
+    // Whole 16-byte pieces, 128 contiguous bytes per token row.
+#pragma unroll
+    for (int u = 0; u < kUvTokens * 8 / 256; ++u) {
+      const int idx = u * 256 + tid;
+      const int r = idx >> 3, p = idx & 7;
+      if (n0 + r < N && jb + 8 * p < J)
+        *reinterpret_cast<bf16x8_t*>(out + ((size_t)(n0 + r) * H + h) * out_stride + jb + 8 * p) =
+            *reinterpret_cast<const bf16x8_t*>(so + r * kUvOStride + 16 * p);
+    }
+    __syncthreads();  // before the next token rows overwrite sa and so
   }
 }
 
-// The MFMA form needs 16-byte aligned rows: K a multiple of 16, J and the
-// output row a multiple of 4 (8-byte stores), 16-byte aligned bases.
+// The MFMA forms need 16-byte aligned rows: K a multiple of 16, J and the
+// output row a multiple of 8 (whole 16-byte output pieces), 16-byte aligned
+// bases.
 bool mfma_shape(const void* A, const void* W, const void* out, int K, int J, int out_stride) {
-  return K % 16 == 0 && J % 8 == 0 && out_stride % 4 == 0 && ((uintptr_t)A % 16) == 0 && ((uintptr_t)W % 16) == 0 &&
-         ((uintptr_t)out % 8) == 0;
+  return K % 16 == 0 && J % 8 == 0 && out_stride % 8 == 0 && ((uintptr_t)A % 16) == 0 && ((uintptr_t)W % 16) == 0 &&
+         ((uintptr_t)out % 16) == 0;
 }
 
 }  // namespace
@@ -416,9 +477,12 @@ hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w
                            int dn, int dr, int dc, bool bf16, void* q_lat, hipStream_t stream) {
   if (bf16 && mfma_shape(q_nope, w_uk, q_lat, dn, dc, dc + dr) && dn == kAbK) {
     const dim3 grid((unsigned)H, (unsigned)((dc + 127) / 128));
+    // 16-byte tail pieces: whole pieces per row (at most 16), 16-byte aligned bases and row starts.
+    const int tail_vec = dr > 0 && dr % 8 == 0 && dr <= 128 && dc % 8 == 0 && (dc + dr) % 8 == 0 &&
+                         ((uintptr_t)q_rope % 16) == 0 && ((uintptr_t)q_lat % 16) == 0;
     hipLaunchKernelGGL(absorb_lds_kernel, grid, dim3(256), 0, stream, static_cast<const __bf16*>(q_nope),
                        static_cast<const __bf16*>(w_uk), N, H, dc, static_cast<__bf16*>(q_lat), dc + dr,
-                       static_cast<const __bf16*>(q_rope), dr);
+                       static_cast<const __bf16*>(q_rope), dr, tail_vec);
     return hipGetLastError();
   }
   if (bf16 && mfma_shape(q_nope, w_uk, q_lat, dn, dc, dc + dr)) {

@@ -186,7 +186,8 @@ template <int kK>
 __global__ __launch_bounds__(256) void bmm_lds_kernel(const __bf16* __restrict__ X, const float* __restrict__ partials,
                                                      int n_parts, const uint8_t* __restrict__ W, float w_scale, int N,
                                                      int H, int K_arg, int J, int JS_arg, __bf16* __restrict__ out,
-                                                     int out_stride, const __bf16* __restrict__ tail_src, int tail) {
+                                                     int out_stride, const __bf16* __restrict__ tail_src, int tail,
+                                                     int vec_out) {
   const int K = kK ? kK : K_arg;
   const int JS = kK ? (kK <= 256 ? 128 : 64) : JS_arg;
   __shared__ float red[4];
@@ -261,15 +262,38 @@ __global__ __launch_bounds__(256) void bmm_lds_kernel(const __bf16* __restrict__
   }
   const float sc = (1.f / r) * w_scale;
   const int row_tiles = JS / 32;
+  // vec_out (J, the output row and the base 16-byte multiples, the tail a
+  // multiple of 8 of at most 128): a round's outputs are staged in sx once
+  // its products are done and leave as whole 16-byte pieces of contiguous
+  // row segments, and the RoPE tail moves in 16-byte pieces too; otherwise
+  // each lane stores its 8-byte pieces directly.
+  const int SO = 2 * JS + 16;  // staged output row stride, bytes (<= 272: fits in sx)
+  const bool copy_tail = vec_out && tail > 0 && blockIdx.y == 0;
+  const int tp = tail / 8;
   for (int n0 = 0; n0 < N; n0 += kF8Tokens) {
     if (n0 > 0) {
       bf16x8_t xv[16];
       load_tokens(n0, xv);
       store_tokens(xv);
     }
+    constexpr int kTailPer = 4;  // 64 rows x up to 16 pieces
+    bf16x8_t tv[kTailPer];
+    if (copy_tail) {
+#pragma unroll
+      for (int u = 0; u < kTailPer; ++u) {
+        const int idx = u * 256 + tid;
+        const int rr = idx / 16, p = idx % 16;
+        if (p < tp && n0 + rr < N)
+          tv[u] = *reinterpret_cast<const bf16x8_t*>(tail_src + ((size_t)(n0 + rr) * H + h) * tail + 8 * p);
+      }
+    }
     __syncthreads();
     const int n_tiles = min(N - n0 + 31, kF8Tokens) / 32;
-    for (int t = wave; t < row_tiles * n_tiles; t += 4) {
+    f32x16_t outs[2];  // vec_out: this wave's tiles (at most 4 x 2 / 4 per round)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = wave + 4 * i;
+      if (t >= row_tiles * n_tiles) break;
       const int rt = t % row_tiles, nt = t / row_tiles;
       const int j0 = jb + 32 * rt;
       const int n = n0 + 32 * nt + r32;
@@ -283,7 +307,9 @@ __global__ __launch_bounds__(256) void bmm_lds_kernel(const __bf16* __restrict__
       for (int k = 0; k < K; k += 16)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(*reinterpret_cast<const long*>(wa + k),
                                                          *reinterpret_cast<const long*>(xa + k), acc, 0, 0, 0);
-      if (n < N) {
+      if (vec_out) {
+        outs[i] = acc;  // staged after every wave has read sx
+      } else if (n < N) {
         __bf16* orow = out + ((size_t)n * H + h) * out_stride;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -301,9 +327,46 @@ __global__ __launch_bounds__(256) void bmm_lds_kernel(const __bf16* __restrict__
         }
       }
     }
+    if (vec_out) {
+      __syncthreads();  // every wave has read its token rows: sx takes the outputs
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = wave + 4 * i;
+        if (t >= row_tiles * n_tiles) break;
+        const int rt = t % row_tiles, nt = t / row_tiles;
+        if (jb + 32 * rt >= J) continue;
+        char* const srow = sx + (32 * nt + r32) * SO + 64 * rt;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(outs[i][4 * q4 + e] * sc);
+          *reinterpret_cast<bf16x4_t*>(srow + 2 * (8 * q4 + 4 * hi32)) = v;
+        }
+      }
+      __syncthreads();
+      const int pieces = JS / 8;  // 16-byte pieces per staged row
+#pragma unroll
+      for (int u = 0; u < kF8Tokens * 16 / 256; ++u) {
+        const int idx = u * 256 + tid;
+        const int rr = idx / 16, p = idx % 16;
+        if (p < pieces && n0 + rr < N && jb + 8 * p < J)
+          *reinterpret_cast<bf16x8_t*>(out + ((size_t)(n0 + rr) * H + h) * out_stride + jb + 8 * p) =
+              *reinterpret_cast<const bf16x8_t*>(sx + rr * SO + 16 * p);
+      }
+      if (copy_tail) {
+#pragma unroll
+        for (int u = 0; u < kTailPer; ++u) {
+          const int idx = u * 256 + tid;
+          const int rr = idx / 16, p = idx % 16;
+          if (p < tp && n0 + rr < N)
+            *reinterpret_cast<bf16x8_t*>(out + ((size_t)(n0 + rr) * H + h) * out_stride + J + 8 * p) = tv[u];
+        }
+      }
+    }
     __syncthreads();  // before the next token rows overwrite sx
   }
-  if (tail > 0 && blockIdx.y == 0)
+  if (tail > 0 && !vec_out && blockIdx.y == 0)
     for (int idx = tid; idx < N * tail; idx += 256) {
       const int n = idx / tail, e = idx - (idx / tail) * tail;
       out[((size_t)n * H + h) * out_stride + J + e] = tail_src[((size_t)n * H + h) * tail + e];
@@ -344,8 +407,11 @@ hipError_t launch_bmm_fp8(const void* X, float* partials, const uint8_t* W, floa
     const int JS = K <= 256 ? 128 : 64;
     const dim3 grid((unsigned)H, (unsigned)((J + JS - 1) / JS));
     auto kern = K == 128 ? bmm_lds_kernel<128> : K == 512 ? bmm_lds_kernel<512> : bmm_lds_kernel<0>;
+    const int vec_out = J % 8 == 0 && out_stride % 8 == 0 && ((uintptr_t)out % 16) == 0 && tail % 8 == 0 &&
+                        tail <= 128 && (tail == 0 || ((uintptr_t)tail_src % 16) == 0);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, static_cast<const __bf16*>(X), partials, parts, W, w_scale, N,
-                       H, K, J, JS, static_cast<__bf16*>(out), out_stride, static_cast<const __bf16*>(tail_src), tail);
+                       H, K, J, JS, static_cast<__bf16*>(out), out_stride, static_cast<const __bf16*>(tail_src), tail,
+                       vec_out);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((J + 127) / 128), (unsigned)((N + 31) / 32), (unsigned)H);

@@ -378,14 +378,17 @@ def test_absorb_q_and_out_uv_deepseek_shape(dtype):
 
 
 @pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(5, 3, 48, 8, 40, 24), (33, 2, 16, 4, 136, 200), (7, 4, 24, 4, 12, 20),
-                                            (70, 3, 128, 64, 208, 72), (130, 2, 128, 64, 512, 128)])
+                                            (70, 3, 128, 64, 208, 72), (130, 2, 128, 64, 512, 128),
+                                            (9, 2, 128, 136, 64, 24), (21, 2, 128, 4, 60, 24)])
 def test_absorb_q_and_out_uv_bf16_odd_shapes(N, H, dn, dr, dc, dv):
     # Partial column blocks, a partial last k slice, and (third case) shapes
     # the MFMA form does not take, which run through the general kernel. The
-    # last two take the staged d_nope = 128 absorption with a partial weight
+    # next two take the staged d_nope = 128 absorption with a partial weight
     # slab and partial token rounds, and the staged out_uv with partial
     # column slabs, a k count that is not a multiple of 128 and three token
-    # tiles spread over the waves.
+    # tiles spread over the waves. The sixth has a RoPE tail too long for the
+    # staged absorption's 16-byte tail copy (its element-wise copy runs); the
+    # last has output rows that are not 16-byte multiples (general kernel).
     rng = np.random.default_rng(42 + N)
     q_n = torch.from_numpy(rng.standard_normal((N, H, dn), dtype=np.float32)).to(torch.bfloat16)
     q_r = torch.from_numpy(rng.standard_normal((N, H, dr), dtype=np.float32)).to(torch.bfloat16)
@@ -395,6 +398,7 @@ def test_absorb_q_and_out_uv_bf16_odd_shapes(N, H, dn, dr, dc, dv):
     ql = mla.mla_absorb_q(q_n.cuda(), q_r.cuda(), w_uk.cuda())
     ou = mla.mla_out_uv(o_lat.cuda(), w_uv.cuda())
     torch.cuda.synchronize()
+    assert torch.equal(ql[..., dc:].cpu(), q_r)  # the RoPE tail is copied unchanged
     for got, ref, name in [(ql[..., :dc], orc.absorb_q(to_np(q_n), to_np(q_r), to_np(w_uk))[..., :dc], "absorb_q"),
                            (ou, orc.out_uv(to_np(o_lat), to_np(w_uv)), "out_uv")]:
         g = to_np(got)
@@ -687,11 +691,14 @@ def _fp8_compare(got, ref, label):
     assert np.all(np.isfinite(g)) and rel <= 5e-3 and mabs <= 2e-2 * max(1.0, np.max(np.abs(ref))), (label, rel, mabs)
 
 
-@pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(37, 3, 48, 8, 208, 72), (9, 2, 128, 64, 640, 40)])
+@pytest.mark.parametrize("N,H,dn,dr,dc,dv", [(37, 3, 48, 8, 208, 72), (9, 2, 128, 64, 640, 40),
+                                            (70, 2, 128, 4, 144, 20)])
 def test_fp8_products_odd_shapes(N, H, dn, dr, dc, dv):
     # A contracted length other than the staged forms' fixed 128 / 512
-    # (generic staging), partial weight slabs, and (second case) a contracted
-    # length past 512, which takes the direct-load kernel.
+    # (generic staging), partial weight slabs, (second case) a contracted
+    # length past 512, which takes the direct-load kernel, and (third) a RoPE
+    # tail and output rows that are not 16-byte multiples, which the staged
+    # kernel stores piece by piece from the MFMA layout, over two token rounds.
     from mla_inputs import fp8_bmm_case
     c = fp8_bmm_case(N, H=H, d_nope=dn, d_rope=dr, d_c=dc, d_v=dv, seed=180 + N)
     q_lat = mla.mla_absorb_q_fp8(c["q_nope"].cuda(), c["q_rope"].cuda(), c["w_uk_codes"].cuda(), c["w_uk_scale"])
