@@ -118,6 +118,46 @@ __device__ __forceinline__ void issue_page(const PageLoad& p) {
   for (int n = 0; n < kBlocksPerWave; ++n) issue_line(p, n);
 }
 
+// The query rows of a workgroup go to the MFMA operand registers through
+// LDS. Loaded straight into the B layout of v_mfma_f32_32x32x16_bf16 (lane
+// l: 16 bytes of row l&31), each of the 36 load instructions of a wave would
+// touch 32 rows with 32 bytes each, and the address unit spends ~3 us per
+// workgroup on them (measured on MI355X: the first page of a chunk landed
+// 8.2 us after the chunk began, 5.0 us with a quarter of those loads).
+// Direct loads instead fill LDS in 1 KB runs of contiguous row bytes, and
+// each wave then reads its operands with one 16-byte LDS read per k-step.
+// Rows sit at a stride of their length + 16 bytes, so the 16 rows of a read
+// pass start on 16 different 4-bank groups. A 128-row group stages dims
+// 0..287 and then 288..575 of every row (two rounds of 74 KB; the first
+// overlaps the first page's load); a 64-row group stages whole rows in one
+// round (73 KB). The staging area is the second page buffer, extended by
+// kQStageExtra bytes. (Loading half of the rows' dims directly instead of a
+// second round was measured slower: its address work delays the page.)
+constexpr int kQStageExtra = 2048;
+
+// Round `round` of the staged query rows: `nrows` rows of `cols` bytes from
+// column byte `col0`, row R at R * (cols + 16) bytes of the area. Instruction
+// i of the round fills area bytes 1024i .. 1024i + 1023; the waves take
+// instructions w, w + 4, ... Lanes that fall on a row's padding load the
+// row's first piece (never read).
+__device__ __forceinline__ void issue_q_round(const char* q_seq, int rows, int row_base, int nrows, int cols,
+                                              int col0, char* area, int wave, int lane) {
+  const int stride = cols + 16;
+  const int n_inst = nrows * stride / 1024;
+  const uint64_t gp = (uint64_t)(uintptr_t)q_seq;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gp);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(gp >> 32));
+  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)area);
+  for (int i = wave; i < n_inst; i += kWaves) {
+    const int byte = 1024 * i + 16 * lane;
+    const int R = byte / stride, off = byte - R * stride;
+    const int row = min(row_base + R, rows - 1);
+    dma_line_cached(sbase, row * (kDqk * 2) + col0 + (off < cols ? off : 0), lds0 + 1024 * i);
+  }
+}
+
 // Top-k decode: a "page" is 64 listed tokens whose rows sit anywhere in the
 // pool, so each lane carries its own two source addresses (the rows of its
 // two tokens, at its chunk) and the load takes a 64-bit VGPR address. The
@@ -250,10 +290,16 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
   // (the B layout of v_mfma_f32_32x32x16_bf16: lane l holds k = 8(l>>5) .. +8
   // of column l&31).
   bf16x8_t qf[kQSteps];
-  {
+  if constexpr (kSparse) {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(q_base) + ((size_t)b * rows + row_c) * kDqk + 8 * hi32;
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
+  } else {
+    // Staged (issue_q_round): the first round goes out now, ahead of the
+    // first page, and is read once it has landed; the page keeps loading.
+    const char* const q_seq = q_base + (size_t)b * rows * (kDqk * 2);
+    constexpr int kRound = kHalf ? 2 * kDqk : kDqk;  // bytes per row per round
+    issue_q_round(q_seq, rows, rgrp * kGroupRows, kGroupRows, kRound, 0, smem + kPageBytes, wave, lane);
   }
 
   int phys_ahead = 0;
@@ -273,10 +319,39 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
     }
     __syncthreads();
     if (pg0 < pg1) issue_page(make_gather_load(cache, s_ids, smem, wave, lane));
-  } else if (pg0 < pg1) {
-    const int phys = min(max(bt0, 0), last_phys);
-    issue_page(make_page_load(cache + (size_t)phys * kPageBytes, smem, wave, lane));
-    phys_ahead = bt1;
+  } else {
+    if (pg0 < pg1) {
+      const int phys = min(max(bt0, 0), last_phys);
+      issue_page(make_page_load(cache + (size_t)phys * kPageBytes, smem, wave, lane));
+      phys_ahead = bt1;
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(kBlocksPerWave));  // the query round, not the page
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    __syncthreads();
+    const char* const area = smem + kPageBytes;
+    const int R = slice * kWaveRows + r32;  // this lane's row in the staged group
+    if constexpr (kHalf) {
+      const char* const src = area + R * (2 * kDqk + 16) + 16 * hi32;
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(src + 32 * s);
+    } else {
+      const char* const src = area + R * (kDqk + 16) + 16 * hi32;
+#pragma unroll
+      for (int s = 0; s < kQSteps / 2; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(src + 32 * s);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __syncthreads();  // every wave has its first half: the area takes the second
+      const char* const q_seq = q_base + (size_t)b * rows * (kDqk * 2);
+      issue_q_round(q_seq, rows, rgrp * kGroupRows, kGroupRows, kDqk, kDqk, smem + kPageBytes, wave, lane);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+#pragma unroll
+      for (int s = kQSteps / 2; s < kQSteps; ++s)
+        qf[s] = *reinterpret_cast<const bf16x8_t*>(src + 32 * (s - kQSteps / 2));
+    }
+    // The next page's loads overwrite the area: every read must be done
+    // before the page loop's first barrier.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 
   f32x16_t acc_o[kColTiles];
@@ -745,7 +820,7 @@ __device__ __forceinline__ void load_chunk_desc(const int32_t* desc, int c, int&
 template <bool kSparse, bool kHalf>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a, int row_groups, int n_units) {
   constexpr int kSparseBytes = kSparse ? kSparseMaxTopk * 4 + (kSparseMaxTopk / kPage) * 8 : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + kSparseBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + (kSparse ? kSparseBytes : kQStageExtra)];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it in an SGPR
 
