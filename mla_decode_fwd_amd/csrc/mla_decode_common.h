@@ -110,782 +110,39 @@ __device__ __forceinline__ void agpr_fence() {
 // no VALU use of the accumulators is visible to the register allocator
 // (which would otherwise stage all of O through VGPRs and spill). Trailing
 // wait states cover the AGPR write -> MFMA srcC hazard.
+// Four AGPRs a(n) .. a(n+3) scaled through the four temporaries.
+#define MLA_SCALE4(n0, n1, n2, n3)                                                        \
+  "v_accvgpr_read_b32 %0, a" #n0 "\n\tv_accvgpr_read_b32 %1, a" #n1 "\n\t"              \
+  "v_accvgpr_read_b32 %2, a" #n2 "\n\tv_accvgpr_read_b32 %3, a" #n3 "\n\t"              \
+  "v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\t"                                    \
+  "v_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\t"                                    \
+  "v_accvgpr_write_b32 a" #n0 ", %0\n\tv_accvgpr_write_b32 a" #n1 ", %1\n\t"            \
+  "v_accvgpr_write_b32 a" #n2 ", %2\n\tv_accvgpr_write_b32 a" #n3 ", %3\n\t"
 __device__ __forceinline__ void scale_accumulators(float alpha) {
   float t0, t1, t2, t3;
   asm volatile(
-      "v_accvgpr_read_b32 %0, a0\n\t"
-      "v_accvgpr_read_b32 %1, a1\n\t"
-      "v_accvgpr_read_b32 %2, a2\n\t"
-      "v_accvgpr_read_b32 %3, a3\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a0, %0\n\t"
-      "v_accvgpr_write_b32 a1, %1\n\t"
-      "v_accvgpr_write_b32 a2, %2\n\t"
-      "v_accvgpr_write_b32 a3, %3\n\t"
-      "v_accvgpr_read_b32 %0, a4\n\t"
-      "v_accvgpr_read_b32 %1, a5\n\t"
-      "v_accvgpr_read_b32 %2, a6\n\t"
-      "v_accvgpr_read_b32 %3, a7\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a4, %0\n\t"
-      "v_accvgpr_write_b32 a5, %1\n\t"
-      "v_accvgpr_write_b32 a6, %2\n\t"
-      "v_accvgpr_write_b32 a7, %3\n\t"
-      "v_accvgpr_read_b32 %0, a8\n\t"
-      "v_accvgpr_read_b32 %1, a9\n\t"
-      "v_accvgpr_read_b32 %2, a10\n\t"
-      "v_accvgpr_read_b32 %3, a11\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a8, %0\n\t"
-      "v_accvgpr_write_b32 a9, %1\n\t"
-      "v_accvgpr_write_b32 a10, %2\n\t"
-      "v_accvgpr_write_b32 a11, %3\n\t"
-      "v_accvgpr_read_b32 %0, a12\n\t"
-      "v_accvgpr_read_b32 %1, a13\n\t"
-      "v_accvgpr_read_b32 %2, a14\n\t"
-      "v_accvgpr_read_b32 %3, a15\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a12, %0\n\t"
-      "v_accvgpr_write_b32 a13, %1\n\t"
-      "v_accvgpr_write_b32 a14, %2\n\t"
-      "v_accvgpr_write_b32 a15, %3\n\t"
-      "v_accvgpr_read_b32 %0, a16\n\t"
-      "v_accvgpr_read_b32 %1, a17\n\t"
-      "v_accvgpr_read_b32 %2, a18\n\t"
-      "v_accvgpr_read_b32 %3, a19\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a16, %0\n\t"
-      "v_accvgpr_write_b32 a17, %1\n\t"
-      "v_accvgpr_write_b32 a18, %2\n\t"
-      "v_accvgpr_write_b32 a19, %3\n\t"
-      "v_accvgpr_read_b32 %0, a20\n\t"
-      "v_accvgpr_read_b32 %1, a21\n\t"
-      "v_accvgpr_read_b32 %2, a22\n\t"
-      "v_accvgpr_read_b32 %3, a23\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a20, %0\n\t"
-      "v_accvgpr_write_b32 a21, %1\n\t"
-      "v_accvgpr_write_b32 a22, %2\n\t"
-      "v_accvgpr_write_b32 a23, %3\n\t"
-      "v_accvgpr_read_b32 %0, a24\n\t"
-      "v_accvgpr_read_b32 %1, a25\n\t"
-      "v_accvgpr_read_b32 %2, a26\n\t"
-      "v_accvgpr_read_b32 %3, a27\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a24, %0\n\t"
-      "v_accvgpr_write_b32 a25, %1\n\t"
-      "v_accvgpr_write_b32 a26, %2\n\t"
-      "v_accvgpr_write_b32 a27, %3\n\t"
-      "v_accvgpr_read_b32 %0, a28\n\t"
-      "v_accvgpr_read_b32 %1, a29\n\t"
-      "v_accvgpr_read_b32 %2, a30\n\t"
-      "v_accvgpr_read_b32 %3, a31\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a28, %0\n\t"
-      "v_accvgpr_write_b32 a29, %1\n\t"
-      "v_accvgpr_write_b32 a30, %2\n\t"
-      "v_accvgpr_write_b32 a31, %3\n\t"
-      "v_accvgpr_read_b32 %0, a32\n\t"
-      "v_accvgpr_read_b32 %1, a33\n\t"
-      "v_accvgpr_read_b32 %2, a34\n\t"
-      "v_accvgpr_read_b32 %3, a35\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a32, %0\n\t"
-      "v_accvgpr_write_b32 a33, %1\n\t"
-      "v_accvgpr_write_b32 a34, %2\n\t"
-      "v_accvgpr_write_b32 a35, %3\n\t"
-      "v_accvgpr_read_b32 %0, a36\n\t"
-      "v_accvgpr_read_b32 %1, a37\n\t"
-      "v_accvgpr_read_b32 %2, a38\n\t"
-      "v_accvgpr_read_b32 %3, a39\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a36, %0\n\t"
-      "v_accvgpr_write_b32 a37, %1\n\t"
-      "v_accvgpr_write_b32 a38, %2\n\t"
-      "v_accvgpr_write_b32 a39, %3\n\t"
-      "v_accvgpr_read_b32 %0, a40\n\t"
-      "v_accvgpr_read_b32 %1, a41\n\t"
-      "v_accvgpr_read_b32 %2, a42\n\t"
-      "v_accvgpr_read_b32 %3, a43\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a40, %0\n\t"
-      "v_accvgpr_write_b32 a41, %1\n\t"
-      "v_accvgpr_write_b32 a42, %2\n\t"
-      "v_accvgpr_write_b32 a43, %3\n\t"
-      "v_accvgpr_read_b32 %0, a44\n\t"
-      "v_accvgpr_read_b32 %1, a45\n\t"
-      "v_accvgpr_read_b32 %2, a46\n\t"
-      "v_accvgpr_read_b32 %3, a47\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a44, %0\n\t"
-      "v_accvgpr_write_b32 a45, %1\n\t"
-      "v_accvgpr_write_b32 a46, %2\n\t"
-      "v_accvgpr_write_b32 a47, %3\n\t"
-      "v_accvgpr_read_b32 %0, a48\n\t"
-      "v_accvgpr_read_b32 %1, a49\n\t"
-      "v_accvgpr_read_b32 %2, a50\n\t"
-      "v_accvgpr_read_b32 %3, a51\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a48, %0\n\t"
-      "v_accvgpr_write_b32 a49, %1\n\t"
-      "v_accvgpr_write_b32 a50, %2\n\t"
-      "v_accvgpr_write_b32 a51, %3\n\t"
-      "v_accvgpr_read_b32 %0, a52\n\t"
-      "v_accvgpr_read_b32 %1, a53\n\t"
-      "v_accvgpr_read_b32 %2, a54\n\t"
-      "v_accvgpr_read_b32 %3, a55\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a52, %0\n\t"
-      "v_accvgpr_write_b32 a53, %1\n\t"
-      "v_accvgpr_write_b32 a54, %2\n\t"
-      "v_accvgpr_write_b32 a55, %3\n\t"
-      "v_accvgpr_read_b32 %0, a56\n\t"
-      "v_accvgpr_read_b32 %1, a57\n\t"
-      "v_accvgpr_read_b32 %2, a58\n\t"
-      "v_accvgpr_read_b32 %3, a59\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a56, %0\n\t"
-      "v_accvgpr_write_b32 a57, %1\n\t"
-      "v_accvgpr_write_b32 a58, %2\n\t"
-      "v_accvgpr_write_b32 a59, %3\n\t"
-      "v_accvgpr_read_b32 %0, a60\n\t"
-      "v_accvgpr_read_b32 %1, a61\n\t"
-      "v_accvgpr_read_b32 %2, a62\n\t"
-      "v_accvgpr_read_b32 %3, a63\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a60, %0\n\t"
-      "v_accvgpr_write_b32 a61, %1\n\t"
-      "v_accvgpr_write_b32 a62, %2\n\t"
-      "v_accvgpr_write_b32 a63, %3\n\t"
-      "v_accvgpr_read_b32 %0, a64\n\t"
-      "v_accvgpr_read_b32 %1, a65\n\t"
-      "v_accvgpr_read_b32 %2, a66\n\t"
-      "v_accvgpr_read_b32 %3, a67\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a64, %0\n\t"
-      "v_accvgpr_write_b32 a65, %1\n\t"
-      "v_accvgpr_write_b32 a66, %2\n\t"
-      "v_accvgpr_write_b32 a67, %3\n\t"
-      "v_accvgpr_read_b32 %0, a68\n\t"
-      "v_accvgpr_read_b32 %1, a69\n\t"
-      "v_accvgpr_read_b32 %2, a70\n\t"
-      "v_accvgpr_read_b32 %3, a71\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a68, %0\n\t"
-      "v_accvgpr_write_b32 a69, %1\n\t"
-      "v_accvgpr_write_b32 a70, %2\n\t"
-      "v_accvgpr_write_b32 a71, %3\n\t"
-      "v_accvgpr_read_b32 %0, a72\n\t"
-      "v_accvgpr_read_b32 %1, a73\n\t"
-      "v_accvgpr_read_b32 %2, a74\n\t"
-      "v_accvgpr_read_b32 %3, a75\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a72, %0\n\t"
-      "v_accvgpr_write_b32 a73, %1\n\t"
-      "v_accvgpr_write_b32 a74, %2\n\t"
-      "v_accvgpr_write_b32 a75, %3\n\t"
-      "v_accvgpr_read_b32 %0, a76\n\t"
-      "v_accvgpr_read_b32 %1, a77\n\t"
-      "v_accvgpr_read_b32 %2, a78\n\t"
-      "v_accvgpr_read_b32 %3, a79\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a76, %0\n\t"
-      "v_accvgpr_write_b32 a77, %1\n\t"
-      "v_accvgpr_write_b32 a78, %2\n\t"
-      "v_accvgpr_write_b32 a79, %3\n\t"
-      "v_accvgpr_read_b32 %0, a80\n\t"
-      "v_accvgpr_read_b32 %1, a81\n\t"
-      "v_accvgpr_read_b32 %2, a82\n\t"
-      "v_accvgpr_read_b32 %3, a83\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a80, %0\n\t"
-      "v_accvgpr_write_b32 a81, %1\n\t"
-      "v_accvgpr_write_b32 a82, %2\n\t"
-      "v_accvgpr_write_b32 a83, %3\n\t"
-      "v_accvgpr_read_b32 %0, a84\n\t"
-      "v_accvgpr_read_b32 %1, a85\n\t"
-      "v_accvgpr_read_b32 %2, a86\n\t"
-      "v_accvgpr_read_b32 %3, a87\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a84, %0\n\t"
-      "v_accvgpr_write_b32 a85, %1\n\t"
-      "v_accvgpr_write_b32 a86, %2\n\t"
-      "v_accvgpr_write_b32 a87, %3\n\t"
-      "v_accvgpr_read_b32 %0, a88\n\t"
-      "v_accvgpr_read_b32 %1, a89\n\t"
-      "v_accvgpr_read_b32 %2, a90\n\t"
-      "v_accvgpr_read_b32 %3, a91\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a88, %0\n\t"
-      "v_accvgpr_write_b32 a89, %1\n\t"
-      "v_accvgpr_write_b32 a90, %2\n\t"
-      "v_accvgpr_write_b32 a91, %3\n\t"
-      "v_accvgpr_read_b32 %0, a92\n\t"
-      "v_accvgpr_read_b32 %1, a93\n\t"
-      "v_accvgpr_read_b32 %2, a94\n\t"
-      "v_accvgpr_read_b32 %3, a95\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a92, %0\n\t"
-      "v_accvgpr_write_b32 a93, %1\n\t"
-      "v_accvgpr_write_b32 a94, %2\n\t"
-      "v_accvgpr_write_b32 a95, %3\n\t"
-      "v_accvgpr_read_b32 %0, a96\n\t"
-      "v_accvgpr_read_b32 %1, a97\n\t"
-      "v_accvgpr_read_b32 %2, a98\n\t"
-      "v_accvgpr_read_b32 %3, a99\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a96, %0\n\t"
-      "v_accvgpr_write_b32 a97, %1\n\t"
-      "v_accvgpr_write_b32 a98, %2\n\t"
-      "v_accvgpr_write_b32 a99, %3\n\t"
-      "v_accvgpr_read_b32 %0, a100\n\t"
-      "v_accvgpr_read_b32 %1, a101\n\t"
-      "v_accvgpr_read_b32 %2, a102\n\t"
-      "v_accvgpr_read_b32 %3, a103\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a100, %0\n\t"
-      "v_accvgpr_write_b32 a101, %1\n\t"
-      "v_accvgpr_write_b32 a102, %2\n\t"
-      "v_accvgpr_write_b32 a103, %3\n\t"
-      "v_accvgpr_read_b32 %0, a104\n\t"
-      "v_accvgpr_read_b32 %1, a105\n\t"
-      "v_accvgpr_read_b32 %2, a106\n\t"
-      "v_accvgpr_read_b32 %3, a107\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a104, %0\n\t"
-      "v_accvgpr_write_b32 a105, %1\n\t"
-      "v_accvgpr_write_b32 a106, %2\n\t"
-      "v_accvgpr_write_b32 a107, %3\n\t"
-      "v_accvgpr_read_b32 %0, a108\n\t"
-      "v_accvgpr_read_b32 %1, a109\n\t"
-      "v_accvgpr_read_b32 %2, a110\n\t"
-      "v_accvgpr_read_b32 %3, a111\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a108, %0\n\t"
-      "v_accvgpr_write_b32 a109, %1\n\t"
-      "v_accvgpr_write_b32 a110, %2\n\t"
-      "v_accvgpr_write_b32 a111, %3\n\t"
-      "v_accvgpr_read_b32 %0, a112\n\t"
-      "v_accvgpr_read_b32 %1, a113\n\t"
-      "v_accvgpr_read_b32 %2, a114\n\t"
-      "v_accvgpr_read_b32 %3, a115\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a112, %0\n\t"
-      "v_accvgpr_write_b32 a113, %1\n\t"
-      "v_accvgpr_write_b32 a114, %2\n\t"
-      "v_accvgpr_write_b32 a115, %3\n\t"
-      "v_accvgpr_read_b32 %0, a116\n\t"
-      "v_accvgpr_read_b32 %1, a117\n\t"
-      "v_accvgpr_read_b32 %2, a118\n\t"
-      "v_accvgpr_read_b32 %3, a119\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a116, %0\n\t"
-      "v_accvgpr_write_b32 a117, %1\n\t"
-      "v_accvgpr_write_b32 a118, %2\n\t"
-      "v_accvgpr_write_b32 a119, %3\n\t"
-      "v_accvgpr_read_b32 %0, a120\n\t"
-      "v_accvgpr_read_b32 %1, a121\n\t"
-      "v_accvgpr_read_b32 %2, a122\n\t"
-      "v_accvgpr_read_b32 %3, a123\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a120, %0\n\t"
-      "v_accvgpr_write_b32 a121, %1\n\t"
-      "v_accvgpr_write_b32 a122, %2\n\t"
-      "v_accvgpr_write_b32 a123, %3\n\t"
-      "v_accvgpr_read_b32 %0, a124\n\t"
-      "v_accvgpr_read_b32 %1, a125\n\t"
-      "v_accvgpr_read_b32 %2, a126\n\t"
-      "v_accvgpr_read_b32 %3, a127\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a124, %0\n\t"
-      "v_accvgpr_write_b32 a125, %1\n\t"
-      "v_accvgpr_write_b32 a126, %2\n\t"
-      "v_accvgpr_write_b32 a127, %3\n\t"
-      "v_accvgpr_read_b32 %0, a128\n\t"
-      "v_accvgpr_read_b32 %1, a129\n\t"
-      "v_accvgpr_read_b32 %2, a130\n\t"
-      "v_accvgpr_read_b32 %3, a131\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a128, %0\n\t"
-      "v_accvgpr_write_b32 a129, %1\n\t"
-      "v_accvgpr_write_b32 a130, %2\n\t"
-      "v_accvgpr_write_b32 a131, %3\n\t"
-      "v_accvgpr_read_b32 %0, a132\n\t"
-      "v_accvgpr_read_b32 %1, a133\n\t"
-      "v_accvgpr_read_b32 %2, a134\n\t"
-      "v_accvgpr_read_b32 %3, a135\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a132, %0\n\t"
-      "v_accvgpr_write_b32 a133, %1\n\t"
-      "v_accvgpr_write_b32 a134, %2\n\t"
-      "v_accvgpr_write_b32 a135, %3\n\t"
-      "v_accvgpr_read_b32 %0, a136\n\t"
-      "v_accvgpr_read_b32 %1, a137\n\t"
-      "v_accvgpr_read_b32 %2, a138\n\t"
-      "v_accvgpr_read_b32 %3, a139\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a136, %0\n\t"
-      "v_accvgpr_write_b32 a137, %1\n\t"
-      "v_accvgpr_write_b32 a138, %2\n\t"
-      "v_accvgpr_write_b32 a139, %3\n\t"
-      "v_accvgpr_read_b32 %0, a140\n\t"
-      "v_accvgpr_read_b32 %1, a141\n\t"
-      "v_accvgpr_read_b32 %2, a142\n\t"
-      "v_accvgpr_read_b32 %3, a143\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a140, %0\n\t"
-      "v_accvgpr_write_b32 a141, %1\n\t"
-      "v_accvgpr_write_b32 a142, %2\n\t"
-      "v_accvgpr_write_b32 a143, %3\n\t"
-      "v_accvgpr_read_b32 %0, a144\n\t"
-      "v_accvgpr_read_b32 %1, a145\n\t"
-      "v_accvgpr_read_b32 %2, a146\n\t"
-      "v_accvgpr_read_b32 %3, a147\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a144, %0\n\t"
-      "v_accvgpr_write_b32 a145, %1\n\t"
-      "v_accvgpr_write_b32 a146, %2\n\t"
-      "v_accvgpr_write_b32 a147, %3\n\t"
-      "v_accvgpr_read_b32 %0, a148\n\t"
-      "v_accvgpr_read_b32 %1, a149\n\t"
-      "v_accvgpr_read_b32 %2, a150\n\t"
-      "v_accvgpr_read_b32 %3, a151\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a148, %0\n\t"
-      "v_accvgpr_write_b32 a149, %1\n\t"
-      "v_accvgpr_write_b32 a150, %2\n\t"
-      "v_accvgpr_write_b32 a151, %3\n\t"
-      "v_accvgpr_read_b32 %0, a152\n\t"
-      "v_accvgpr_read_b32 %1, a153\n\t"
-      "v_accvgpr_read_b32 %2, a154\n\t"
-      "v_accvgpr_read_b32 %3, a155\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a152, %0\n\t"
-      "v_accvgpr_write_b32 a153, %1\n\t"
-      "v_accvgpr_write_b32 a154, %2\n\t"
-      "v_accvgpr_write_b32 a155, %3\n\t"
-      "v_accvgpr_read_b32 %0, a156\n\t"
-      "v_accvgpr_read_b32 %1, a157\n\t"
-      "v_accvgpr_read_b32 %2, a158\n\t"
-      "v_accvgpr_read_b32 %3, a159\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a156, %0\n\t"
-      "v_accvgpr_write_b32 a157, %1\n\t"
-      "v_accvgpr_write_b32 a158, %2\n\t"
-      "v_accvgpr_write_b32 a159, %3\n\t"
-      "v_accvgpr_read_b32 %0, a160\n\t"
-      "v_accvgpr_read_b32 %1, a161\n\t"
-      "v_accvgpr_read_b32 %2, a162\n\t"
-      "v_accvgpr_read_b32 %3, a163\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a160, %0\n\t"
-      "v_accvgpr_write_b32 a161, %1\n\t"
-      "v_accvgpr_write_b32 a162, %2\n\t"
-      "v_accvgpr_write_b32 a163, %3\n\t"
-      "v_accvgpr_read_b32 %0, a164\n\t"
-      "v_accvgpr_read_b32 %1, a165\n\t"
-      "v_accvgpr_read_b32 %2, a166\n\t"
-      "v_accvgpr_read_b32 %3, a167\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a164, %0\n\t"
-      "v_accvgpr_write_b32 a165, %1\n\t"
-      "v_accvgpr_write_b32 a166, %2\n\t"
-      "v_accvgpr_write_b32 a167, %3\n\t"
-      "v_accvgpr_read_b32 %0, a168\n\t"
-      "v_accvgpr_read_b32 %1, a169\n\t"
-      "v_accvgpr_read_b32 %2, a170\n\t"
-      "v_accvgpr_read_b32 %3, a171\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a168, %0\n\t"
-      "v_accvgpr_write_b32 a169, %1\n\t"
-      "v_accvgpr_write_b32 a170, %2\n\t"
-      "v_accvgpr_write_b32 a171, %3\n\t"
-      "v_accvgpr_read_b32 %0, a172\n\t"
-      "v_accvgpr_read_b32 %1, a173\n\t"
-      "v_accvgpr_read_b32 %2, a174\n\t"
-      "v_accvgpr_read_b32 %3, a175\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a172, %0\n\t"
-      "v_accvgpr_write_b32 a173, %1\n\t"
-      "v_accvgpr_write_b32 a174, %2\n\t"
-      "v_accvgpr_write_b32 a175, %3\n\t"
-      "v_accvgpr_read_b32 %0, a176\n\t"
-      "v_accvgpr_read_b32 %1, a177\n\t"
-      "v_accvgpr_read_b32 %2, a178\n\t"
-      "v_accvgpr_read_b32 %3, a179\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a176, %0\n\t"
-      "v_accvgpr_write_b32 a177, %1\n\t"
-      "v_accvgpr_write_b32 a178, %2\n\t"
-      "v_accvgpr_write_b32 a179, %3\n\t"
-      "v_accvgpr_read_b32 %0, a180\n\t"
-      "v_accvgpr_read_b32 %1, a181\n\t"
-      "v_accvgpr_read_b32 %2, a182\n\t"
-      "v_accvgpr_read_b32 %3, a183\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a180, %0\n\t"
-      "v_accvgpr_write_b32 a181, %1\n\t"
-      "v_accvgpr_write_b32 a182, %2\n\t"
-      "v_accvgpr_write_b32 a183, %3\n\t"
-      "v_accvgpr_read_b32 %0, a184\n\t"
-      "v_accvgpr_read_b32 %1, a185\n\t"
-      "v_accvgpr_read_b32 %2, a186\n\t"
-      "v_accvgpr_read_b32 %3, a187\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a184, %0\n\t"
-      "v_accvgpr_write_b32 a185, %1\n\t"
-      "v_accvgpr_write_b32 a186, %2\n\t"
-      "v_accvgpr_write_b32 a187, %3\n\t"
-      "v_accvgpr_read_b32 %0, a188\n\t"
-      "v_accvgpr_read_b32 %1, a189\n\t"
-      "v_accvgpr_read_b32 %2, a190\n\t"
-      "v_accvgpr_read_b32 %3, a191\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a188, %0\n\t"
-      "v_accvgpr_write_b32 a189, %1\n\t"
-      "v_accvgpr_write_b32 a190, %2\n\t"
-      "v_accvgpr_write_b32 a191, %3\n\t"
-      "v_accvgpr_read_b32 %0, a192\n\t"
-      "v_accvgpr_read_b32 %1, a193\n\t"
-      "v_accvgpr_read_b32 %2, a194\n\t"
-      "v_accvgpr_read_b32 %3, a195\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a192, %0\n\t"
-      "v_accvgpr_write_b32 a193, %1\n\t"
-      "v_accvgpr_write_b32 a194, %2\n\t"
-      "v_accvgpr_write_b32 a195, %3\n\t"
-      "v_accvgpr_read_b32 %0, a196\n\t"
-      "v_accvgpr_read_b32 %1, a197\n\t"
-      "v_accvgpr_read_b32 %2, a198\n\t"
-      "v_accvgpr_read_b32 %3, a199\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a196, %0\n\t"
-      "v_accvgpr_write_b32 a197, %1\n\t"
-      "v_accvgpr_write_b32 a198, %2\n\t"
-      "v_accvgpr_write_b32 a199, %3\n\t"
-      "v_accvgpr_read_b32 %0, a200\n\t"
-      "v_accvgpr_read_b32 %1, a201\n\t"
-      "v_accvgpr_read_b32 %2, a202\n\t"
-      "v_accvgpr_read_b32 %3, a203\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a200, %0\n\t"
-      "v_accvgpr_write_b32 a201, %1\n\t"
-      "v_accvgpr_write_b32 a202, %2\n\t"
-      "v_accvgpr_write_b32 a203, %3\n\t"
-      "v_accvgpr_read_b32 %0, a204\n\t"
-      "v_accvgpr_read_b32 %1, a205\n\t"
-      "v_accvgpr_read_b32 %2, a206\n\t"
-      "v_accvgpr_read_b32 %3, a207\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a204, %0\n\t"
-      "v_accvgpr_write_b32 a205, %1\n\t"
-      "v_accvgpr_write_b32 a206, %2\n\t"
-      "v_accvgpr_write_b32 a207, %3\n\t"
-      "v_accvgpr_read_b32 %0, a208\n\t"
-      "v_accvgpr_read_b32 %1, a209\n\t"
-      "v_accvgpr_read_b32 %2, a210\n\t"
-      "v_accvgpr_read_b32 %3, a211\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a208, %0\n\t"
-      "v_accvgpr_write_b32 a209, %1\n\t"
-      "v_accvgpr_write_b32 a210, %2\n\t"
-      "v_accvgpr_write_b32 a211, %3\n\t"
-      "v_accvgpr_read_b32 %0, a212\n\t"
-      "v_accvgpr_read_b32 %1, a213\n\t"
-      "v_accvgpr_read_b32 %2, a214\n\t"
-      "v_accvgpr_read_b32 %3, a215\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a212, %0\n\t"
-      "v_accvgpr_write_b32 a213, %1\n\t"
-      "v_accvgpr_write_b32 a214, %2\n\t"
-      "v_accvgpr_write_b32 a215, %3\n\t"
-      "v_accvgpr_read_b32 %0, a216\n\t"
-      "v_accvgpr_read_b32 %1, a217\n\t"
-      "v_accvgpr_read_b32 %2, a218\n\t"
-      "v_accvgpr_read_b32 %3, a219\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a216, %0\n\t"
-      "v_accvgpr_write_b32 a217, %1\n\t"
-      "v_accvgpr_write_b32 a218, %2\n\t"
-      "v_accvgpr_write_b32 a219, %3\n\t"
-      "v_accvgpr_read_b32 %0, a220\n\t"
-      "v_accvgpr_read_b32 %1, a221\n\t"
-      "v_accvgpr_read_b32 %2, a222\n\t"
-      "v_accvgpr_read_b32 %3, a223\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a220, %0\n\t"
-      "v_accvgpr_write_b32 a221, %1\n\t"
-      "v_accvgpr_write_b32 a222, %2\n\t"
-      "v_accvgpr_write_b32 a223, %3\n\t"
-      "v_accvgpr_read_b32 %0, a224\n\t"
-      "v_accvgpr_read_b32 %1, a225\n\t"
-      "v_accvgpr_read_b32 %2, a226\n\t"
-      "v_accvgpr_read_b32 %3, a227\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a224, %0\n\t"
-      "v_accvgpr_write_b32 a225, %1\n\t"
-      "v_accvgpr_write_b32 a226, %2\n\t"
-      "v_accvgpr_write_b32 a227, %3\n\t"
-      "v_accvgpr_read_b32 %0, a228\n\t"
-      "v_accvgpr_read_b32 %1, a229\n\t"
-      "v_accvgpr_read_b32 %2, a230\n\t"
-      "v_accvgpr_read_b32 %3, a231\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a228, %0\n\t"
-      "v_accvgpr_write_b32 a229, %1\n\t"
-      "v_accvgpr_write_b32 a230, %2\n\t"
-      "v_accvgpr_write_b32 a231, %3\n\t"
-      "v_accvgpr_read_b32 %0, a232\n\t"
-      "v_accvgpr_read_b32 %1, a233\n\t"
-      "v_accvgpr_read_b32 %2, a234\n\t"
-      "v_accvgpr_read_b32 %3, a235\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a232, %0\n\t"
-      "v_accvgpr_write_b32 a233, %1\n\t"
-      "v_accvgpr_write_b32 a234, %2\n\t"
-      "v_accvgpr_write_b32 a235, %3\n\t"
-      "v_accvgpr_read_b32 %0, a236\n\t"
-      "v_accvgpr_read_b32 %1, a237\n\t"
-      "v_accvgpr_read_b32 %2, a238\n\t"
-      "v_accvgpr_read_b32 %3, a239\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a236, %0\n\t"
-      "v_accvgpr_write_b32 a237, %1\n\t"
-      "v_accvgpr_write_b32 a238, %2\n\t"
-      "v_accvgpr_write_b32 a239, %3\n\t"
-      "v_accvgpr_read_b32 %0, a240\n\t"
-      "v_accvgpr_read_b32 %1, a241\n\t"
-      "v_accvgpr_read_b32 %2, a242\n\t"
-      "v_accvgpr_read_b32 %3, a243\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a240, %0\n\t"
-      "v_accvgpr_write_b32 a241, %1\n\t"
-      "v_accvgpr_write_b32 a242, %2\n\t"
-      "v_accvgpr_write_b32 a243, %3\n\t"
-      "v_accvgpr_read_b32 %0, a244\n\t"
-      "v_accvgpr_read_b32 %1, a245\n\t"
-      "v_accvgpr_read_b32 %2, a246\n\t"
-      "v_accvgpr_read_b32 %3, a247\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a244, %0\n\t"
-      "v_accvgpr_write_b32 a245, %1\n\t"
-      "v_accvgpr_write_b32 a246, %2\n\t"
-      "v_accvgpr_write_b32 a247, %3\n\t"
-      "v_accvgpr_read_b32 %0, a248\n\t"
-      "v_accvgpr_read_b32 %1, a249\n\t"
-      "v_accvgpr_read_b32 %2, a250\n\t"
-      "v_accvgpr_read_b32 %3, a251\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a248, %0\n\t"
-      "v_accvgpr_write_b32 a249, %1\n\t"
-      "v_accvgpr_write_b32 a250, %2\n\t"
-      "v_accvgpr_write_b32 a251, %3\n\t"
-      "v_accvgpr_read_b32 %0, a252\n\t"
-      "v_accvgpr_read_b32 %1, a253\n\t"
-      "v_accvgpr_read_b32 %2, a254\n\t"
-      "v_accvgpr_read_b32 %3, a255\n\t"
-      "v_mul_f32 %0, %0, %4\n\t"
-      "v_mul_f32 %1, %1, %4\n\t"
-      "v_mul_f32 %2, %2, %4\n\t"
-      "v_mul_f32 %3, %3, %4\n\t"
-      "v_accvgpr_write_b32 a252, %0\n\t"
-      "v_accvgpr_write_b32 a253, %1\n\t"
-      "v_accvgpr_write_b32 a254, %2\n\t"
-      "v_accvgpr_write_b32 a255, %3\n\t"
+      MLA_SCALE4(0, 1, 2, 3) MLA_SCALE4(4, 5, 6, 7) MLA_SCALE4(8, 9, 10, 11) MLA_SCALE4(12, 13, 14, 15)
+      MLA_SCALE4(16, 17, 18, 19) MLA_SCALE4(20, 21, 22, 23) MLA_SCALE4(24, 25, 26, 27) MLA_SCALE4(28, 29, 30, 31)
+      MLA_SCALE4(32, 33, 34, 35) MLA_SCALE4(36, 37, 38, 39) MLA_SCALE4(40, 41, 42, 43) MLA_SCALE4(44, 45, 46, 47)
+      MLA_SCALE4(48, 49, 50, 51) MLA_SCALE4(52, 53, 54, 55) MLA_SCALE4(56, 57, 58, 59) MLA_SCALE4(60, 61, 62, 63)
+      MLA_SCALE4(64, 65, 66, 67) MLA_SCALE4(68, 69, 70, 71) MLA_SCALE4(72, 73, 74, 75) MLA_SCALE4(76, 77, 78, 79)
+      MLA_SCALE4(80, 81, 82, 83) MLA_SCALE4(84, 85, 86, 87) MLA_SCALE4(88, 89, 90, 91) MLA_SCALE4(92, 93, 94, 95)
+      MLA_SCALE4(96, 97, 98, 99) MLA_SCALE4(100, 101, 102, 103) MLA_SCALE4(104, 105, 106, 107) MLA_SCALE4(108, 109, 110, 111)
+      MLA_SCALE4(112, 113, 114, 115) MLA_SCALE4(116, 117, 118, 119) MLA_SCALE4(120, 121, 122, 123) MLA_SCALE4(124, 125, 126, 127)
+      MLA_SCALE4(128, 129, 130, 131) MLA_SCALE4(132, 133, 134, 135) MLA_SCALE4(136, 137, 138, 139) MLA_SCALE4(140, 141, 142, 143)
+      MLA_SCALE4(144, 145, 146, 147) MLA_SCALE4(148, 149, 150, 151) MLA_SCALE4(152, 153, 154, 155) MLA_SCALE4(156, 157, 158, 159)
+      MLA_SCALE4(160, 161, 162, 163) MLA_SCALE4(164, 165, 166, 167) MLA_SCALE4(168, 169, 170, 171) MLA_SCALE4(172, 173, 174, 175)
+      MLA_SCALE4(176, 177, 178, 179) MLA_SCALE4(180, 181, 182, 183) MLA_SCALE4(184, 185, 186, 187) MLA_SCALE4(188, 189, 190, 191)
+      MLA_SCALE4(192, 193, 194, 195) MLA_SCALE4(196, 197, 198, 199) MLA_SCALE4(200, 201, 202, 203) MLA_SCALE4(204, 205, 206, 207)
+      MLA_SCALE4(208, 209, 210, 211) MLA_SCALE4(212, 213, 214, 215) MLA_SCALE4(216, 217, 218, 219) MLA_SCALE4(220, 221, 222, 223)
+      MLA_SCALE4(224, 225, 226, 227) MLA_SCALE4(228, 229, 230, 231) MLA_SCALE4(232, 233, 234, 235) MLA_SCALE4(236, 237, 238, 239)
+      MLA_SCALE4(240, 241, 242, 243) MLA_SCALE4(244, 245, 246, 247) MLA_SCALE4(248, 249, 250, 251) MLA_SCALE4(252, 253, 254, 255)
       "s_nop 7"
       : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
       : "v"(alpha)
       : "memory");
 }
+#undef MLA_SCALE4
 
 struct WorkItem {
   int b, k, n, L;  // sequence, chunk index, chunk count, sequence length
