@@ -78,6 +78,32 @@ __device__ __forceinline__ int lane_id() {
   return l;
 }
 
+// One round of staged query rows (both decode kernels stage the rows of a
+// workgroup through LDS with coalesced direct loads, then read their
+// operands from there): `nrows` rows of `cols` bytes from column byte
+// `col0`, row R at R * (cols + 16) bytes of the area, so that the 16 rows of
+// a 16-byte read pass start on 16 different bank groups. nrows * (cols + 16)
+// must be a multiple of 1024: instruction i of the round fills area bytes
+// 1024i .. 1024i + 1023, and the waves take instructions w, w + 4, ... Lanes
+// that fall on a row's padding load the row's first piece (never read).
+__device__ __forceinline__ void issue_q_round(const char* q_seq, int rows, int row_base, int nrows, int cols,
+                                              int col0, char* area, int wave, int lane) {
+  const int stride = cols + 16;
+  const int n_inst = nrows * stride / 1024;
+  const uint64_t gp = (uint64_t)(uintptr_t)q_seq;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gp);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(gp >> 32));
+  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)area);
+  for (int i = wave; i < n_inst; i += kWaves) {
+    const int byte = 1024 * i + 16 * lane;
+    const int R = byte / stride, off = byte - R * stride;
+    const int row = min(row_base + R, rows - 1);
+    dma_line_cached(sbase, row * (kDqk * 2) + col0 + (off < cols ? off : 0), lds0 + 1024 * i);
+  }
+}
+
 // Value of lane l ^ 32 (gfx950 lane swap; VALU, no LDS round trip). With
 // both operands equal, permlane32_swap yields the values of lanes l and l^32.
 __device__ __forceinline__ float other_half(float v) {

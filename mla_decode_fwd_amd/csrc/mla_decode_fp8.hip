@@ -65,6 +65,9 @@ constexpr int kQPairs = kQSteps / 2;                 // 18 LDS reads per tile, 2
 // allocation covers that as well as the two page buffers.
 constexpr int kStageBytes = kWaves * kWaveRows * kDv * 2;  // 131,072
 constexpr int kSmemBytes = 2 * kBufBytes > kStageBytes ? 2 * kBufBytes : kStageBytes;
+// The staged query rows (two rounds of 128 rows x 592 bytes) follow the
+// first page buffer.
+static_assert(kBufBytes + kRowsPerGroup * (kDqk + 16) <= kSmemBytes, "query staging area");
 
 // Line n of a page covers LDS slots 64n .. 64n+63; lane l loads slot 64n + l:
 // row t = k / 37, chunk c = k % 37 (the padding chunk re-reads chunk 35).
@@ -168,19 +171,44 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
   __builtin_amdgcn_sched_barrier(0);
 
   // Q^T fragments in the permuted contraction order: k-step 2s+e holds
-  // q[row][32s + 16*hi32 + 8e .. +8].
+  // q[row][32s + 16*hi32 + 8e .. +8]. The workgroup's 128 rows are staged
+  // through LDS (issue_q_round) in two rounds, dims 0..287 (issued ahead of
+  // the first page, whose loads go on while it is read) and 288..575, in the
+  // area past the first page buffer.
   bf16x8_t qf[kQSteps];
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q_lat) + ((size_t)b * rows + row_c) * kDqk + 16 * hi32;
-#pragma unroll
-    for (int s = 0; s < kQSteps; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (s >> 1) + 8 * (s & 1));
-  }
+  const char* const q_seq = static_cast<const char*>(a.q_lat) + (size_t)b * rows * (kDqk * 2);
+  char* const q_area = smem + kBufBytes;
+  issue_q_round(q_seq, rows, rgrp * kRowsPerGroup, kRowsPerGroup, kDqk, 0, q_area, wave, lane);
 
   int phys_ahead = 0;
   if (pg0 < pg1) {
     issue_page8(make_load8(cache, a.row_scales, min(max(bt0, 0), last_phys), smem), wave, lane);
     phys_ahead = bt1;
+    // The query round, not the page (10 loads on waves 0 and 1, 9 on the others).
+    if (wave < 2)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(10));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(9));
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+  __syncthreads();
+  {
+    const char* const src = q_area + (wave * kWaveRows + r32) * (kDqk + 16) + 32 * hi32;
+#pragma unroll
+    for (int s = 0; s < kQSteps / 2; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8_t*>(src + 64 * (s >> 1) + 16 * (s & 1));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __syncthreads();  // every wave has its first half: the area takes the second
+    issue_q_round(q_seq, rows, rgrp * kRowsPerGroup, kRowsPerGroup, kDqk, kDqk, q_area, wave, lane);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+#pragma unroll
+    for (int s = kQSteps / 2; s < kQSteps; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8_t*>(src + 64 * ((s - kQSteps / 2) >> 1) + 16 * (s & 1));
+    // The next page's loads overwrite the area: every read is done before
+    // the page loop's first barrier.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 
   f32x16_t acc_o[kColTiles];
