@@ -459,6 +459,7 @@ def main():
         absorb_main(args)
         return
 
+    import numpy as np
     import torch
 
     import mla_decode_fwd_amd as mla
@@ -550,6 +551,28 @@ def main():
     rr = interleaved_regions(step, lambda i: dec_calls[i % 2](), comb_call, stream, args.roofline_rounds,
                              args.roofline_block)
     decode_ms, combine_ms = rr["decode_ms"], rr["combine_ms"]
+    # The shader clock the decode ran at: per-workgroup clock stamps
+    # (mla_decode_clock_probe; the bf16 kernel only) over 20 more launches
+    # right after the interleaved rounds, read from the last launch.
+    clock = None
+    if not fp8_mode:
+        stamps = torch.zeros(2 * 8192, dtype=torch.int64, device=dev)
+        torch.cuda.synchronize()
+        mla.decode_clock_probe(stamps)
+        for i in range(20):
+            dec_calls[i % 2]()
+        torch.cuda.synchronize()
+        mla.decode_clock_probe(None)
+        st = stamps.view(-1, 2).cpu().numpy()
+        st = st[st[:, 1] > 0]
+        if len(st):
+            mhz = st[:, 0] / st[:, 1] * 100.0
+            clock = {"median_mhz": round(float(np.median(mhz)), 1),
+                     "p10_mhz": round(float(np.percentile(mhz, 10)), 1),
+                     "p90_mhz": round(float(np.percentile(mhz, 90)), 1),
+                     "workgroups": int(len(st)),
+                     "source": "s_memtime cycles over s_memrealtime (100 MHz) ticks per workgroup, "
+                               "last of 20 decode launches after the interleaved rounds"}
     # Distribution and warm-cache figures, from separate regions after the
     # timed ones: one event pair per step (each event costs the GPU a few
     # microseconds, so these steps read a little slower than ms_per_step),
@@ -637,7 +660,8 @@ def main():
                                 f"interleaved rounds of [{rr['block']} steps | {rr['block']} decode launches | "
                                 f"{rr['block']} merge launches], after the timed steps"),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-                     "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4)},
+                     "mfma_tflops": round(dec_rf["tflops"], 1), "mfma_frac": round(dec_rf["frac_mfma"], 4),
+                     "shader_clock": clock},
         "plan_host_us": round(plan_us, 1),
         "step_gpu_ms": round(step_gpu_ms, 5),
         "step_us_percentiles": None if args.skip_extra else {"p10": round(per_step_us[len(per_step_us) // 10], 2),

@@ -76,11 +76,12 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t status);
 
-/* Library ABI version, currently 7 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
+/* Library ABI version, currently 8 (2 added mla_sparse_decode_fwd, 3 mla_decode_fwd_fp8,
    4 the expanded path: mla_select_path, mla_prefill_workspace_size, mla_prefill_fwd,
    5 the FP8 products: mla_fp8_workspace_size, mla_quantize_e4m3, mla_absorb_q_fp8,
    mla_out_uv_fp8, 6 mla_decode_noalloc_scratch_bytes and mla_decode_fwd_noalloc, 7 the balanced
-   schedule: mla_decode_schedule_capacity, mla_decode_schedule, mla_decode_fwd_scheduled). */
+   schedule: mla_decode_schedule_capacity, mla_decode_schedule, mla_decode_fwd_scheduled,
+   8 mla_decode_clock_probe). */
 int mla_abi_version(void);
 
 /*
@@ -479,6 +480,23 @@ mla_status_t mla_absorb_q_fp8(const void* q_nope, const void* q_rope, const uint
  */
 mla_status_t mla_out_uv_fp8(const void* o_lat, const uint8_t* w_uv_t, float w_scale, int N, int H, int d_c, int d_v,
                             void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * A measurement aid, not part of the computation: the shader clock at which
+ * the bf16 decode kernel runs (mla_decode_fwd and mla_decode_fwd_scheduled
+ * with bf16 inputs, dense or top-k). While `device_buffer` is set, every
+ * workgroup x < capacity of later launches on the current device writes two
+ * uint64 words at device_buffer[2x]: the shader-clock cycles (s_memtime) and
+ * the 100 MHz reference-clock ticks (s_memrealtime) from its start to its
+ * end, so cycles / ticks * 100 MHz is the clock it ran at. Workgroups with no
+ * work write nothing. device_buffer = NULL (capacity ignored) switches the
+ * stamps off; the setting is per device and stays until changed. The caller
+ * owns the buffer (device memory, 2 * capacity uint64 words) and keeps it
+ * alive while the setting is on; launches already queued may or may not see
+ * a change, so synchronize around it. capacity < 0 with a non-NULL buffer
+ * gives MLA_ERR_INVALID_ARG.
+ */
+mla_status_t mla_decode_clock_probe(uint64_t* device_buffer, int capacity);
 
 #ifdef __cplusplus
 }

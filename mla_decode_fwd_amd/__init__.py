@@ -28,7 +28,7 @@ __all__ = [
     "select_path", "prefill_workspace_size", "mla_prefill_fwd", "mla_attention_fwd",
     "fp8_workspace_size", "quantize_e4m3", "mla_absorb_q_fp8", "mla_out_uv_fp8",
     "mla_decode_fwd_noalloc", "noalloc_scratch_bytes", "NOALLOC_SCRATCH_BYTES",
-    "DecodeSchedule", "decode_schedule",
+    "DecodeSchedule", "decode_schedule", "decode_clock_probe",
     "D_QK", "D_V", "PAGE_SIZE", "MAX_SPLITS", "MAX_DECODE_SQ",
 ]
 
@@ -75,6 +75,7 @@ def load_library():
         "mla_status_string": ([I], ctypes.c_char_p),
         "mla_abi_version": ([], I),
         "mla_decode_workspace_size": ([I, I, I], Z),
+        "mla_decode_clock_probe": ([P, I], I),
         "mla_decode_plan": ([P, I, I, I, I, I, P, P, P], I),
         "mla_decode_fwd": ([P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, Z, P, P, P], I),
         "mla_sparse_decode_fwd": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P, Z, P, P, P], I),
@@ -135,6 +136,21 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None):
 
 def decode_workspace_size(total_splits: int, s_q: int, H: int) -> int:
     return int(load_library().mla_decode_workspace_size(int(total_splits), int(s_q), int(H)))
+
+
+def decode_clock_probe(buffer: Optional[torch.Tensor]) -> None:
+    """Clock stamps of the bf16 decode kernel (mla_decode_clock_probe): with a
+    device int64 tensor of 2 * capacity elements, workgroup x of later launches
+    on its device writes [shader cycles, 100 MHz ticks] at buffer[2x:2x+2];
+    None switches them off (on the current device)."""
+    if buffer is None:
+        st = load_library().mla_decode_clock_probe(None, 0)
+    else:
+        _need(buffer, "buffer", dtype=torch.int64)
+        if buffer.dim() != 1 or buffer.numel() % 2:
+            raise ValueError("buffer must be a 1-D int64 tensor of 2 * capacity elements")
+        st = load_library().mla_decode_clock_probe(_ptr(buffer), buffer.numel() // 2)
+    _check("mla_decode_clock_probe", st)
 
 
 class DecodePlan:

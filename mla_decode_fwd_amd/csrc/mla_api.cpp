@@ -46,7 +46,7 @@ const char* mla_status_string(mla_status_t status) {
   return "unknown status";
 }
 
-int mla_abi_version(void) { return 7; }
+int mla_abi_version(void) { return 8; }
 
 size_t mla_decode_workspace_size(int total_splits, int s_q, int H) {
   return workspace_size(total_splits, s_q, H);
@@ -551,6 +551,11 @@ mla_status_t mla_out_uv_fp8(const void* o_lat, const uint8_t* w_uv_t, float w_sc
   if (!workspace || workspace_bytes < mla_fp8_workspace_size(n)) return MLA_ERR_WORKSPACE;
   return from_hip(mla::launch_bmm_fp8(o_lat, static_cast<float*>(workspace), w_uv_t, w_scale, N, H, d_c, d_v, out,
                                       d_v, nullptr, 0, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_decode_clock_probe(uint64_t* device_buffer, int capacity) {
+  if (device_buffer != nullptr && capacity < 0) return MLA_ERR_INVALID_ARG;
+  return from_hip(mla::set_clock_probe(device_buffer, capacity));
 }
 
 }  // extern "C"

@@ -794,6 +794,34 @@ __device__ __forceinline__ void load_chunk_desc(const int32_t* desc, int c, int&
   L = __builtin_amdgcn_readlane(v, 3);
 }
 
+// Measurement aid (mla_decode_clock_probe): while `buf` is set, workgroup x
+// < cap writes its shader-clock cycles and 100 MHz reference ticks from its
+// start to its end at buf[2x], buf[2x+1]. One copy per device. The start
+// stamps go to the buffer (nothing is held in registers through the kernel,
+// where every register is taken) and the end turns them into differences.
+struct ClockProbe {
+  uint64_t* buf;
+  int cap;
+};
+__device__ ClockProbe g_clock_probe = {nullptr, 0};
+
+__device__ __forceinline__ void clock_begin() {
+  const ClockProbe p = g_clock_probe;
+  if (p.buf != nullptr && threadIdx.x == 0 && (int)blockIdx.x < p.cap) {
+    p.buf[2 * (size_t)blockIdx.x] = __builtin_amdgcn_s_memtime();
+    p.buf[2 * (size_t)blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+__device__ __forceinline__ void clock_end() {
+  const ClockProbe p = g_clock_probe;
+  if (p.buf != nullptr && threadIdx.x == 0 && (int)blockIdx.x < p.cap) {
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    uint64_t* const w = p.buf + 2 * (size_t)blockIdx.x;
+    w[0] = t1 - __builtin_nontemporal_load(w);
+    w[1] = r1 - __builtin_nontemporal_load(w + 1);
+  }
+}
+
 template <bool kSparse, bool kHalf>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a, int row_groups, int n_units) {
   constexpr int kSparseBytes = kSparse ? kSparseMaxTopk * 4 + (kSparseMaxTopk / kPage) * 8 : 0;
@@ -813,6 +841,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int per_xcd = (n_units + 7) / 8;
   const int g = xcd * per_xcd + rest / row_groups;
   if (rest / row_groups >= per_xcd || g >= n_units) return;
+  clock_begin();
 
   if (a.schedule != nullptr) {
     // Balanced schedule: unit g is segment g; its chunks are consecutive
@@ -837,6 +866,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       decode_chunk<false, kHalf>(a, smem, b, L, p0, p1, c, direct, rgrp, wave);
       __syncthreads();  // the staging area is the next chunk's first page buffer
     }
+    clock_end();
     return;
   }
 
@@ -850,6 +880,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int pg0 = (int)((unsigned)kk * (unsigned)P / (unsigned)n_chunks);
   const int pg1 = (int)((unsigned)(kk + 1) * (unsigned)P / (unsigned)n_chunks);
   decode_chunk<kSparse, kHalf>(a, smem, wi.b, L, pg0, pg1, g, n_chunks == 1 && a.o_lat != nullptr, rgrp, wave);
+  clock_end();
 }
 
 template <bool kSparse, bool kHalf>
@@ -871,5 +902,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   return launch<false, false>(a, stream);
 }
 hipError_t launch_sparse_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch<true, false>(a, stream); }
+
+hipError_t set_clock_probe(uint64_t* buf, int cap) {
+  const ClockProbe p = {buf, buf != nullptr ? cap : 0};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_clock_probe), &p, sizeof(p));
+}
 
 }  // namespace mla

@@ -79,6 +79,10 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 // LSE merge. skip_single: sequences with one chunk were written directly by
 // the decode kernel and are left alone.
 // o_part holds the output dtype (bf16 when out_bf16, else fp32).
+// Sets (buf non-null) or clears the bf16 decode kernel's clock stamps on the
+// current device (mla_decode_clock_probe).
+hipError_t set_clock_probe(uint64_t* buf, int cap);
+
 hipError_t launch_combine(const void* o_part, const float* lse_part, const int32_t* split_offsets,
                           int total_splits, int B, int s_q, int H, bool out_bf16, bool skip_single,
                           void* o_lat, float* lse, hipStream_t stream);

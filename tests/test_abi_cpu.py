@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert mla.abi_version() == 7
+    assert mla.abi_version() == 8
     for code in range(5):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -396,3 +396,8 @@ def test_schedule_invalid_arguments(lib):
     assert fwd(rpg=32) == INVALID
     assert fwd(nseg=0) == INVALID
     assert fwd(nseg=5) == INVALID  # more segments than chunks
+
+
+def test_clock_probe_rejects_a_negative_capacity(lib):
+    # Checked before any HIP call: a buffer with a negative capacity.
+    assert lib.mla_decode_clock_probe(FAKE, -1) == INVALID

@@ -101,3 +101,30 @@ def test_schedule_mtp_workloads(s_q):
     o, lse = run(case, plan="schedule")
     o_ref, l_ref = oracle(case)
     compare(o, lse, o_ref, l_ref, torch.bfloat16, case.name + " (schedule)")
+
+
+@pytest.mark.gpu
+def test_clock_probe_stamps_every_workgroup_and_stops_when_off():
+    """mla_decode_clock_probe: with a buffer set, every workgroup of a bf16
+    decode writes its shader-clock cycles and 100 MHz ticks; the clock they
+    give is a plausible MI355X shader clock; the results are unchanged; with
+    the probe off the buffer is left alone."""
+    case = make_decode_case([300, 64, 129, 7], s_q=1, H=128, seed=31)
+    o_ref, l_ref = run(case, plan="schedule")
+    stamps = torch.zeros(2 * 1024, dtype=torch.int64, device="cuda")
+    mla.decode_clock_probe(stamps)
+    try:
+        o, lse = run(case, plan="schedule")
+    finally:
+        mla.decode_clock_probe(None)
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+    st = stamps.view(-1, 2).cpu().numpy()
+    n = int((st[:, 1] > 0).sum())
+    sched = mla.decode_schedule(case.seqlens.tolist(), case.s_q, case.H)
+    groups = -(-(case.s_q * case.H) // sched.rows_per_group)
+    assert n == sched.num_segments * groups, (n, sched.num_segments, groups)
+    mhz = st[st[:, 1] > 0, 0] / st[st[:, 1] > 0, 1] * 100.0
+    assert np.all((mhz > 300) & (mhz < 4000)), mhz
+    snap = stamps.clone()
+    run(case, plan="schedule")
+    assert torch.equal(stamps, snap)
