@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "mla_decode.h"
 #include "mla_internal.h"
@@ -170,57 +171,122 @@ mla_status_t mla_decode_schedule(const int32_t* seqlens_host, int B, int s_q, in
       best_rpg = rpg;
     }
   }
-  // Build the chunks in the global page order (sequence-major), and the
-  // chunk range of every segment.
-  const size_t need_segs = best_seg < 0 ? (size_t)B : (size_t)((total_pages + best_seg - 1) / best_seg);
-  long long total_chunks = 0;
+  // Segment ends (global page offsets). Every chunk costs a workgroup a
+  // fixed prologue and finalize besides its pages (measured on MI355X: one
+  // more chunk in a workgroup adds about as much time as kChunkPages pages),
+  // so segments are cut to equal cost, pages + kChunkPages * chunks, rather
+  // than to equal pages: the smallest cost bound T for which a greedy walk
+  // over the concatenated pages needs at most G segments and cuts no
+  // sequence into more than max_splits chunks. With uniform lengths that
+  // divide evenly this gives the equal segments; with mixed lengths
+  // segments that start or cross more sequences get fewer pages.
+  std::vector<int64_t> P(B);
+  for (int b = 0; b < B; ++b) P[b] = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+  std::vector<int64_t> ends;
   if (best_seg < 0) {
-    total_chunks = B;
+    long long acc = 0;
+    for (int b = 0; b < B; ++b) ends.push_back(acc += P[b]);  // one segment per sequence
   } else {
+    const double kChunkPages = best_rpg == 128 ? 2.0 : 3.4;
+    const long long groups = (rows + best_rpg - 1) / best_rpg;
+    const long long G = num_cus / groups >= 1 ? num_cus / groups : 1;
+    // Greedy walk under bound T: segment count, and (if out) the ends; false
+    // if some sequence gets more than max_splits chunks.
+    const auto walk = [&](double T, long long* n_segs, std::vector<int64_t>* out) {
+      long long segs = 0, pos = 0, chunks_b = 0;
+      int b = 0;
+      long long off = 0;  // pages of sequence b already taken
+      while (b < B) {
+        double cost = 0.0;
+        ++segs;
+        for (;;) {
+          const long long left = P[b] - off;
+          const double room = T - cost - kChunkPages;
+          if (cost > 0.0 && room < 1.0) break;  // no room for another chunk
+          const long long take = room >= (double)left ? left : (room >= 1.0 ? (long long)room : 1);
+          cost += kChunkPages + (double)take;
+          pos += take;
+          off += take;
+          ++chunks_b;
+          if (off == P[b]) {
+            if (chunks_b > max_splits) return false;
+            ++b;
+            off = 0;
+            chunks_b = 0;
+            if (b == B) break;
+          } else {
+            break;  // the segment ends inside sequence b
+          }
+        }
+        if (out) out->push_back(pos);
+      }
+      *n_segs = segs;
+      return true;
+    };
+    // Bisection on T between a bound that needs too many segments (or
+    // breaks the cap) and one that holds: the equal segments' cost.
+    double lo = 0.0, hi = (double)best_seg + kChunkPages * (double)(B + 1) + 1.0;
+    long long n = 0;
+    if (!walk(hi, &n, nullptr) || n > G) hi = (double)total_pages + kChunkPages * (double)B + 1.0;
+    for (int it = 0; it < 60; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (walk(mid, &n, nullptr) && n <= G) hi = mid; else lo = mid;
+    }
+    if (walk(hi, &n, &ends) && n <= G) {
+      // cost-balanced ends
+    } else {
+      ends.clear();  // fall back to the equal segments
+      for (long long e = best_seg; ; e += best_seg) {
+        ends.push_back(e < total_pages ? e : total_pages);
+        if (e >= total_pages) break;
+      }
+    }
+  }
+  // Build the chunks in the global page order (sequence-major): the pieces
+  // of each sequence between segment ends.
+  const size_t need_segs = ends.size();
+  long long total_chunks = 0;
+  {
     long long start = 0;
+    size_t e = 0;
     for (int b = 0; b < B; ++b) {
-      const long long P = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
-      total_chunks += (start + P - 1) / best_seg - start / best_seg + 1;
-      start += P;
+      const long long stop = start + P[b];
+      while (e < ends.size() && ends[e] <= start) ++e;
+      size_t f = e;
+      long long n_b = 1;
+      while (f < ends.size() && ends[f] < stop) { ++n_b; ++f; }
+      total_chunks += n_b;
+      start = stop;
     }
   }
   if (total_chunks > INT_MAX / 4) return MLA_ERR_INVALID_ARG;
   if (need_segs + 1 + 4 * (size_t)total_chunks > schedule_capacity) return MLA_ERR_WORKSPACE;
-  int32_t* seg_first = schedule_host;                    // [segments + 1]
-  int32_t* desc = schedule_host + need_segs + 1;         // [chunks][4]: b, first page, end page, L_b
+  int32_t* seg_first = schedule_host;             // [segments + 1]
+  int32_t* desc = schedule_host + need_segs + 1;  // [chunks][4]: b, first page, end page, L_b
   long long c = 0, start = 0;
+  size_t e = 0;  // first segment whose end lies past the current page
+  seg_first[0] = 0;
+  size_t s = 0;  // segments whose chunk lists are closed
   split_offsets_host[0] = 0;
   for (int b = 0; b < B; ++b) {
-    const long long L = seqlens_host[b];
-    const long long P = (L + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
     long long p = 0;
-    while (p < P) {
-      const long long seg_end = best_seg < 0 ? P : ((start + p) / best_seg + 1) * best_seg - start;
-      const long long e = seg_end < P ? seg_end : P;
+    while (p < P[b]) {
+      while (e < ends.size() && ends[e] <= start + p) ++e;
+      // Segment e holds page start + p: every segment before it is complete.
+      while (s < e) seg_first[++s] = (int32_t)c;
+      const long long seg_end = e < ends.size() ? ends[e] - start : P[b];
+      const long long q = seg_end < P[b] ? seg_end : P[b];
       desc[4 * c + 0] = b;
       desc[4 * c + 1] = (int32_t)p;
-      desc[4 * c + 2] = (int32_t)e;
-      desc[4 * c + 3] = (int32_t)L;
+      desc[4 * c + 2] = (int32_t)q;
+      desc[4 * c + 3] = seqlens_host[b];
       ++c;
-      p = e;
+      p = q;
     }
     split_offsets_host[b + 1] = (int32_t)c;
-    start += P;
+    start += P[b];
   }
-  // Segment s holds the chunks whose first page lies in it.
-  long long s = 0;
-  seg_first[0] = 0;
-  start = 0;
-  long long ci = 0;
-  for (int b = 0; b < B; ++b) {
-    const long long P = ((long long)seqlens_host[b] + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
-    for (long long k = split_offsets_host[b]; k < split_offsets_host[b + 1]; ++k, ++ci) {
-      const long long g = best_seg < 0 ? b : (start + desc[4 * k + 1]) / best_seg;
-      while (s < g) seg_first[++s] = (int32_t)ci;
-    }
-    start += P;
-  }
-  while (s < (long long)need_segs) seg_first[++s] = (int32_t)ci;
+  while (s < need_segs) seg_first[++s] = (int32_t)c;
   *num_segments = (int)need_segs;
   *rows_per_group_out = best_rpg;
   if (workspace_bytes) *workspace_bytes = workspace_size(total_chunks, s_q, H);
