@@ -123,11 +123,13 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
  * that every unit gets about the same work).
  *
  * The pages of all sequences are laid end to end (sequence 0 first) and cut
- * into equal contiguous segments, one per workgroup slot; a segment's
- * intersection with one sequence is a chunk (one partial of the LSE merge),
- * so a segment may cover the end of one sequence and the start of the next,
- * and every workgroup gets the same page count (the last one possibly
- * fewer). A workgroup covers one row group of rows_per_group (query token,
+ * into contiguous segments, one per workgroup slot; a segment's intersection
+ * with one sequence is a chunk (one partial of the LSE merge), so a segment
+ * may cover the end of one sequence and the start of the next. Segments are
+ * cut to equal cost, pages plus a fixed cost per chunk (2 pages for 128-row
+ * groups, 3.4 half pages for 64-row groups: a chunk's prologue and finalize),
+ * so a segment that holds more chunks gets fewer pages; uniform batches get
+ * equal segments. A workgroup covers one row group of rows_per_group (query token,
  * head) rows: 128 (all heads of one new token), or 64, where two waves share
  * each 32-row slice and take one 32-token half of every page each, merging
  * their softmax states at the end. With R = ceil(s_q*H / rows_per_group) row
@@ -135,8 +137,8 @@ mla_status_t mla_decode_plan(const int32_t* seqlens_host, int B, int s_q, int H,
  * workgroups at once. 64-row groups are chosen when the chunk cap
  * (max_splits per sequence) would otherwise leave compute units idle: with
  * them each segment holds twice the pages of half the rows. If the cap
- * still binds, segments are lengthened until no sequence is cut into more
- * than max_splits chunks.
+ * still binds, the cost bound rises until no sequence is cut into more than
+ * max_splits chunks.
  *
  *   seqlens_host[B]     L_b, each >= s_q (the same values as the device seqlens
  *                       passed to mla_decode_fwd_scheduled).
