@@ -358,15 +358,7 @@ def test_schedule_balances_the_workload_shapes():
     assert s.rows_per_group == 128 and s.num_segments == 128
     cost = pages + 2.0 * np.diff(s.segment_first_chunk)
     assert cost.max() <= cost.sum() / 128 + 3.0, (cost.max(), cost.sum() / 128)
-    P = np.array([(L + 63) // 64 for L in lens])
-    seg = -(-P.sum() // 128)
-    start = np.concatenate([[0], np.cumsum(P)])
-    equal_chunks = np.zeros(-(-P.sum() // seg), int)  # chunks per equal-page segment
-    for b in range(len(P)):
-        for g in range(start[b] // seg, (start[b + 1] - 1) // seg + 1):
-            equal_chunks[g] += 1
-    equal_cost = np.minimum(seg, P.sum() - seg * np.arange(len(equal_chunks))) + 2.0 * equal_chunks
-    assert cost.max() < equal_cost.max(), (cost.max(), equal_cost.max())
+    assert cost.max() < _equal_page_max_cost(lens, 128), cost.max()
 
 
 def test_schedule_cap_and_forced_row_groups():
@@ -414,3 +406,34 @@ def test_schedule_invalid_arguments(lib):
 def test_clock_probe_rejects_a_negative_capacity(lib):
     # Checked before any HIP call: a buffer with a negative capacity.
     assert lib.mla_decode_clock_probe(FAKE, -1) == INVALID
+
+
+@pytest.mark.parametrize("seed,B,num_cus,max_splits", [(0, 700, 256, 64), (1, 50, 256, 3), (2, 1, 256, 64),
+                                                       (3, 300, 16, 64), (4, 9, 1000, 64)])
+def test_schedule_random_batches_are_tiled_within_the_cap(seed, B, num_cus, max_splits):
+    # Mixed lengths (1 token .. 40K), more or fewer sequences than segments,
+    # tight caps: every page is covered once, in order, within the cap and
+    # the segment count, and (128-row groups) no segment costs more than the
+    # costliest segment of an equal-page cut into as many segments.
+    rng = np.random.default_rng(seed)
+    lens = np.maximum(1, (rng.pareto(1.2, B) * 2000).astype(int) % 40000).tolist()
+    s = mla.decode_schedule(lens, 1, 128, num_cus=num_cus, max_splits=max_splits)
+    pages = np.array(_check_schedule(s, lens, 1, 128, num_cus, max_splits))
+    assert pages.sum() == sum((L + 63) // 64 for L in lens)
+    if s.rows_per_group == 128 and max_splits > 1:
+        cost = pages + 2.0 * np.diff(s.segment_first_chunk)
+        assert cost.max() <= _equal_page_max_cost(lens, s.num_segments) + 1e-9
+
+
+def _equal_page_max_cost(lens, G):
+    """Costliest segment (pages + 2 per chunk) when the concatenated pages are
+    cut into segments of ceil(total / G) pages."""
+    P = np.array([(L + 63) // 64 for L in lens])
+    seg = -(-int(P.sum()) // G)
+    start = np.concatenate([[0], np.cumsum(P)])
+    n_seg = -(-int(P.sum()) // seg)
+    chunks = np.zeros(n_seg, int)
+    for b in range(len(P)):
+        for g in range(start[b] // seg, (start[b + 1] - 1) // seg + 1):
+            chunks[g] += 1
+    return float((np.minimum(seg, P.sum() - seg * np.arange(n_seg)) + 2.0 * chunks).max())
