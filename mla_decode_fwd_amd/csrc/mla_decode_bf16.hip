@@ -712,18 +712,18 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
         const int rr = r + hi32f;  // two half rows per store instruction
         if (row0 + rr < rows) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + rr * 512 + (((ln & 31) ^ rr) * 16));
-          u32x4_t* const dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + rr) * kDv + 256 * t + 8 * (ln & 31));
           if (direct)
-            __builtin_nontemporal_store(v, dst);
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + rr) * kDv + 256 * t + 8 * (ln & 31)));
           else
-            *dst = v;
+            store_device_scope(out + (size_t)row0 * kDv + 256 * t, 2 * (rr * kDv + 8 * (ln & 31)), v);
         }
       }
       if (t == 0 && hi32f == 0 && rowf < rows) {
         if (direct)
           a.lse[(size_t)b * rows + rowf] = lse_v;
         else
-          a.lse_part[(size_t)part * rows + rowf] = lse_v;
+          store_device_scope(a.lse_part + (size_t)part * rows, 4 * rowf, lse_v);
       }
     };
     if (wave < 2)
@@ -742,11 +742,13 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
   // that stay dirty in L2 until the end of the kernel and then cost
   // microseconds to write back. Staged, every store instruction writes one
   // whole 1 KB row. A sequence's final rows are stored non-temporally (the
-  // next reader is another kernel's, much later); chunk partials are stored
-  // cacheable, because the merge kernel reads them right after this one and
-  // then finds them in the caches (measured on MI355X: the step is 1.5-2.5
-  // us shorter than with non-temporal partial stores, although this kernel's
-  // end-of-launch write-back grows). Row r of a wave's 32 KB staging area
+  // next reader is another kernel's, much later); chunk partials and their
+  // LSE values are stored at device scope, written through L2 to the memory
+  // side where the merge kernel, on any XCD, reads them right after this one,
+  // and none of them is left dirty for the end-of-launch write-back
+  // (measured on MI355X: the step is 1.5-2.5 us shorter than with
+  // non-temporal partial stores, and about 1 us shorter again than with
+  // plain cacheable ones). Row r of a wave's 32 KB staging area
   // keeps its 64 16-byte pieces XOR-permuted by r so that the 32 rows of a
   // write do not fall on the same LDS banks.
   char* stage = smem + wave * (kWaveRows * kDv * 2);
@@ -769,17 +771,16 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
   for (int r = 0; r < kWaveRows; ++r) {
     if (row0 + r >= rows) break;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * (kDv * 2) + ((ln ^ r) * 16));
-    u32x4_t* const dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln);
     if (direct)
-      __builtin_nontemporal_store(v, dst);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln));
     else
-      *dst = v;
+      store_device_scope(out + (size_t)(row0 + r) * kDv, 16 * ln, v);
   }
   if (hi32f == 0 && rowf < rows) {
     if (direct)
       a.lse[(size_t)b * rows + rowf] = lse_v;
     else
-      a.lse_part[(size_t)part * rows + rowf] = lse_v;
+      store_device_scope(a.lse_part + (size_t)part * rows, 4 * rowf, lse_v);
   }
 }
 

@@ -63,6 +63,24 @@ __device__ __forceinline__ void dma_line_cached(uint64_t sbase, int voff, uint32
 }
 #pragma clang diagnostic pop
 
+// A 16-byte store at device scope (cache-policy bit sc1 of a gfx950 buffer
+// store): the line is written through this XCD's L2 to the memory side at
+// once instead of staying dirty in L2 until the end-of-launch write-back, and
+// the next kernel finds it there whichever XCD it runs on. `base` must be
+// wave-uniform: it becomes the buffer descriptor, in SGPRs; `off` is the
+// lane's byte offset from it (below 2 GiB). Descriptor word 3 selects the
+// 32-bit data format that untyped buffer accesses need.
+__device__ __forceinline__ void store_device_scope(void* base, uint32_t off, u32x4_t v) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, 16 /* sc1 */);
+}
+// The same for one float (a chunk's partial LSE values).
+__device__ __forceinline__ void store_device_scope(void* base, uint32_t off, float v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 16 /* sc1 */);
+}
+
 // s_waitcnt immediate for gfx9 waiting until at most n (< 64) vector memory
 // operations are outstanding (vmcnt is split over bits 3:0 and 15:14).
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4); }

@@ -431,17 +431,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
   for (int r = 0; r < kWaveRows; ++r) {
     if (row0 + r >= rows) break;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * (kDv * 2) + ((ln ^ r) * 16));
-    u32x4_t* const dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln);
-    if (direct)  // final rows: non-temporal; chunk partials: cacheable, the merge reads them next
-      __builtin_nontemporal_store(v, dst);
+    if (direct)  // final rows: non-temporal; chunk partials: device scope, the merge reads them next
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * kDv + 8 * ln));
     else
-      *dst = v;
+      store_device_scope(out + (size_t)(row0 + r) * kDv, 16 * ln, v);
   }
   if (hi32f == 0 && rowf < rows) {
     if (direct)
       a.lse[(size_t)b * rows + rowf] = lse_v;
     else
-      a.lse_part[(size_t)g * rows + rowf] = lse_v;
+      store_device_scope(a.lse_part + (size_t)g * rows, 4 * rowf, lse_v);
   }
 }
 
