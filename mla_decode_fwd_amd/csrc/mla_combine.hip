@@ -39,15 +39,18 @@ struct RawRow {
   u32x4_t w[kBf16 ? 1 : 2];
 };
 
+// Each partial is read exactly once, so the loads are non-temporal (measured
+// on MI355X: the long-context step, decode plus merge, is 1.8-2.2 us shorter,
+// the single-sequence step 0.5 us; B=64 x 4096 unchanged).
 template <bool kBf16>
 __device__ __forceinline__ RawRow<kBf16> load_row(const void* o_part, size_t off) {
   RawRow<kBf16> r;
   if constexpr (kBf16) {
-    r.w[0] = *reinterpret_cast<const u32x4_t*>(static_cast<const __bf16*>(o_part) + off);
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const __bf16*>(o_part) + off));
   } else {
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(o_part) + off);
-    r.w[0] = src[0];
-    r.w[1] = src[1];
+    r.w[0] = __builtin_nontemporal_load(src);
+    r.w[1] = __builtin_nontemporal_load(src + 1);
   }
   return r;
 }
