@@ -374,10 +374,13 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
     __syncthreads();
     // The next page's 18 loads per wave are spread over this page's QK
     // k-steps: in a denser burst the four waves' loads queue up in the
-    // address unit and stall the MFMA stream behind them. (Built
-    // unconditionally, from a clamped table index, so that its bases stay
-    // wave-uniform SGPRs.)
-    const bool has_next = pg + 1 < pg1;
+    // address unit and stall the MFMA stream behind them. They are issued on
+    // every page, the last one included, where the clamped table index makes
+    // them reload the current page into the idle buffer: a uniform branch
+    // around each load cost more than that one page's reload (measured on
+    // MI355X: 200 cycles per page in the 64-row mode; the B=64 x 4096 step
+    // 4-5 us and the MTP step 8-10 us shorter without the branches, with the
+    // same results bit for bit). The bases stay wave-uniform SGPRs.
     char* const next_buf = smem + ((pg + 1 - pg0) & 1) * kPageBytes;
     const auto next = [&]() {
       if constexpr (kSparse) {
@@ -498,7 +501,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
           if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(T, s + kKDepth);
           st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
-          if (has_next && (s & 1) == 0) issue_line(next, s >> 1);
+          if ((s & 1) == 0) issue_line(next, s >> 1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -550,7 +553,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
           if (s + kKDepth < kQSteps) kf[s % kKDepth] = k_frag(0, s + kKDepth);
           st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], st0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
-          if (has_next && (s & 3) == 0) issue_line(next, s >> 2);
+          if ((s & 3) == 0) issue_line(next, s >> 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -578,7 +581,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
             neg0 = (m_ref == -INFINITY) ? 0.f : -m_ref;
           }
           if ((s & 3) == 0 && s >= 4) p_pair(st0, (s - 4) >> 1, neg0, pf0, psum0);
-          if (has_next && (s & 3) == 2) issue_line(next, 9 + (s >> 2));
+          if ((s & 3) == 2) issue_line(next, 9 + (s >> 2));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -633,6 +636,9 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, char* smem, co
     }
   }
 
+  // The last page's reload is still landing in the idle buffer, which the
+  // finalize reuses for staging.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   // ---- finalize: o = O / l, lse = ln2 * (m_ref + log2 l); l is split over
   // the two lanes of a row.
   agpr_fence();

@@ -232,9 +232,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     char* buf = smem + ((pg - pg0) & 1) * kBufBytes;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    const bool has_next = pg + 1 < pg1;
     const int phys_next = min(max(phys_ahead, 0), last_phys);
     phys_ahead = btab[min(pg + 2, pg1 - 1)];
+    // Issued on every page: on the last one the clamped table index reloads
+    // the current page into the idle buffer, which costs less than a branch
+    // around each load (as in the bf16 kernel).
     const PageLoad8 next = make_load8(cache, a.row_scales, phys_next, smem + ((pg + 1 - pg0) & 1) * kBufBytes);
     const int valid = L - pg * kPage;
     if (valid < kPage) {
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) st0[r] = 0.f;
     qk_tile(0, st0, [&](int s2) {
-      if (has_next && (s2 & 1) == 0 && s2 < 10) issue_line8(next, wave, lane, s2 >> 1);
+      if ((s2 & 1) == 0 && s2 < 10) issue_line8(next, wave, lane, s2 >> 1);
     });
     float sc0[16];
     tile_scales(0, sc0);
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
       if ((s2 & 1) == 0 && s2 < 16) {
         p_pair(st0, s2, neg0, sc0, pf0, psum0);
       }
-      if (has_next && (s2 & 1) == 1 && s2 < 10) issue_line8(next, wave, lane, 5 + (s2 >> 1));
+      if ((s2 & 1) == 1 && s2 < 10) issue_line8(next, wave, lane, 5 + (s2 >> 1));
     });
     l_loc += psum0;
     float sc1[16];
@@ -395,6 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     pv_tile(1, pf1, [&](int) {});
   }
 
+  // The last page's reload is still landing in the idle buffer, which the
+  // finalize reuses for staging.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   // ---- finalize, as in the bf16 kernel; MFMA row m of column tile i is
   // column 16a + m (m < 16) or 16(a + 4) + m - 16, a = (i&3) + 8(i>>2).
   agpr_fence();
