@@ -28,10 +28,13 @@
 //     registers: the score layout of a 16-token half tile is exactly the B
 //     layout of one k-step with the tokens of the k-step permuted, and the
 //     V^T reads use the same permutation). The two tiles are staggered in
-//     the source: each tile's exponentials are written between the MFMAs of
-//     the other tile's product. The compiler moves them down to just before
-//     the first PV MFMA that reads them; pinning them in place (an empty asm
-//     on each result) measured no faster.
+//     the source: each tile's exponentials run between the MFMAs of the
+//     other tile's product, one per MFMA (an exponential issues at quarter
+//     rate), held in those slots by empty asm uses (the compiler otherwise
+//     sinks them to the first PV MFMA that reads them).
+//   * With few sequences, a 64-row variant puts two workgroups on each page
+//     range: a wave pair shares 32 rows, each wave takes one 32-token tile
+//     of every page, and the pair merges its two (m, l, O) at the end.
 //   * Softmax in base 2 with a lazily updated reference max: O and l are
 //     rescaled only when a row's max grows by more than 8 (so P <= 2^8); the
 //     result is exact because P, l and O always share the reference.
