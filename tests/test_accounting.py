@@ -87,3 +87,27 @@ def test_sparse_counts_and_bytes():
     assert acc.sparse_decode_flops(counts, 128) == 5 * 2 * 128 * (576 + 512)
     b = acc.sparse_decode_bytes(counts, 2, 1, 128, 4)
     assert b == 5 * 1152 + 2 * 4 * 4 + 5 * 4 + 2 * 128 * (1152 + 1024 + 4)
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    # Each rocprofv3 summary under profiles/ records the hash of the kernel
+    # sources it was taken with (comments excluded); a summary whose kernel
+    # changed since is stale and must be taken again.
+    import glob
+    import os
+    import re
+    from mla_decode_fwd_amd.profile_summary import decode_source_sha256
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = sorted(glob.glob(os.path.join(root, "profiles", "*.md")))
+    assert files
+    checked = 0
+    for f in files:
+        text = open(f, encoding="utf-8").read()
+        src = re.search(r"--sources (\S+)", text)
+        rec = re.search(r"kernel_source_sha256: (\w+)", text)
+        if src is None or rec is None:
+            continue
+        assert decode_source_sha256(tuple(src.group(1).split(","))) == rec.group(1), os.path.basename(f)
+        checked += 1
+    assert checked >= 5
