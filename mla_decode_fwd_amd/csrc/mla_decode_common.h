@@ -50,6 +50,21 @@ __device__ __forceinline__ void dma_line(uint64_t sbase, int voff, uint32_t lds)
       : "v"(voff), "s"(sbase), "s"(lds)
       : "memory", "m0");
 }
+// The same load with M0 written by a single SALU add (lds_base + lds_off)
+// and an immediate byte offset that the instruction adds to both the global
+// and the LDS address: one instruction fewer per line than computing the LDS
+// address into an SGPR first, and no VALU add for the global offset (the
+// per-lane offset stays the unsigned, non-negative voff).
+__device__ __forceinline__ void dma_line_off(uint64_t sbase, int voff, uint32_t lds_base, const int lds_off,
+                                             const int imm) {
+  asm volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 offset:%4 nt"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base), "i"(lds_off), "i"(imm)
+      : "memory", "m0", "scc");
+}
 // The same load without the non-temporal hint (data that other workgroups
 // read again soon: the query rows).
 __device__ __forceinline__ void dma_line_cached(uint64_t sbase, int voff, uint32_t lds) {
